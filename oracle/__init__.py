@@ -1,0 +1,250 @@
+"""CPU oracle for the quantized INT8 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (the HIP library and its
+Python binding) never imports it and shares no code with it.
+
+The arithmetic lives in ``sq_oracle.c`` (plain C, gcc, exact int64
+accumulation, IEEE binary32 steps with round-half-to-even); this module only
+marshals numpy arrays.  The composite functions at the bottom chain those steps
+in the order the pages give: smooth -> per-token quantize -> int8 GEMM ->
+dequantize ("量化基础与INT8", section "INT8推理流程"; "SmoothQuant量化实战",
+section 3.4), and the LLM.int8() split ("LLM.int8()技术解析", section 3.1).
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_F32, _F16 = 0, 1
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = C.CDLL(_build.LIB)
+    P, I64, F, D, I = C.c_void_p, C.c_int64, C.c_float, C.c_double, C.c_int
+    sig = {
+        "orc_half_to_float_array": (None, [P, P, I64]),
+        "orc_float_to_half_array": (None, [P, P, I64]),
+        "orc_num_threads": (I, []),
+        "orc_col_absmax": (None, [P, I, I64, I64, P]),
+        "orc_smooth_from_maxima": (None, [P, P, I64, F, P]),
+        "orc_smooth_scales": (None, [P, I, I64, P, I, I64, I64, F, P, P]),
+        "orc_quantize_weight": (None, [P, I, I64, I64, P, I, P, P]),
+        "orc_quantize_per_token": (None, [P, I, I64, I64, P, P, P, P]),
+        "orc_gemm_i8": (I64, [P, P, I64, I64, I64, P]),
+        "orc_gemm_i8_sampled": (I64, [P, P, I64, P, P, I64, P]),
+        "orc_dequant": (None, [P, P, P, I, P, I64, I64, P]),
+        "orc_dequant_sampled": (None, [P, P, P, I, P, P, P, I64, P]),
+        "orc_outlier_columns": (I64, [P, I64, I64, F, P, P]),
+        "orc_side_product_sampled": (None, [P, P, I64, P, I64, P, P, I64, P]),
+        "orc_combine_to_half": (None, [P, P, I64, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _as(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _fp(a):
+    """(contiguous array, dtype code) for a float16 or float32 input."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a, _F16
+    if a.dtype == np.float32:
+        return a, _F32
+    raise TypeError(f"oracle takes float16 or float32, got {a.dtype}")
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def half_to_float(h):
+    h = _as(h, np.float16)
+    out = np.empty(h.shape, np.float32)
+    _load().orc_half_to_float_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def float_to_half(f):
+    f = _as(f, np.float32)
+    out = np.empty(f.shape, np.float16)
+    _load().orc_float_to_half_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def col_absmax(X, amax=None):
+    """Running per-column absolute maximum (calibration statistic)."""
+    X, dt = _fp(X)
+    M, K = X.shape
+    amax = np.zeros(K, np.float32) if amax is None else _as(amax, np.float32).copy()
+    _load().orc_col_absmax(_ptr(X), dt, M, K, _ptr(amax))
+    return amax
+
+
+def smooth_from_maxima(act_max, w_max, alpha):
+    act_max, w_max = _as(act_max, np.float32), _as(w_max, np.float32)
+    s = np.empty(act_max.shape[0], np.float32)
+    _load().orc_smooth_from_maxima(_ptr(act_max), _ptr(w_max), act_max.shape[0], float(alpha), _ptr(s))
+    return s
+
+
+def smooth_scales(X_cal, W, alpha, act_max=None):
+    """Returns (updated act_max, s)."""
+    W, wdt = _fp(W)
+    N, K = W.shape
+    amax = np.zeros(K, np.float32) if act_max is None else _as(act_max, np.float32).copy()
+    if X_cal is None:
+        xp, xdt, Mc = None, _F32, 0
+    else:
+        X_cal, xdt = _fp(X_cal)
+        xp, Mc = _ptr(X_cal), X_cal.shape[0]
+    s = np.empty(K, np.float32)
+    _load().orc_smooth_scales(xp, xdt, Mc, _ptr(W), wdt, N, K, float(alpha), _ptr(amax), _ptr(s))
+    return amax, s
+
+
+def quantize_weight(W, s=None, gran=0):
+    """gran 0: per output channel; 1: per tensor.  Returns (Wq int8 [N,K], w_scale)."""
+    W, dt = _fp(W)
+    N, K = W.shape
+    s = None if s is None else _as(s, np.float32)
+    Wq = np.empty((N, K), np.int8)
+    ws = np.empty(N if gran == 0 else 1, np.float32)
+    _load().orc_quantize_weight(_ptr(W), dt, N, K, _ptr(s), int(gran), _ptr(Wq), _ptr(ws))
+    return Wq, ws
+
+
+def quantize_per_token(X, s=None, skip=None):
+    """Returns (Xq int8 [M,K], x_scale [M]).  skip: bool/uint8 [K] columns to leave out."""
+    X, dt = _fp(X)
+    M, K = X.shape
+    s = None if s is None else _as(s, np.float32)
+    skip = None if skip is None else _as(skip, np.uint8)
+    Xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    _load().orc_quantize_per_token(_ptr(X), dt, M, K, _ptr(s), _ptr(skip), _ptr(Xq), _ptr(xs))
+    return Xq, xs
+
+
+def gemm_i8(A, B):
+    A, B = _as(A, np.int8), _as(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    acc = np.empty((M, N), np.int32)
+    bad = _load().orc_gemm_i8(_ptr(A), _ptr(B), M, N, K, _ptr(acc))
+    if bad:
+        raise OverflowError(f"{bad} accumulators exceed int32")
+    return acc
+
+
+def gemm_i8_sampled(A, B, rows, cols):
+    A, B = _as(A, np.int8), _as(B, np.int8)
+    rows, cols = _as(rows, np.int64), _as(cols, np.int64)
+    out = np.empty(rows.shape[0], np.int32)
+    bad = _load().orc_gemm_i8_sampled(_ptr(A), _ptr(B), A.shape[1], _ptr(rows), _ptr(cols),
+                                      rows.shape[0], _ptr(out))
+    if bad:
+        raise OverflowError(f"{bad} accumulators exceed int32")
+    return out
+
+
+def dequant(acc, x_scale, w_scale, gran=0, bias=None):
+    acc = _as(acc, np.int32)
+    M, N = acc.shape
+    xs, ws = _as(x_scale, np.float32), _as(w_scale, np.float32)
+    bias = None if bias is None else _as(bias, np.float32)
+    y = np.empty((M, N), np.float32)
+    _load().orc_dequant(_ptr(acc), _ptr(xs), _ptr(ws), int(gran), _ptr(bias), M, N, _ptr(y))
+    return y
+
+
+def dequant_sampled(acc, x_scale, w_scale, gran, bias, rows, cols):
+    acc = _as(acc, np.int32)
+    xs, ws = _as(x_scale, np.float32), _as(w_scale, np.float32)
+    bias = None if bias is None else _as(bias, np.float32)
+    rows, cols = _as(rows, np.int64), _as(cols, np.int64)
+    y = np.empty(rows.shape[0], np.float32)
+    _load().orc_dequant_sampled(_ptr(acc), _ptr(xs), _ptr(ws), int(gran), _ptr(bias), _ptr(rows),
+                                _ptr(cols), rows.shape[0], _ptr(y))
+    return y
+
+
+def outlier_columns(X16, threshold):
+    """Returns (mask uint8 [K], ascending idx int32 [count])."""
+    X16 = _as(X16, np.float16)
+    M, K = X16.shape
+    mask = np.empty(K, np.uint8)
+    idx = np.empty(K, np.int32)
+    count = _load().orc_outlier_columns(_ptr(X16), M, K, float(threshold), _ptr(mask), _ptr(idx))
+    return mask, idx[:count].copy()
+
+
+def side_product_sampled(X16, W16, idx, rows, cols):
+    X16, W16 = _as(X16, np.float16), _as(W16, np.float16)
+    idx = _as(idx, np.int32)
+    rows, cols = _as(rows, np.int64), _as(cols, np.int64)
+    side = np.empty(rows.shape[0], np.float64)
+    _load().orc_side_product_sampled(_ptr(X16), _ptr(W16), X16.shape[1], _ptr(idx), idx.shape[0],
+                                     _ptr(rows), _ptr(cols), rows.shape[0], _ptr(side))
+    return side
+
+
+def combine_to_half(y_int8, side):
+    y, side = _as(y_int8, np.float32), _as(side, np.float64)
+    out = np.empty(y.shape, np.float16)
+    _load().orc_combine_to_half(_ptr(y), _ptr(side), y.size, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Composite paths (steps chained in the pages' order; no extra arithmetic).
+# ---------------------------------------------------------------------------
+
+def _store(y, out_dtype):
+    return y if out_dtype == np.float32 else float_to_half(y)
+
+
+def w8a8_linear(X, s, Wq, w_scale, gran=0, bias=None, out_dtype=np.float16, rows=None):
+    """X [M,K] -> (Xq, xs, acc, Y) for the rows given (all rows when None).
+
+    Per-token quantization of X diag(s)^-1, int8 GEMM against the prepared
+    Wq, dequantization, output stored as out_dtype."""
+    Xr = X if rows is None else X[rows]
+    Xq, xs = quantize_per_token(Xr, s)
+    acc = gemm_i8(Xq, Wq)
+    y = dequant(acc, xs, w_scale, gran, bias)
+    return Xq, xs, acc, _store(y, out_dtype)
+
+
+def llm_int8_linear(X16, W16, Wq, w_scale, threshold, bias=None, rows=None):
+    """LLM.int8(): returns (mask, idx, Xq, xs, acc, Y fp16) for the rows given."""
+    mask, idx = outlier_columns(X16, threshold)          # columns decided over all rows
+    Xr = X16 if rows is None else X16[rows]
+    Xq, xs = quantize_per_token(Xr, None, skip=mask)
+    acc = gemm_i8(Xq, Wq)
+    y = dequant(acc, xs, w_scale, 0, bias)
+    M, N = y.shape
+    rr = np.repeat(np.arange(M, dtype=np.int64), N)
+    cc = np.tile(np.arange(N, dtype=np.int64), M)
+    side = side_product_sampled(Xr, W16, idx, rr, cc).reshape(M, N)
+    return mask, idx, Xq, xs, acc, combine_to_half(y, side)

@@ -1,0 +1,368 @@
+/*
+ * CPU oracle for the quantized INT8 linear layer.  TEST INFRASTRUCTURE ONLY:
+ * the tests, the smoke check and the benchmark's CPU-baseline leg are the only
+ * callers.  The product path never links or calls this file; it shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * Plain C99, built with `gcc -O2 -fopenmp -ffp-contract=off` (no fast-math, so
+ * no flush-to-zero and no fused multiply-add).  Every floating-point step below
+ * is one IEEE-754 binary32 operation with round-to-nearest-even, except where a
+ * comment says fp64.  Integer products are accumulated in int64, exactly.
+ *
+ * Sources (pages are cited by title and section):
+ *  - "量化基础与INT8" (quantization basics notes): symmetric mapping
+ *    scale = max|x|/127 and q = round(x/scale) clamped to the int8 range;
+ *    per-tensor / per-channel / per-token granularity; the INT8 inference
+ *    flow (quantize -> int8 GEMM with int32 accumulation -> dequantize as
+ *    acc * x_scale * w_scale), sections "量化粒度", "INT8推理流程",
+ *    "量化流程示例".
+ *  - "SmoothQuant量化实战：W8A8推理部署与单节点530B模型落地": the smoothing
+ *    identity (section 1.3), s_j = max|X_j|^a / max|W_j|^(1-a) (section 2.1),
+ *    compute_smooth_scale with the 1e-8 floors (section 3.3), the calibration
+ *    running max (section 3.2), the W8A8 forward (section 3.4), bias kept in
+ *    floating point (section 4.5).
+ *  - "LLM.int8()技术解析：8位量化如何优化大语言模型计算": column-wise absmax,
+ *    columns above a threshold handled in fp16, the rest in int8, results
+ *    combined (sections 2.1 and 3.1).
+ *
+ * Readings where the pages leave a step open (all listed in the design notes):
+ *  rounding is half-to-even (torch.round in every code sample); quantizing
+ *  divides by the scale (not multiply by 127/max); clamp to [-128,127]; an
+ *  all-zero row/column gets scale 0 and q = 0; the smoothing factor is
+ *  evaluated in fp64 and rounded once to fp32, without the optional
+ *  normalisation of section 3.3's sample; the LLM.int8() per-token scale uses
+ *  the non-outlier columns only; the int8 and fp16 parts are summed.
+ *
+ * Dtype codes used by this file only: 0 = float32, 1 = float16 (raw bits).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_F16 1
+
+/* ------------------------------------------------------------------ */
+/* fp16 <-> fp32 conversions, written out from the binary16 format.     */
+/* ------------------------------------------------------------------ */
+
+/* Exact widening of an IEEE binary16 bit pattern to binary32. */
+float orc_half_to_float(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t expo = (uint32_t)(h >> 10) & 0x1fu;
+    uint32_t mant = (uint32_t)h & 0x3ffu;
+    float v;
+    if (expo == 0) {
+        v = (float)mant * 0x1p-24f;              /* subnormal (or zero): mant * 2^-24, exact */
+    } else if (expo == 31) {
+        v = mant ? NAN : INFINITY;
+    } else {
+        uint32_t bits = ((expo - 15u + 127u) << 23) | (mant << 13);
+        memcpy(&v, &bits, 4);
+    }
+    return sign ? -v : v;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even. */
+uint16_t orc_float_to_half(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    uint32_t ax = x & 0x7fffffffu;
+    if (ax > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);   /* NaN */
+    if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);  /* >= 65520 rounds to inf */
+    int e = (int)(ax >> 23) - 127;                               /* unbiased exponent */
+    if (e >= -14) {                                              /* normal binary16 */
+        uint32_t mant = ax & 0x7fffffu;
+        uint32_t h = ((uint32_t)(e + 15) << 10) | (mant >> 13);
+        uint32_t rem = mant & 0x1fffu;
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;   /* carry into exponent is correct */
+        return (uint16_t)(sign | h);
+    }
+    if (e < -25) return sign;                                    /* below 2^-25: rounds to zero */
+    /* subnormal binary16: the result is round(value * 2^24) */
+    uint32_t sig = (ax & 0x7fffffu) | 0x800000u;                 /* value = sig * 2^(e-23) */
+    int shift = -(e + 1);                                        /* value*2^24 = sig >> shift */
+    uint32_t q = sig >> shift;
+    uint32_t rem = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1u;
+    return (uint16_t)(sign | q);
+}
+
+void orc_half_to_float_array(const uint16_t* in, float* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_half_to_float(in[i]);
+}
+
+void orc_float_to_half_array(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_float_to_half(in[i]);
+}
+
+static float load_elem(const void* p, int dt, int64_t i)
+{
+    if (dt == ORC_F16) return orc_half_to_float(((const uint16_t*)p)[i]);
+    return ((const float*)p)[i];
+}
+
+/* round half to even, then clamp to the int8 range */
+static int8_t quant_code(float v)
+{
+    float r = rintf(v);            /* default rounding mode: nearest, ties to even */
+    if (r > 127.0f) r = 127.0f;
+    if (r < -128.0f) r = -128.0f;
+    return (int8_t)r;
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ */
+/* Calibration statistic and smoothing factors (SmoothQuant page,       */
+/* sections 2.1, 3.2, 3.3).                                             */
+/* ------------------------------------------------------------------ */
+
+/* amax[j] = max(amax[j], max_m |X[m,j]|): the per-input-channel running
+ * maximum that the calibration hook accumulates across batches. */
+void orc_col_absmax(const void* X, int dt, int64_t M, int64_t K, float* amax)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < K; ++j) {
+        float a = amax[j];
+        for (int64_t m = 0; m < M; ++m) {
+            float v = fabsf(load_elem(X, dt, m * K + j));
+            if (v > a) a = v;
+        }
+        amax[j] = a;
+    }
+}
+
+/* s_j = max(a_j,1e-8)^alpha / max(w_j,1e-8)^(1-alpha), both powers in fp64,
+ * the ratio rounded once to fp32. */
+void orc_smooth_from_maxima(const float* act_max, const float* w_max, int64_t K,
+                            float alpha, float* s)
+{
+    double al = (double)alpha;
+    for (int64_t j = 0; j < K; ++j) {
+        float a = act_max[j] > 1e-8f ? act_max[j] : 1e-8f;
+        float w = w_max[j] > 1e-8f ? w_max[j] : 1e-8f;
+        s[j] = (float)(pow((double)a, al) / pow((double)w, 1.0 - al));
+    }
+}
+
+/* Full step a1+a2: update the running activation maximum with a calibration
+ * batch (X_cal may be NULL when M_cal == 0), take the column maxima of W over
+ * its output rows, and form s. */
+void orc_smooth_scales(const void* X_cal, int xdt, int64_t M_cal,
+                       const void* W, int wdt, int64_t N, int64_t K,
+                       float alpha, float* act_max, float* s)
+{
+    if (X_cal && M_cal > 0) orc_col_absmax(X_cal, xdt, M_cal, K, act_max);
+    float* w_max = (float*)calloc((size_t)K, sizeof(float));
+    orc_col_absmax(W, wdt, N, K, w_max);
+    orc_smooth_from_maxima(act_max, w_max, K, alpha, s);
+    free(w_max);
+}
+
+/* ------------------------------------------------------------------ */
+/* Weight smoothing and quantization (SmoothQuant page 3.3-3.4; basics  */
+/* notes "量化粒度").  gran: 0 = one scale per output row (channel),     */
+/* 1 = one scale for the whole tensor.                                  */
+/* ------------------------------------------------------------------ */
+void orc_quantize_weight(const void* W, int dt, int64_t N, int64_t K, const float* s,
+                         int gran, int8_t* Wq, float* w_scale)
+{
+    float* Ws = (float*)malloc((size_t)(N * K) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K; ++j) {
+            float w = load_elem(W, dt, n * K + j);
+            Ws[n * K + j] = s ? w * s[j] : w;          /* W' = W diag(s): scales input channels */
+        }
+
+    if (gran == 0) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            float m = 0.0f;
+            for (int64_t j = 0; j < K; ++j) {
+                float v = fabsf(Ws[n * K + j]);
+                if (v > m) m = v;
+            }
+            float sc = m / 127.0f;
+            w_scale[n] = sc;
+            for (int64_t j = 0; j < K; ++j)
+                Wq[n * K + j] = sc == 0.0f ? 0 : quant_code(Ws[n * K + j] / sc);
+        }
+    } else {
+        float m = 0.0f;
+        for (int64_t i = 0; i < N * K; ++i) {
+            float v = fabsf(Ws[i]);
+            if (v > m) m = v;
+        }
+        float sc = m / 127.0f;
+        w_scale[0] = sc;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < N * K; ++i)
+            Wq[i] = sc == 0.0f ? 0 : quant_code(Ws[i] / sc);
+    }
+    free(Ws);
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-token activation quantization with optional smoothing (basics    */
+/* notes "量化流程示例"; SmoothQuant page 3.4).  skip (may be NULL) marks */
+/* columns excluded from the int8 part (LLM.int8() outliers): they get  */
+/* q = 0 and do not enter the row maximum.                              */
+/* ------------------------------------------------------------------ */
+void orc_quantize_per_token(const void* X, int dt, int64_t M, int64_t K, const float* s,
+                            const uint8_t* skip, int8_t* Xq, float* x_scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            if (skip && skip[j]) continue;
+            float x = load_elem(X, dt, m * K + j);
+            if (s) x = x / s[j];                        /* X' = X diag(s)^-1 */
+            float v = fabsf(x);
+            if (v > a) a = v;
+        }
+        float sc = a / 127.0f;
+        x_scale[m] = sc;
+        for (int64_t j = 0; j < K; ++j) {
+            if ((skip && skip[j]) || sc == 0.0f) {
+                Xq[m * K + j] = 0;
+                continue;
+            }
+            float x = load_elem(X, dt, m * K + j);
+            if (s) x = x / s[j];
+            Xq[m * K + j] = quant_code(x / sc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* int8 x int8 -> int32 GEMM, "NT": acc[m,n] = sum_k A[m,k] * B[n,k],  */
+/* accumulated in int64 and checked to fit int32 (basics notes          */
+/* "INT8推理流程").  Returns the number of results that did not fit.      */
+/* ------------------------------------------------------------------ */
+int64_t orc_gemm_i8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K,
+                    int32_t* acc)
+{
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t t = 0;
+            for (int64_t k = 0; k < K; ++k) t += (int64_t)A[m * K + k] * (int64_t)B[n * K + k];
+            if (t > INT32_MAX || t < INT32_MIN) ++bad;
+            acc[m * N + n] = (int32_t)t;
+        }
+    return bad;
+}
+
+/* The same dot products at nsamp given (row, col) positions. */
+int64_t orc_gemm_i8_sampled(const int8_t* A, const int8_t* B, int64_t K, const int64_t* rows,
+                            const int64_t* cols, int64_t nsamp, int32_t* out)
+{
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t i = 0; i < nsamp; ++i) {
+        int64_t t = 0;
+        const int8_t* a = A + rows[i] * K;
+        const int8_t* b = B + cols[i] * K;
+        for (int64_t k = 0; k < K; ++k) t += (int64_t)a[k] * (int64_t)b[k];
+        if (t > INT32_MAX || t < INT32_MIN) ++bad;
+        out[i] = (int32_t)t;
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization: y = ((float)acc * x_scale[m]) * w_scale[n or 0],    */
+/* left to right, then + bias[n] (bias stays floating point, SmoothQuant */
+/* page 4.5).  Writes fp32.                                              */
+/* ------------------------------------------------------------------ */
+static float dequant_one(int32_t acc, float xs, float ws, const float* bias, int64_t n)
+{
+    float y = (float)acc;          /* int32 -> fp32, nearest-even (exact below 2^24) */
+    y = y * xs;
+    y = y * ws;
+    if (bias) y = y + bias[n];
+    return y;
+}
+
+void orc_dequant(const int32_t* acc, const float* x_scale, const float* w_scale, int wgran,
+                 const float* bias, int64_t M, int64_t N, float* y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = dequant_one(acc[m * N + n], x_scale[m], w_scale[wgran == 0 ? n : 0], bias, n);
+}
+
+void orc_dequant_sampled(const int32_t* acc, const float* x_scale, const float* w_scale, int wgran,
+                         const float* bias, const int64_t* rows, const int64_t* cols, int64_t nsamp,
+                         float* y)
+{
+    for (int64_t i = 0; i < nsamp; ++i)
+        y[i] = dequant_one(acc[i], x_scale[rows[i]], w_scale[wgran == 0 ? cols[i] : 0], bias, cols[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* LLM.int8() pieces (LLM.int8() page, sections 2.1 and 3.1).           */
+/* ------------------------------------------------------------------ */
+
+/* Column j is an outlier when max_m |X[m,j]| > threshold (strictly).
+ * Writes mask[K] (0/1), the ascending index list idx[0..count) and returns count. */
+int64_t orc_outlier_columns(const uint16_t* X16, int64_t M, int64_t K, float threshold,
+                            uint8_t* mask, int32_t* idx)
+{
+    float* cmax = (float*)calloc((size_t)K, sizeof(float));
+    orc_col_absmax(X16, ORC_F16, M, K, cmax);
+    int64_t count = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        mask[j] = cmax[j] > threshold ? 1 : 0;
+        if (mask[j]) idx[count++] = (int32_t)j;
+    }
+    free(cmax);
+    return count;
+}
+
+/* side[i] = sum over the listed columns t of X[row,t] * W16[col,t], in fp64,
+ * at the given (row, col) positions (pass rows/cols covering a full matrix for
+ * a dense result). */
+void orc_side_product_sampled(const uint16_t* X16, const uint16_t* W16, int64_t K,
+                              const int32_t* idx, int64_t count, const int64_t* rows,
+                              const int64_t* cols, int64_t nsamp, double* side)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nsamp; ++i) {
+        double t = 0.0;
+        for (int64_t c = 0; c < count; ++c) {
+            int64_t j = idx[c];
+            t += (double)orc_half_to_float(X16[rows[i] * K + j]) *
+                 (double)orc_half_to_float(W16[cols[i] * K + j]);
+        }
+        side[i] = t;
+    }
+}
+
+/* out = fp16( fp32( (double)y_int8 + side ) ) */
+void orc_combine_to_half(const float* y_int8, const double* side, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_float_to_half((float)((double)y_int8[i] + side[i]));
+}

@@ -1,0 +1,464 @@
+"""Pins of the CPU oracle to facts fixed outside it (no GPU).
+
+Each test ties one oracle function to something other than its own formula:
+a value a page prints, a closed form, an invariant, brute force on tiny inputs,
+or a special case that reduces to a library routine.  Together they are
+chosen so that a plausible slip (wrong rounding mode, multiply instead of
+divide, /128 instead of /127, the smoothing vector applied to the wrong axis or
+inverted, a dropped term in the epilogue, a transposed GEMM operand, outlier
+columns counted in the per-token scale) fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng0 = np.random.default_rng(1234)
+
+
+# --------------------------------------------------------------------------
+# fp16 <-> fp32 conversions: special case = numpy's IEEE conversions
+# --------------------------------------------------------------------------
+
+def test_half_to_float_all_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    ours = orc.half_to_float(h)
+    ref = h.astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_float_to_half_matches_numpy_rne(orc):
+    rng = np.random.default_rng(7)
+    parts = [
+        rng.standard_normal(200000).astype(np.float32) * np.float32(100),
+        (rng.random(100000) * 7e-5).astype(np.float32),                    # binary16 subnormal range
+        rng.uniform(60000, 70000, 20000).astype(np.float32),               # overflow edge
+        rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+    ]
+    # exact ties: midpoints between neighbouring binary16 values
+    h = np.arange(0, 0x7bff, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mid = ((h[:-1] + h[1:]) / 2).astype(np.float32)
+    parts += [mid, -mid, np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, np.inf, -np.inf],
+                                  np.float32)]
+    f = np.concatenate(parts)
+    f = f[~np.isnan(f)]
+    ours = orc.float_to_half(f)
+    ref = f.astype(np.float16)
+    assert np.array_equal(ours.view(np.uint16), ref.view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# Quantizer: the page's worked example, ties, bounds and invariants
+# --------------------------------------------------------------------------
+
+def test_worked_example_outlier_channel_scale(orc):
+    """SmoothQuant page, section 1.2: one +-50 channel among [-1,1] values forces
+    scale 50/127 ~ 0.39 and leaves the [-1,1] values 2-3 bits."""
+    g = json.load(open(os.path.join(GOLDEN, "smoothquant_s12_outlier_channel.json")))
+    rng = np.random.default_rng(0)
+    x = rng.uniform(-1, 1, 64).astype(np.float32)
+    x[:4] = [1.0, -1.0, 0.5, 0.25]
+    x[37] = 50.0
+    Xq, xs = orc.quantize_per_token(x[None, :])
+    pv = g["page_values"]
+    assert abs(float(xs[0]) - pv["scale_approx"]) < pv["scale_tolerance"]
+    assert np.float32(xs[0]) == np.float32(g["derived_exact"]["scale_fp32"])
+    for v, q in g["derived_exact"]["q_of"].items():
+        row = np.zeros(64, np.float32)
+        row[37] = 50.0
+        row[0] = float(v)
+        qq, _ = orc.quantize_per_token(row[None, :])
+        assert int(qq[0, 0]) == q, v
+    levels = np.unique(Xq[0][np.abs(x) <= 1.0])
+    assert set(levels.tolist()) <= set(range(-3, 4))
+    assert pv["bits_low"] <= math.log2(g["derived_exact"]["levels_in_unit_range"]) <= pv["bits_high"]
+
+
+def test_ties_round_half_to_even(orc):
+    """A row whose absmax is exactly 127 has scale 1.0, so x/scale = x exactly and
+    the code is x rounded half to even (torch.round semantics)."""
+    row = np.array([127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5, 126.5, -126.5, 4.4999995, 0.0],
+                   np.float32)
+    Xq, xs = orc.quantize_per_token(row[None, :])
+    assert xs[0] == np.float32(1.0)
+    assert Xq[0].tolist() == [127, 2, 4, -2, -4, 0, 2, 0, 126, -126, 4, 0]
+
+
+def _brute_code(v):
+    """Nearest integer in [-128,127] by exhaustive search, ties to the even one."""
+    best = None
+    for q in range(-128, 128):
+        d = abs(Fraction(float(v)) - q)
+        if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
+            best = (d, q)
+    return best[1]
+
+
+def test_quantizer_brute_force_tiny(orc):
+    rng = np.random.default_rng(3)
+    X = (rng.standard_normal((6, 10)) * rng.uniform(0.01, 100, (6, 1))).astype(np.float32)
+    X[2, 4] = X[2].max() * 1.5
+    Xq, xs = orc.quantize_per_token(X)
+    for m in range(6):
+        a = max(abs(Fraction(float(v))) for v in X[m])
+        # scale is the correctly rounded a/127 (a library division, numpy IEEE fp32)
+        assert xs[m] == np.float32(np.float32(a) / np.float32(127.0))
+        for j in range(10):
+            v = np.float32(X[m, j]) / np.float32(xs[m])
+            assert Xq[m, j] == _brute_code(v)
+
+
+def test_roundtrip_error_bound_and_full_range(orc):
+    """|x - q*scale| <= scale/2 (plus the rounding of x/scale) for every element,
+    |q| <= 127, and every non-zero row reaches |q| = 127."""
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((64, 300)).astype(np.float32) * rng.uniform(1e-3, 1e3, (64, 1)).astype(np.float32)
+    X[3] = 0.0
+    Xq, xs = orc.quantize_per_token(X)
+    err = np.abs(X.astype(np.float64) - Xq.astype(np.float64) * xs[:, None].astype(np.float64))
+    assert np.all(err <= xs[:, None].astype(np.float64) * (0.5 + 1e-5))
+    assert np.abs(Xq.astype(np.int32)).max() <= 127
+    nz = np.any(X != 0, axis=1)
+    assert np.all(np.abs(Xq[nz].astype(np.int32)).max(axis=1) == 127)
+    assert xs[3] == 0 and np.all(Xq[3] == 0)
+
+
+def test_scale_and_sign_invariance(orc):
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((32, 128)).astype(np.float32)
+    Xq, xs = orc.quantize_per_token(X)
+    for k in (-7, -1, 3, 11):
+        Xq2, xs2 = orc.quantize_per_token(X * np.float32(2.0 ** k))
+        assert np.array_equal(Xq, Xq2)
+        assert np.array_equal(xs2, xs * np.float32(2.0 ** k))
+    Xq3, xs3 = orc.quantize_per_token(-X)
+    assert np.array_equal(Xq3, -Xq) and np.array_equal(xs3, xs)
+
+
+def test_fp16_input_equals_widened_fp32(orc):
+    X, _, _ = workloads.random_layer(11, 24, 256, 8, np.float16, n_outliers=3)
+    a = orc.quantize_per_token(X)
+    b = orc.quantize_per_token(X.astype(np.float32))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------
+# Weight quantization granularities
+# --------------------------------------------------------------------------
+
+def test_per_channel_weight_is_per_output_row(orc):
+    """Each output channel (row of the [out, in] weight) gets its own absmax scale:
+    the same computation as per-token quantization of those rows."""
+    _, W, _ = workloads.random_layer(12, 1, 200, 48, np.float32)
+    W[5] *= 40
+    Wq, ws = orc.quantize_weight(W, None, 0)
+    Wq2, ws2 = orc.quantize_per_token(W)
+    assert np.array_equal(Wq, Wq2) and np.array_equal(ws, ws2)
+    assert np.all(np.abs(Wq.astype(int)).max(axis=1) == 127)
+
+
+def test_per_tensor_weight_is_one_row(orc):
+    """Per-tensor quantization = one scale for the whole matrix: the special
+    case of absmax quantization over one flattened row."""
+    _, W, _ = workloads.random_layer(13, 1, 96, 40, np.float32)
+    Wq, ws = orc.quantize_weight(W, None, 1)
+    Wq1, ws1 = orc.quantize_per_token(W.reshape(1, -1))
+    assert ws.shape == (1,) and ws[0] == ws1[0]
+    assert np.array_equal(Wq.reshape(1, -1), Wq1)
+    assert np.abs(Wq.astype(int)).max() == 127
+    assert (np.abs(Wq.astype(int)).max(axis=1) < 127).sum() > 0
+
+
+# --------------------------------------------------------------------------
+# Smoothing factors (SmoothQuant page, sections 1.3, 2.1, 3.3)
+# --------------------------------------------------------------------------
+
+def _ulps(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.abs(a - b) / np.spacing(np.abs(b).astype(np.float32)).astype(np.float64)
+
+
+def test_smooth_alpha_half_balances_maxima(orc):
+    """alpha = 0.5: max|X'_j| = a_j/s_j and max|W'_j| = w_j*s_j both equal
+    sqrt(a_j*w_j) -- the difficulty is split evenly."""
+    X, W, _ = workloads.random_layer(21, 128, 256, 64, np.float32, n_outliers=4)
+    amax, s = orc.smooth_scales(X, W, 0.5)
+    a = np.abs(X).max(0).astype(np.float64)
+    w = np.abs(W).max(0).astype(np.float64)
+    assert np.array_equal(amax, np.abs(X).max(0))
+    g = np.sqrt(a * w)
+    assert np.all(_ulps(a / s.astype(np.float64), g) <= 2)
+    assert np.all(_ulps(w * s.astype(np.float64), g) <= 2)
+
+
+def test_smooth_alpha_extremes(orc):
+    X, W, _ = workloads.random_layer(22, 64, 128, 32, np.float32, n_outliers=2)
+    _, s1 = orc.smooth_scales(X, W, 1.0)
+    assert np.array_equal(s1, np.abs(X).max(0))               # s = a: max|X'_j| = 1 exactly
+    Xq, xs = orc.quantize_per_token(X, s1)
+    Xs = X / s1                                               # numpy IEEE division
+    assert np.all(np.abs(Xs).max(0) == 1.0)
+    _, s0 = orc.smooth_scales(X, W, 0.0)
+    w = np.abs(W).max(0).astype(np.float64)
+    assert np.all(_ulps(w * s0.astype(np.float64), np.ones_like(w)) <= 1)   # max|W'_j| ~ 1
+
+
+def test_smooth_floor_and_running_max(orc):
+    X, W, _ = workloads.random_layer(23, 16, 32, 8, np.float32)
+    X[:, 5] = 0.0
+    W[:, 7] = 0.0
+    amax, s = orc.smooth_scales(X, W, 0.5)
+    w5 = float(np.abs(W[:, 5]).max())
+    assert abs(float(s[5]) - math.sqrt(1e-8) / math.sqrt(w5)) <= 1e-6 * abs(float(s[5]))
+    a7 = float(np.abs(X[:, 7]).max())
+    assert abs(float(s[7]) - math.sqrt(a7) / math.sqrt(float(np.float32(1e-8)))) <= 1e-6 * float(s[7])
+    # running maximum across calibration batches == maximum over the union
+    amax2, _ = orc.smooth_scales(X[8:], W, 0.5, act_max=orc.smooth_scales(X[:8], W, 0.5)[0])
+    assert np.array_equal(amax2, amax)
+
+
+def test_smoothing_axis_and_direction_power_of_two(orc):
+    """With s_j powers of two, X/s and W*s are exact, so smoothing inside the
+    oracle must equal quantizing the numpy-scaled tensors: divides X's columns,
+    multiplies W's columns (input channels), never rows."""
+    X, W, _ = workloads.random_layer(24, 20, 64, 12, np.float32, n_outliers=3)
+    s = (2.0 ** np.random.default_rng(0).integers(-6, 7, 64)).astype(np.float32)
+    assert np.array_equal(orc.quantize_per_token(X, s)[0], orc.quantize_per_token(X / s)[0])
+    for g in (0, 1):
+        a, b = orc.quantize_weight(W, s, g), orc.quantize_weight(W * s, None, g)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_smoothing_identity_fp64():
+    """(X diag(s)^-1)(diag(s) W) = X W exactly in exact arithmetic; in fp64 the
+    difference is rounding only (SmoothQuant page, section 1.3)."""
+    X, W, _ = workloads.random_layer(25, 32, 256, 48, np.float64, n_outliers=4)
+    s = np.random.default_rng(1).uniform(0.01, 50, 256)
+    ref = X @ W.T
+    sm = (X / s) @ (W * s).T
+    assert np.max(np.abs(sm - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_normalisation_is_invariant_power_of_two(orc):
+    """Scaling s by a power of two (the optional s/max(s)*127 normalisation of the
+    calibration sample, restricted to exact multipliers) changes no int8 code."""
+    X, W, _ = workloads.random_layer(26, 24, 128, 16, np.float32, n_outliers=3)
+    _, s = orc.smooth_scales(X, W, 0.5)
+    c = np.float32(2.0 ** 5)
+    for g in (0, 1):
+        Wa, wa = orc.quantize_weight(W, s, g)
+        Wb, wb = orc.quantize_weight(W, s * c, g)
+        assert np.array_equal(Wa, Wb) and np.array_equal(wb, wa * c)
+    Xa, xa = orc.quantize_per_token(X, s)
+    Xb, xb = orc.quantize_per_token(X, s * c)
+    assert np.array_equal(Xa, Xb) and np.array_equal(xb, xa / c)
+
+
+# --------------------------------------------------------------------------
+# int8 GEMM
+# --------------------------------------------------------------------------
+
+def test_gemm_brute_force_tiny(orc):
+    rng = np.random.default_rng(31)
+    for M, N, K in ((1, 1, 1), (3, 5, 7), (8, 4, 16), (5, 9, 33)):
+        A = rng.integers(-128, 128, (M, K)).astype(np.int8)
+        B = rng.integers(-128, 128, (N, K)).astype(np.int8)
+        A[0, :] = -128
+        B[0, :] = -128
+        acc = orc.gemm_i8(A, B)
+        for m in range(M):
+            for n in range(N):
+                assert acc[m, n] == sum(int(A[m, k]) * int(B[n, k]) for k in range(K))
+
+
+def test_gemm_vs_fp64_blas_and_identity(orc):
+    """fp64 matmul of int8-valued matrices is exact (partial sums < 2^53), an
+    independent check at a larger size; Wq = 127 I gives acc = 127 Xq."""
+    rng = np.random.default_rng(32)
+    A = rng.integers(-127, 128, (70, 1040)).astype(np.int8)
+    B = rng.integers(-127, 128, (90, 1040)).astype(np.int8)
+    acc = orc.gemm_i8(A, B)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    assert np.array_equal(acc.astype(np.float64), ref)
+    I = (np.eye(1040) * 127).astype(np.int8)
+    assert np.array_equal(orc.gemm_i8(A, I), A.astype(np.int32) * 127)
+    rows = rng.integers(0, 70, 500)
+    cols = rng.integers(0, 90, 500)
+    assert np.array_equal(orc.gemm_i8_sampled(A, B, rows, cols), acc[rows, cols])
+
+
+def test_gemm_extreme_values_and_overflow_guard(orc):
+    K = 20480
+    A = np.full((2, K), 127, np.int8)
+    B = np.full((2, K), -127, np.int8)
+    assert np.all(orc.gemm_i8(A, B) == -127 * 127 * K)
+    K = 133200                                                 # 127^2 * K > 2^31 - 1
+    with pytest.raises(OverflowError):
+        orc.gemm_i8(np.full((1, K), 127, np.int8), np.full((1, K), 127, np.int8))
+
+
+# --------------------------------------------------------------------------
+# Dequantization epilogue
+# --------------------------------------------------------------------------
+
+def test_dequant_closed_form(orc):
+    rng = np.random.default_rng(41)
+    acc = rng.integers(-2**23, 2**23, (8, 12)).astype(np.int32)
+    xs = (2.0 ** rng.integers(-12, -4, 8)).astype(np.float32)       # exact products
+    ws = (2.0 ** rng.integers(-10, -3, 12)).astype(np.float32)
+    bias = (rng.integers(-64, 64, 12) / 8.0).astype(np.float32)
+    y = orc.dequant(acc, xs, ws, 0, bias)
+    for m in range(8):
+        for n in range(12):
+            ex = Fraction(int(acc[m, n])) * Fraction(float(xs[m])) * Fraction(float(ws[n])) + Fraction(float(bias[n]))
+            assert Fraction(float(y[m, n])) == ex or abs(float(y[m, n]) - float(ex)) <= 2 ** -23 * abs(float(ex))
+    yt = orc.dequant(acc, xs, ws[:1], 1, None)
+    assert np.allclose(yt, acc.astype(np.float64) * xs[:, None] * float(ws[0]), rtol=0, atol=0)
+
+
+def test_dequant_rounding_bound_general(orc):
+    rng = np.random.default_rng(42)
+    acc = rng.integers(-3 * 10**8, 3 * 10**8, (16, 16)).astype(np.int32)
+    xs = rng.uniform(1e-4, 1e-1, 16).astype(np.float32)
+    ws = rng.uniform(1e-5, 1e-2, 16).astype(np.float32)
+    y = orc.dequant(acc, xs, ws, 0, None).astype(np.float64)
+    ref = acc.astype(np.float64) * xs.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]
+    assert np.all(np.abs(y - ref) <= 3 * 2.0 ** -24 * np.abs(ref))
+    rows = rng.integers(0, 16, 40)
+    cols = rng.integers(0, 16, 40)
+    assert np.array_equal(orc.dequant_sampled(acc[rows, cols], xs, ws, 0, None, rows, cols),
+                          orc.dequant(acc, xs, ws, 0, None)[rows, cols])
+
+
+def test_half_store_is_numpy_rne(orc):
+    y = np.random.default_rng(43).standard_normal(5000).astype(np.float32) * 30
+    assert np.array_equal(orc.float_to_half(y).view(np.uint16), y.astype(np.float16).view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# Whole W8A8 layer: error bounded by the quantization steps
+# --------------------------------------------------------------------------
+
+def test_w8a8_layer_error_bound(orc):
+    """|Y - X W^T| is bounded by the propagated quantization errors,
+    sum_k (xs/2 |W'| + |X'| ws/2 + xs ws / 4); a smoothing applied to the wrong
+    axis or a dequant missing a factor breaks it by orders of magnitude."""
+    X, W, _ = workloads.random_layer(51, 32, 512, 64, np.float32, n_outliers=4)
+    _, s = orc.smooth_scales(X, W, 0.5)
+    Wq, ws = orc.quantize_weight(W, s, 0)
+    _, xs, _, Y = orc.w8a8_linear(X, s, Wq, ws, 0, None, np.float32)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    Xs = X.astype(np.float64) / s
+    Ws = W.astype(np.float64) * s
+    xs64, ws64 = xs.astype(np.float64)[:, None], ws.astype(np.float64)[None, :]
+    bound = (xs64 / 2) * np.abs(Ws).sum(1)[None, :] + np.abs(Xs).sum(1)[:, None] * (ws64 / 2) \
+        + xs64 * ws64 / 4 * X.shape[1]
+    assert np.all(np.abs(Y - ref) <= bound * 1.001 + 1e-6)
+    snr = 10 * np.log10(np.var(ref) / np.var(Y - ref))
+    assert snr > 20
+
+
+# --------------------------------------------------------------------------
+# LLM.int8() decomposition
+# --------------------------------------------------------------------------
+
+def _small_llm_case(seed=61, M=48, K=256, N=40, n_out=3):
+    X, W, idx = workloads.random_layer(seed, M, K, N, np.float16, n_outliers=n_out, factor=20.0)
+    return X, W, idx
+
+
+def test_outlier_columns_are_numpy_column_max(orc):
+    X, _, idx = _small_llm_case()
+    mask, got = orc.outlier_columns(X, 6.0)
+    ref = np.abs(X.astype(np.float32)).max(0) > 6.0
+    assert np.array_equal(mask.astype(bool), ref)
+    assert np.array_equal(got, np.nonzero(ref)[0])
+    X2 = X.copy()
+    X2[0, 0] = np.float16(6.0)                     # equal to the threshold: not an outlier
+    X2[1:, 0] = 0
+    assert orc.outlier_columns(X2, 6.0)[0][0] == 0
+
+
+def test_llm_int8_no_outliers_reduces_to_w8a8(orc):
+    X, W, _ = _small_llm_case()
+    Wq, ws = orc.quantize_weight(W, None, 0)
+    mask, idx, Xq, xs, acc, Y = orc.llm_int8_linear(X, W, Wq, ws, np.inf)
+    assert idx.size == 0
+    Xq2, xs2, acc2, Y2 = orc.w8a8_linear(X, None, Wq, ws, 0, None, np.float16)
+    assert np.array_equal(Xq, Xq2) and np.array_equal(xs, xs2) and np.array_equal(acc, acc2)
+    assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+
+
+def test_llm_int8_all_outliers_is_fp16_gemm(orc):
+    X, W, _ = _small_llm_case()
+    X = np.where(X == 0, np.float16(0.5), X)
+    Wq, ws = orc.quantize_weight(W, None, 0)
+    _, idx, Xq, xs, acc, Y = orc.llm_int8_linear(X, W, Wq, ws, 0.0)
+    assert idx.size == X.shape[1]
+    assert np.all(Xq == 0) and np.all(xs == 0) and np.all(acc == 0)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(Y.astype(np.float64), ref, rtol=1e-3, atol=1e-3 * np.abs(ref).mean())
+
+
+def test_llm_int8_outlier_magnitude_does_not_touch_int8_part(orc):
+    """The per-token scale is taken over normal columns only: scaling the outlier
+    columns changes neither Xq nor x_scale, and the fp16 side product carries them."""
+    X, W, idx = _small_llm_case()
+    Wq, ws = orc.quantize_weight(W, None, 0)
+    r1 = orc.llm_int8_linear(X, W, Wq, ws, 6.0)
+    X2 = X.copy()
+    X2[:, r1[1]] *= np.float16(2)
+    r2 = orc.llm_int8_linear(X2, W, Wq, ws, 6.0)
+    assert np.array_equal(r1[1], r2[1])
+    assert np.array_equal(r1[2], r2[2]) and np.array_equal(r1[3], r2[3])
+    assert np.all(r1[2][:, r1[1]] == 0)
+    # decomposition = int8 part + exact side product over the listed columns
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    err = np.abs(r1[5].astype(np.float64) - ref)
+    assert np.median(err / (np.abs(ref) + np.abs(ref).mean())) < 2e-2
+
+
+def test_side_product_vs_numpy(orc):
+    X, W, _ = _small_llm_case()
+    idx = np.array([3, 17, 100, 255], np.int32)
+    M, N = X.shape[0], W.shape[0]
+    rr = np.repeat(np.arange(M), N)
+    cc = np.tile(np.arange(N), M)
+    side = orc.side_product_sampled(X, W, idx, rr, cc).reshape(M, N)
+    ref = X[:, idx].astype(np.float64) @ W[:, idx].astype(np.float64).T
+    assert np.allclose(side, ref, rtol=1e-14, atol=0)
+
+
+def test_quantize_divides_by_scale(orc):
+    """The basics notes and the SmoothQuant page divide by scale = max/127 (the
+    LLM.int8() page's multiply-by-127/max form is not taken).  Rows built so that
+    x/scale and x*(1/scale) round to different codes must follow the division
+    (numpy IEEE fp32 division and rint, library routines)."""
+    rng = np.random.default_rng(0)
+    rows = []
+    while len(rows) < 8:
+        a = np.float32(rng.uniform(1, 100))
+        sc = np.float32(a / np.float32(127))
+        r = np.float32(np.float32(1) / sc)
+        x = np.float32((rng.integers(-126, 126) + 0.5) * float(sc))
+        for d in range(-3, 4):
+            xx = x
+            for _ in range(abs(d)):
+                xx = np.nextafter(xx, np.float32(np.inf) if d > 0 else np.float32(-np.inf))
+            if abs(xx) < a and np.rint(xx / sc) != np.rint(xx * r):
+                rows.append((a, xx, np.rint(xx / sc)))
+                break
+    X = np.array([[a, xx] for a, xx, _ in rows], np.float32)
+    Xq, xs = orc.quantize_per_token(X)
+    assert Xq[:, 0].tolist() == [127] * len(rows)
+    assert Xq[:, 1].tolist() == [int(q) for _, _, q in rows]
