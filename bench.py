@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized INT8 linear layer on one MI355X.
+
+One step = one forward of the W8A8 layer on the 7B-shaped prefill workload:
+for each of the fused QKV (12288 x 4096) and FFN-up (11008 x 4096) weights,
+fused smoothing + per-token quantization of X [2048 x 4096] fp16, then the
+int8 MFMA GEMM with the dequant epilogue writing fp16 Y.  Weight preparation
+(calibration, smoothing factors, weight quantization) happens once, before the
+timed region.  Inputs are resident in HBM when timing starts.
+
+value = 2*M*(N_qkv + N_up)*K / step time, in TOPS, quantization included.
+roofline: the GEMM kernel, its algorithmic 2MNK ops per launch over its
+average launch time (HIP events around each launch, inside the timed region),
+against the 5.0 POP/s dense int8 MFMA peak.
+cpu_baseline: the CPU oracle doing the same per-token work on a bounded
+number of token rows, on this host's cores.
+secondary: the decode (GB/s), LLM.int8() and 530B-slice workloads, same method.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 linear TOPS incl. quant+dequant (% int8 MFMA peak); decode GB/s (% HBM peak)"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SRC = os.path.join(ROOT, "int8_quantization_amd", "csrc", "gemm.hip")
+GEMV_SRC = os.path.join(ROOT, "int8_quantization_amd", "csrc", "gemv.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(key, src):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if the kernel source is unchanged since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE)).get(key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha") != sha(src):
+        return None
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+
+
+class Timer:
+    """Events recorded on torch's current stream, which is the stream every
+    library call launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def around(self, fn):
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.append((a, b))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(timer)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, timer.mean_ms()
+
+
+def prepare_weight(torch, sq, d, X_cal, W, alpha, gran):
+    """Offline: calibration max, smoothing factors, smoothed weight quantization (GPU)."""
+    N, K = W.shape
+    act = torch.zeros(K, dtype=torch.float32, device="cuda")
+    s = torch.empty(K, dtype=torch.float32, device="cuda")
+    W_d = d(W)
+    if alpha is None:
+        s = None
+    else:
+        sq.sq_smooth_scales(d(X_cal), W_d, alpha, act, s)
+    Wq = torch.empty(N, K, dtype=torch.int8, device="cuda")
+    ws = torch.empty(N if gran == 0 else 1, dtype=torch.float32, device="cuda")
+    wsp = torch.empty(sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, N, K), dtype=torch.uint8, device="cuda")
+    sq.sq_quantize_weight(W_d, s, gran, Wq, ws, wsp)
+    torch.cuda.synchronize()
+    del W_d
+    return s, Wq, ws
+
+
+def bench_w8a8(torch, sq, d, wl, steps, warmup):
+    """Prefill-style W8A8 forward over every weight of the workload."""
+    M, K = wl.X.shape
+    X = d(wl.X)
+    projs = []
+    for name, W in wl.weights.items():
+        s, Wq, ws = prepare_weight(torch, sq, d, wl.calib, W, wl.alpha, wl.gran)
+        Y = torch.empty(M, W.shape[0], dtype=torch.float16 if wl.out_dtype == np.float16 else torch.float32,
+                        device="cuda")
+        projs.append((name, s, Wq, ws, Y))
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+
+    def step(timer):
+        for _, s, Wq, ws, Y in projs:
+            sq.sq_quantize_per_token(X, s, Xq, xs)
+            g = lambda: sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, wl.gran, None, Y)
+            timer.around(g) if timer else g()
+
+    ms, gemm_ms = time_steps(torch, step, steps, warmup)
+    ops = sum(2.0 * M * p[2].shape[0] * K for p in projs)
+    return dict(ms=ms, gemm_ms=gemm_ms, ops=ops, gemm_ops_per_launch=ops / len(projs),
+                Ns=[p[2].shape[0] for p in projs])
+
+
+def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
+    """M in {1,4,16} against 3 rotated copies of the int8 weight (705 MB > 256 MB MALL)."""
+    W = wl.weights["w"]
+    N, K = W.shape
+    s, Wq0, ws = prepare_weight(torch, sq, d, wl.calib, W, wl.alpha, wl.gran)
+    Wqs = [Wq0] + [Wq0.clone() for _ in range(copies - 1)]
+    out = {}
+    for M in wl.decode_rows:
+        X = d(wl.X[:M])
+        Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+        xs = torch.empty(M, dtype=torch.float32, device="cuda")
+        Y = torch.empty(M, N, dtype=torch.float16, device="cuda")
+        it = [0]
+
+        def step(timer):
+            Wq = Wqs[it[0] % copies]
+            it[0] += 1
+            sq.sq_quantize_per_token(X, s, Xq, xs)
+            g = lambda: sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
+            timer.around(g) if timer else g()
+
+        ms, gemv_ms = time_steps(torch, step, steps, warmup)
+        nbytes = N * K + 4 * N + 2 * M * K + 2 * M * K + 4 * M + 2 * M * N
+        out[f"M{M}"] = dict(ms_per_step=ms, GBps=nbytes / (ms * 1e-3) / 1e9,
+                            hbm_frac=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            gemv_us=gemv_ms * 1e3,
+                            gemv_GBps=(N * K + 4 * N + M * K + 2 * M * N) / (gemv_ms * 1e-3) / 1e9)
+    return out
+
+
+def bench_llm_int8(torch, sq, d, wl, steps, warmup):
+    X, W16 = wl.X, wl.weights["w"]
+    M, K = X.shape
+    N = W16.shape[0]
+    _, Wq, ws = prepare_weight(torch, sq, d, None, W16, None, 0)
+    Xd, Wd = d(X), d(W16)
+    Y = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    wsp = torch.empty(sq.sq_workspace_size(sq.SQ_OP_OUTLIER, M, N, K), dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(timer):
+        sq.int8_outlier_matmul(Xd, Wd, Wq, ws, None, wl.threshold, Y, wsp, cnt)
+
+    ms, _ = time_steps(torch, step, steps, warmup)
+    ops = 2.0 * M * N * K
+    return dict(ms_per_step=ms, TOPS=ops / (ms * 1e-3) / 1e12, mfma_frac=ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                n_outliers=int(cnt.item()))
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle on the same per-token work (quantize + int8 GEMM + dequant +
+    fp16 store, every projection) for a bounded number of token rows."""
+    import oracle
+    prepared = []
+    for name, W in wl.weights.items():
+        s = oracle.smooth_scales(wl.calib, W, wl.alpha)[1] if wl.alpha is not None else None
+        Wq, ws = oracle.quantize_weight(W, s, wl.gran)
+        prepared.append((s, Wq, ws))
+
+    def run(rows):
+        t = time.perf_counter()
+        for s, Wq, ws in prepared:
+            oracle.w8a8_linear(wl.X[:rows], s, Wq, ws, wl.gran, None, wl.out_dtype)
+        return time.perf_counter() - t
+
+    r0 = 8
+    t0 = run(r0)
+    rows = int(min(wl.X.shape[0], max(r0, round(r0 * target_s / max(t0, 1e-6)))))
+    t = run(rows)
+    K = wl.X.shape[1]
+    ops = sum(2.0 * rows * W.shape[0] * K for W in wl.weights.values())
+    return dict(value=ops / t / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {rows} of {wl.X.shape[0]} token rows, all {len(wl.weights)} projections "
+                       f"({ops / 1e9:.1f} GOP in {t:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", default=None, help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs the layer on a single MI355X).", flush=True)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": a.numel() * 4, "launches": 5}))
+        return
+
+    import int8_quantization_amd as sq
+    import workloads
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    result = {}
+    secondary = {}
+    if args.only in (None, "prefill_7b"):
+        log("prefill_7b: generating inputs")
+        wl = workloads.prefill_7b()
+        log("prefill_7b: timing")
+        r = bench_w8a8(torch, sq, d, wl, args.steps, args.warmup)
+        tops = r["ops"] / (r["ms"] * 1e-3) / 1e12
+        gemm_tops = r["gemm_ops_per_launch"] / (r["gemm_ms"] * 1e-3) / 1e12
+        traffic = traffic_for("gemm_prefill_7b", GEMM_SRC)
+        result = {
+            "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["ms"], 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": r["Ns"], "alpha": wl.alpha,
+                       "weight_scale": "per_channel", "act_scale": "per_token", "out_dtype": "fp16",
+                       "parallelism": "single_gpu"},
+            "mfma_frac_incl_quant": round(tops / PEAK_INT8_TOPS, 4),
+            "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                         "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                         "kernel": "gemm_i8_kernel<256,256,fp16>", "gemm_us_per_launch": round(r["gemm_ms"] * 1e3, 2),
+                         "algorithmic_ops_per_launch": r["gemm_ops_per_launch"]},
+        }
+        if not args.no_cpu_baseline:
+            log("prefill_7b: CPU oracle baseline")
+            result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        del wl
+    if not args.quick:
+        sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
+        if args.only in (None, "decode_70b"):
+            log("decode_70b: generating inputs")
+            secondary["decode_70b"] = bench_decode(torch, sq, d, workloads.decode_70b(), sec_steps * 2, sec_warm)
+        if args.only in (None, "llm_int8"):
+            log("llm_int8: generating inputs")
+            secondary["llm_int8"] = bench_llm_int8(torch, sq, d, workloads.llm_int8_4096(), sec_steps, sec_warm)
+        if args.only in (None, "slice_530b"):
+            log("slice_530b: generating inputs")
+            wl5 = workloads.slice_530b()
+            r = bench_w8a8(torch, sq, d, wl5, sec_steps, sec_warm)
+            secondary["slice_530b"] = dict(ms_per_step=r["ms"], TOPS=r["ops"] / (r["ms"] * 1e-3) / 1e12,
+                                           gemm_TOPS=r["gemm_ops_per_launch"] / (r["gemm_ms"] * 1e-3) / 1e12)
+            del wl5
+        torch.cuda.empty_cache()
+        result["secondary"] = secondary
+    if not result.get("metric"):
+        result = {"metric": METRIC, "value": None, "secondary": secondary}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * sq.h -- C ABI of the MI355X (gfx950) quantized INT8 linear layer.
+ *
+ * The layer computes Y = X W^T for X [M x K] (tokens x in_features) and
+ * W [N x K] (out_features x in_features, the PyTorch Linear layout) through
+ *   1. SmoothQuant smoothing X diag(s)^-1 and diag(s) W, with
+ *      s_j = max|X_j|^alpha / max|W_j|^(1-alpha)
+ *      ("SmoothQuant量化实战：W8A8推理部署与单节点530B模型落地", sections 1.3, 2.1, 3.3);
+ *   2. symmetric absmax int8 quantization, scale = max|x|/127, q = round(x/scale)
+ *      clamped to [-128, 127]: per token (row) for activations, per output
+ *      channel or per tensor for weights ("量化基础与INT8", sections 量化粒度 and
+ *      量化流程示例);
+ *   3. an int8 x int8 -> int32 GEMM ("量化基础与INT8", section INT8推理流程);
+ *   4. the dequantizing epilogue Y = acc * x_scale * w_scale (+ bias), stored as
+ *      fp16 or fp32 (same section; bias kept in floating point: SmoothQuant page,
+ *      section 4.5);
+ * and the LLM.int8() variant, where activation columns whose absolute maximum
+ * exceeds a threshold bypass int8 and are multiplied in fp16, the two partial
+ * products being summed ("LLM.int8()技术解析：8位量化如何优化大语言模型计算",
+ * sections 2.1 and 3.1).
+ *
+ * Numerics, common to all entry points:
+ *  - every floating-point step is one IEEE binary32 operation, round to nearest
+ *    even; rounding to an integer code is half-to-even; fp16 inputs are widened
+ *    exactly; fp16 outputs are rounded to nearest even.
+ *  - quantizing divides by the scale; a row (or tensor) whose absolute maximum
+ *    is 0 gets scale 0 and all-zero codes.
+ *  - int32 accumulation is exact for K <= 131071 (|acc| <= 127^2 K < 2^31).
+ *  The int8 codes, the scales and the int32 accumulators are therefore fully
+ *  determined by the inputs.
+ *
+ * Conventions, common to all entry points:
+ *  - Ownership: the caller allocates and owns every buffer; the library never
+ *    allocates, frees, copies device-to-host or synchronizes.
+ *  - Pointers marked "device" are HIP device pointers; all are 16-byte aligned,
+ *    dense, row-major, and outputs do not alias inputs.
+ *  - Streams: every call enqueues its kernels on `stream` (NULL = the default
+ *    stream) and returns without waiting.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on a non-zero status nothing was enqueued, except SQ_ERR_HIP, which
+ *    reports a failed launch (kernels enqueued before it may run).  Faults
+ *    inside kernels surface at the caller's next synchronization, as in HIP.
+ *    Inputs must be finite (NaN/Inf give unspecified codes).
+ *  - Sizes: M, N >= 1; 16 <= K <= 131056 and K % 16 == 0.
+ *  - Thread safety: calls are reentrant; calls that share output or workspace
+ *    buffers must be ordered by the caller (same stream or events).
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (the same declaration as in the HIP headers). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_NULL = 1,      /* a required pointer is NULL */
+    SQ_ERR_SHAPE = 2,     /* M, N or K out of range, or K % 16 != 0 */
+    SQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+    SQ_ERR_DTYPE = 4,     /* unsupported dtype or granularity code */
+    SQ_ERR_VALUE = 5,     /* alpha outside [0,1], threshold negative or NaN */
+    SQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than sq_workspace_size() */
+    SQ_ERR_HIP = 7        /* a HIP launch or device query failed */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_F16 = 1 } sq_dtype;
+typedef enum { SQ_PER_CHANNEL = 0, SQ_PER_TENSOR = 1 } sq_wgran;
+typedef enum { SQ_OP_QUANT_WEIGHT = 0, SQ_OP_OUTLIER = 1 } sq_op;
+
+/* Static, human-readable name of a status code. */
+const char* sq_status_string(sq_status st);
+
+/* Bytes of device workspace an entry point needs.
+ *   SQ_OP_QUANT_WEIGHT: for sq_quantize_weight (M ignored).
+ *   SQ_OP_OUTLIER:      for int8_outlier_matmul; sized for the worst case of
+ *                       all K columns being outliers: (M + N) * K * 2 + 16 * K + 1024.
+ * Returns 0 for an unknown op or sizes out of range. */
+size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K);
+
+/* Calibration and smoothing factors (offline).
+ * [SmoothQuant page, section 3.2: running per-channel max of the activations;
+ *  section 3.3: compute_smooth_scale with both maxima floored at 1e-8;
+ *  section 2.1: s_j = max|X_j|^alpha / max|W_j|^(1-alpha).]
+ *   X_cal   device, [M_cal x K] in xdt; may be NULL when M_cal == 0.
+ *   act_max device, float [K], in/out: act_max[j] = max(act_max[j], max_m |X_cal[m,j]|).
+ *           Start it at zeros; call once per calibration batch.
+ *   W       device, [N x K] in wdt.  If W == NULL only act_max is updated and s may be NULL.
+ *   s       device, float [K], out:
+ *           s_j = (float)( pow((double)max(act_max_j,1e-8f), alpha)
+ *                        / pow((double)max(max_n |W[n,j]|, 1e-8f), 1 - alpha) ),
+ *           pow in fp64 (the device and host pow may differ in the last fp32 ulp).
+ *   alpha   in [0, 1].
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_HIP. */
+sq_status sq_smooth_scales(const void* X_cal, sq_dtype xdt, int64_t M_cal,
+                           const void* W, sq_dtype wdt, int64_t N, int64_t K, float alpha,
+                           float* act_max, float* s, hipStream_t stream);
+
+/* Fused smoothing + dynamic per-token activation quantization (every forward).
+ * [basics notes, 量化流程示例: per-row absmax scale, round, clamp;
+ *  SmoothQuant page, sections 3.3-3.4: X' = X / s before quantizing.]
+ *   X       device, [M x K] in xdt (fp16 or fp32).
+ *   s       device, float [K], or NULL for no smoothing.
+ *   Xq      device, int8 [M x K], out: clamp(rne(fl32(x'_j / xs)), -128, 127),
+ *           x'_j = fl32(x_j / s_j) (x_j when s == NULL).
+ *   x_scale device, float [M], out: xs = fl32(max_j |x'_j| / 127).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status sq_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K,
+                                const float* s, int8_t* Xq, float* x_scale, hipStream_t stream);
+
+/* Weight smoothing + quantization (offline).
+ * [SmoothQuant page, section 3.3: W' = W * s along in_features;
+ *  basics notes, 量化粒度: per-tensor or per-output-channel absmax scales.]
+ *   W       device, [N x K] in wdt.
+ *   s       device, float [K], or NULL for no smoothing: W'[n,j] = fl32(W[n,j] * s_j).
+ *   g       SQ_PER_CHANNEL: w_scale[n] = fl32(max_j |W'[n,j]| / 127), float [N];
+ *           SQ_PER_TENSOR:  w_scale[0] = fl32(max_{n,j} |W'| / 127), float [1].
+ *   Wq      device, int8 [N x K], out: clamp(rne(fl32(W' / w_scale)), -128, 127).
+ *   ws      device workspace of ws_bytes >= sq_workspace_size(SQ_OP_QUANT_WEIGHT, 0, N, K)
+ *           (only SQ_PER_TENSOR uses it; may be NULL for SQ_PER_CHANNEL).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
+sq_status sq_quantize_weight(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s,
+                             sq_wgran g, int8_t* Wq, float* w_scale, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* int8 GEMM with fused dequantization.
+ * [basics notes, INT8推理流程 and 量化流程示例: int32 accumulation, then
+ *  acc * X_scale * W_scale; SmoothQuant page, section 3.4 and 4.5: + bias.]
+ *   Xq [M x K] int8, x_scale float [M], Wq [N x K] int8, all device.
+ *   w_scale float [N] (SQ_PER_CHANNEL) or [1] (SQ_PER_TENSOR), device.
+ *   bias    device float [N], or NULL.
+ *   acc[m,n] = sum_k Xq[m,k] * Wq[n,k]            (exact int32)
+ *   Y[m,n]   = ((fl32(acc) * x_scale[m]) * w_scale[n or 0]) + bias[n],
+ *              each step one fp32 operation, stored as ydt (fp16 rounded to nearest even).
+ *   Y       device, [M x N] in ydt.
+ *   acc_out device int32 [M x N], or NULL; when given, acc is written too (parity checks).
+ * M <= 16 runs a weight-streaming decode kernel; larger M the MFMA tile kernel.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status w8a8_gemm_dequant(const int8_t* Xq, const float* x_scale, const int8_t* Wq,
+                            const float* w_scale, sq_wgran g, const float* bias,
+                            int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                            int32_t* acc_out, hipStream_t stream);
+
+/* LLM.int8() linear layer (no smoothing).
+ * [LLM.int8() page, section 2.1: column-wise absmax of the input, columns above
+ *  the threshold are outliers; section 3.1: bitmask of outlier columns, int8 GEMM
+ *  over the normal columns, fp16 GEMM over the outlier columns, results combined.]
+ *   X        device fp16 [M x K];  W16 device fp16 [N x K] (the unquantized weight).
+ *   Wq, w_scale  device, from sq_quantize_weight(W16, s = NULL, SQ_PER_CHANNEL).
+ *   bias     device float [N], or NULL.
+ *   threshold >= 0: column j is an outlier iff max_m |X[m,j]| > threshold.
+ *   The int8 part quantizes each row over its non-outlier columns only (outlier
+ *   columns get code 0 and stay out of the row maximum), then runs the int8 GEMM
+ *   and the dequant epilogue (+ bias).  The side part is
+ *   side[m,n] = sum over outlier j of X[m,j] * W16[n,j] (fp16 products, fp32 sum).
+ *   Y[m,n] = fp16(y_int8[m,n] + side[m,n]).   Y: device fp16 [M x N].
+ *   ws, ws_bytes  device workspace >= sq_workspace_size(SQ_OP_OUTLIER, M, N, K).
+ *   n_outliers    device int32 [1] or NULL: receives the number of outlier columns.
+ *   outlier_idx   device int32 [K] or NULL: receives them in ascending order.
+ *   acc_out       device int32 [M x N] or NULL: the int8 part's accumulators.
+ * The outlier count stays on the device; no host synchronization happens.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_VALUE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
+sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq,
+                              const float* w_scale, const float* bias,
+                              int64_t M, int64_t N, int64_t K, float threshold, void* Y,
+                              void* ws, size_t ws_bytes, int32_t* n_outliers,
+                              int32_t* outlier_idx, int32_t* acc_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SQ_H */

@@ -1,0 +1,137 @@
+"""MI355X (gfx950) quantized INT8 linear layer -- Python binding of libsq.so.
+
+Every function here marshals torch tensors (device memory, the current HIP
+stream) into the C ABI declared in include/sq.h and raises SqError on a
+non-zero status.  All computation happens in the HIP kernels of libsq.so; if
+the library is missing, importing the binding fails loudly -- there is no
+fallback.
+
+Names match the C entry points:
+  sq_smooth_scales, sq_quantize_per_token, sq_quantize_weight,
+  w8a8_gemm_dequant, int8_outlier_matmul, sq_workspace_size, sq_status_string.
+"""
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
+
+SQ_F32, SQ_F16 = 0, 1
+SQ_PER_CHANNEL, SQ_PER_TENSOR = 0, 1
+SQ_OP_QUANT_WEIGHT, SQ_OP_OUTLIER = 0, 1
+
+
+class SqError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn}: {sq_status_string(code)} (status {code})")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    lib = C.CDLL(LIB_PATH)
+    P, I64, F, I, SZ = C.c_void_p, C.c_int64, C.c_float, C.c_int, C.c_size_t
+    sigs = {
+        "sq_status_string": (C.c_char_p, [I]),
+        "sq_workspace_size": (SZ, [I, I64, I64, I64]),
+        "sq_smooth_scales": (I, [P, I, I64, P, I, I64, I64, F, P, P, P]),
+        "sq_quantize_per_token": (I, [P, I, I64, I64, P, P, P, P]),
+        "sq_quantize_weight": (I, [P, I, I64, I64, P, I, P, P, P, SZ, P]),
+        "w8a8_gemm_dequant": (I, [P, P, P, P, I, P, I64, I64, I64, P, I, P, P]),
+        "int8_outlier_matmul": (I, [P, P, P, P, P, I64, I64, I64, F, P, P, SZ, P, P, P, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quantize_per_token",
+           "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul")
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype == torch.float16:
+        return SQ_F16
+    if t.dtype == torch.float32:
+        return SQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dense(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _check(fn, code):
+    if code != 0:
+        raise SqError(fn, code)
+
+
+def sq_status_string(code: int) -> str:
+    return _lib.sq_status_string(int(code)).decode()
+
+
+def sq_workspace_size(op: int, M: int, N: int, K: int) -> int:
+    return int(_lib.sq_workspace_size(int(op), int(M), int(N), int(K)))
+
+
+def sq_smooth_scales(X_cal, W, alpha, act_max, s):
+    """act_max [K] fp32 (running max, in/out); s [K] fp32 out. X_cal or W may be None."""
+    _dense(X_cal, W, act_max, s)
+    K = act_max.shape[0]
+    Mc = 0 if X_cal is None else X_cal.shape[0]
+    N = 0 if W is None else W.shape[0]
+    _check("sq_smooth_scales", _lib.sq_smooth_scales(
+        _p(X_cal), SQ_F32 if X_cal is None else _dt(X_cal), Mc, _p(W), SQ_F32 if W is None else _dt(W),
+        N, K, float(alpha), _p(act_max), _p(s), _stream()))
+
+
+def sq_quantize_per_token(X, s, Xq, x_scale):
+    _dense(X, s, Xq, x_scale)
+    M, K = X.shape
+    _check("sq_quantize_per_token", _lib.sq_quantize_per_token(
+        _p(X), _dt(X), M, K, _p(s), _p(Xq), _p(x_scale), _stream()))
+
+
+def sq_quantize_weight(W, s, gran, Wq, w_scale, ws=None):
+    _dense(W, s, Wq, w_scale, ws)
+    N, K = W.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("sq_quantize_weight", _lib.sq_quantize_weight(
+        _p(W), _dt(W), N, K, _p(s), int(gran), _p(Wq), _p(w_scale), _p(ws), nbytes, _stream()))
+
+
+def w8a8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
+    _dense(Xq, x_scale, Wq, w_scale, bias, Y, acc_out)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    _check("w8a8_gemm_dequant", _lib.w8a8_gemm_dequant(
+        _p(Xq), _p(x_scale), _p(Wq), _p(w_scale), int(gran), _p(bias), M, N, K, _p(Y), _dt(Y),
+        _p(acc_out), _stream()))
+
+
+def int8_outlier_matmul(X, W16, Wq, w_scale, bias, threshold, Y, ws, n_outliers=None,
+                        outlier_idx=None, acc_out=None):
+    _dense(X, W16, Wq, w_scale, bias, Y, ws, n_outliers, outlier_idx, acc_out)
+    M, K = X.shape
+    N = W16.shape[0]
+    nbytes = ws.numel() * ws.element_size()
+    _check("int8_outlier_matmul", _lib.int8_outlier_matmul(
+        _p(X), _p(W16), _p(Wq), _p(w_scale), _p(bias), M, N, K, float(threshold), _p(Y), _p(ws),
+        nbytes, _p(n_outliers), _p(outlier_idx), _p(acc_out), _stream()))

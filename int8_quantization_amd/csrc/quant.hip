@@ -1,0 +1,455 @@
+// Quantization-side kernels for gfx950:
+//  - fused smoothing + per-row absmax int8 quantization (activations per token,
+//    weights per output channel) ["量化基础与INT8", 量化粒度 / 量化流程示例;
+//    "SmoothQuant量化实战", sections 3.3-3.4];
+//  - calibration column absmax and the smoothing factors [SmoothQuant page,
+//    sections 2.1, 3.2, 3.3];
+//  - per-tensor weight quantization [basics notes, 量化粒度].
+// All of these are HBM-bound: 16-byte coalesced loads, wave-shuffle reductions,
+// packed int8 stores.
+#include <mutex>
+
+#include "sq_internal.h"
+
+namespace sq {
+
+// ---------------------------------------------------------------------------
+// Device info
+// ---------------------------------------------------------------------------
+const DevInfo& dev_info() {
+    static DevInfo info[64];
+    static std::once_flag once[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    std::call_once(once[dev], [dev]() {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        info[dev].cus = cus;
+        info[dev].xcds = 8;
+    });
+    return info[dev];
+}
+
+// ---------------------------------------------------------------------------
+// Fill
+// ---------------------------------------------------------------------------
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte chunk types
+// ---------------------------------------------------------------------------
+template <typename T> struct Chunk;
+template <> struct Chunk<_Float16> {
+    using V = h8;
+    static constexpr int N = 8;
+};
+template <> struct Chunk<float> {
+    using V = v4f;
+    static constexpr int N = 4;
+};
+
+template <int VEC> struct CodeStore;
+template <> struct CodeStore<8> {
+    static __device__ __forceinline__ void store(int8_t* p, const int* q) {
+        uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                      ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+        uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
+                      ((uint32_t)(q[6] & 0xff) << 16) | ((uint32_t)(q[7] & 0xff) << 24);
+        *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+    }
+};
+template <> struct CodeStore<4> {
+    static __device__ __forceinline__ void store(int8_t* p, const int* q) {
+        *reinterpret_cast<uint32_t*>(p) = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                                          ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Fused smoothing + per-row quantization, register-resident rows.
+//
+// A block of T threads owns whole rows; thread t owns the 16-byte chunks
+// t, t+T, ... (CH of them) of every row it visits, so the per-column constants
+// (reciprocal of s_j, or s_j, or the outlier slot) are computed once per block
+// and kept in registers, and blocks loop over rows m = blockIdx.x + i*gridDim.x
+// with the next row's loads issued before the current row's reduction.
+//   mode 0: x' = x;   mode 1: x' = fl32(x / s_j);   mode 2: x' = fl32(x * s_j)
+//   xs = fl32(max |x'| / 127) over non-outlier columns
+//   q  = clamp(rne(fl32(x' / xs)), -128, 127), 0 for outlier columns or xs == 0
+// ---------------------------------------------------------------------------
+template <typename T, int CH, int MODE, bool OUTL>
+__global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X, int64_t M, int64_t K,
+                                                        const float* __restrict__ s, int8_t* __restrict__ Xq,
+                                                        float* __restrict__ scale, const int32_t* __restrict__ pos,
+                                                        _Float16* __restrict__ Xo) {
+    using V = typename Chunk<T>::V;
+    constexpr int VEC = Chunk<T>::N;
+    __shared__ float red[2][16];
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int wave = tid >> 6, lane = tid & 63, nwaves = nthr >> 6;
+    const int64_t nchunk = K / VEC;
+
+    double rs[MODE == 1 ? CH : 1][VEC];
+    float sv[MODE == 2 ? CH : 1][VEC];
+    int pv[OUTL ? CH : 1][VEC];
+    bool valid[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        int64_t c = tid + (int64_t)i * nthr;
+        valid[i] = c < nchunk;
+        int64_t cc = valid[i] ? c : 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (MODE == 1) rs[i][e] = 1.0 / (double)s[cc * VEC + e];
+            if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
+            if constexpr (OUTL) pv[i][e] = valid[i] ? pos[cc * VEC + e] : -1;
+        }
+    }
+
+    V rc[CH], rn[CH];
+    auto load_row = [&](int64_t row, V* r) {
+        const V* src = reinterpret_cast<const V*>(X + row * K);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            int64_t c = tid + (int64_t)i * nthr;
+            if (valid[i]) r[i] = src[c];
+            else r[i] = V{};
+        }
+    };
+
+    int64_t m = blockIdx.x;
+    if (m < M) load_row(m, rc);
+    int it = 0;
+    for (; m < M; m += gridDim.x, ++it) {
+        float xv[CH][VEC];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            int64_t c = tid + (int64_t)i * nthr;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float x = (float)rc[i][e];
+                if constexpr (MODE == 1) {
+                    float q = (float)((double)x * rs[i][e]);
+                    if (__builtin_fabsf(q) < 1.17549435e-38f && x != 0.0f) q = x / s[c * VEC + e];
+                    x = q;
+                }
+                if constexpr (MODE == 2) x = x * sv[i][e];
+                xv[i][e] = x;
+                bool skip = false;
+                if constexpr (OUTL) {
+                    skip = pv[i][e] >= 0;
+                    if (skip) Xo[m * K + pv[i][e]] = (_Float16)rc[i][e];
+                }
+                if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
+            }
+        }
+        int64_t mn = m + gridDim.x;
+        if (mn < M) load_row(mn, rn);
+
+        amax = wave_max(amax);
+        if (lane == 0) red[it & 1][wave] = amax;
+        __syncthreads();
+        float a = red[it & 1][0];
+        for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[it & 1][w]);
+        const float xs = a / 127.0f;
+        if (tid == 0) scale[m] = xs;
+        const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            if (!valid[i]) continue;
+            int64_t c = tid + (int64_t)i * nthr;
+            int q[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                bool zero = xs == 0.0f;
+                if constexpr (OUTL) zero = zero || pv[i][e] >= 0;
+                q[e] = zero ? 0 : code_of(div_rcp64(xv[i][e], rx, xs));
+            }
+            CodeStore<VEC>::store(Xq + m * K + c * VEC, q);
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) rc[i] = rn[i];
+    }
+}
+
+// Fallback for rows too long to keep in registers: two passes over the row
+// (the second from cache), IEEE divisions.
+template <typename T, int MODE, bool OUTL>
+__global__ __launch_bounds__(1024) void quant_rows_generic(const T* __restrict__ X, int64_t M, int64_t K,
+                                                           const float* __restrict__ s, int8_t* __restrict__ Xq,
+                                                           float* __restrict__ scale,
+                                                           const int32_t* __restrict__ pos,
+                                                           _Float16* __restrict__ Xo) {
+    __shared__ float red[2][16];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int wave = tid >> 6, lane = tid & 63, nwaves = nthr >> 6;
+    int it = 0;
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x, ++it) {
+        const T* row = X + m * K;
+        float amax = 0.0f;
+        for (int64_t j = tid; j < K; j += nthr) {
+            float x = (float)row[j];
+            if constexpr (MODE == 1) x = x / s[j];
+            if constexpr (MODE == 2) x = x * s[j];
+            bool skip = false;
+            if constexpr (OUTL) {
+                int p = pos[j];
+                skip = p >= 0;
+                if (skip) Xo[m * K + p] = (_Float16)row[j];
+            }
+            if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
+        }
+        amax = wave_max(amax);
+        if (lane == 0) red[it & 1][wave] = amax;
+        __syncthreads();
+        float a = red[it & 1][0];
+        for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[it & 1][w]);
+        const float xs = a / 127.0f;
+        if (tid == 0) scale[m] = xs;
+        for (int64_t j = tid; j < K; j += nthr) {
+            float x = (float)row[j];
+            if constexpr (MODE == 1) x = x / s[j];
+            if constexpr (MODE == 2) x = x * s[j];
+            bool zero = xs == 0.0f;
+            if constexpr (OUTL) zero = zero || pos[j] >= 0;
+            Xq[m * K + j] = (int8_t)(zero ? 0 : code_of(x / xs));
+        }
+    }
+}
+
+template <typename Kern>
+static int blocks_per_cu(Kern k, int threads) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, threads, 0) != hipSuccess || nb <= 0) nb = 1;
+    return nb;
+}
+
+template <typename T, int MODE, bool OUTL>
+static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
+                               const int32_t* pos, _Float16* Xo, hipStream_t st) {
+    constexpr int VEC = Chunk<T>::N;
+    const int64_t nchunk = K / VEC;
+    int threads = (int)((nchunk + 63) / 64 * 64);
+    int ch = 1;
+    if (threads > 1024) {
+        ch = (int)((nchunk + 1023) / 1024);
+        threads = 1024;
+    }
+    if (threads < 64) threads = 64;
+    const int cus = dev_info().cus;
+    auto grid_for = [&](auto kern) {
+        static int cache[1025] = {0};  // per thread count, for this instantiation
+        int nb = cache[threads];
+        if (nb == 0) cache[threads] = nb = blocks_per_cu(kern, threads);
+        int64_t g = (int64_t)cus * nb;
+        return (unsigned)(g < M ? g : M);
+    };
+    switch (ch) {
+        case 1: {
+            auto k = quant_rows_fast<T, 1, MODE, OUTL>;
+            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(threads), 0, st, X, M, K, s, Xq, scale, pos, Xo);
+            break;
+        }
+        case 2: {
+            auto k = quant_rows_fast<T, 2, MODE, OUTL>;
+            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(threads), 0, st, X, M, K, s, Xq, scale, pos, Xo);
+            break;
+        }
+        case 3: {
+            auto k = quant_rows_fast<T, 3, MODE, OUTL>;
+            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(threads), 0, st, X, M, K, s, Xq, scale, pos, Xo);
+            break;
+        }
+        default: {
+            auto k = quant_rows_generic<T, MODE, OUTL>;
+            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
+            break;
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, int mode,
+                             int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st) {
+    const bool outl = pos != nullptr;
+#define SQ_QR(T, MD, OL) return quant_rows_t<T, MD, OL>((const T*)X, M, K, s, Xq, scale, pos, Xo, st)
+    if (dt == SQ_F16) {
+        if (outl) SQ_QR(_Float16, 0, true);
+        if (mode == 1) SQ_QR(_Float16, 1, false);
+        if (mode == 2) SQ_QR(_Float16, 2, false);
+        SQ_QR(_Float16, 0, false);
+    } else {
+        if (mode == 1) SQ_QR(float, 1, false);
+        if (mode == 2) SQ_QR(float, 2, false);
+        SQ_QR(float, 0, false);
+    }
+#undef SQ_QR
+}
+
+// ---------------------------------------------------------------------------
+// Column absolute maximum (calibration statistic, W column maxima, LLM.int8()
+// outlier detection).  Block = 32 chunk-columns x 8 row lanes; each block
+// reduces a band of rows and issues one atomic max per column.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void colmax_kernel(const T* __restrict__ X, int64_t M, int64_t K,
+                                                     int64_t rows_per_block, uint32_t* __restrict__ amax_bits) {
+    using V = typename Chunk<T>::V;
+    constexpr int VEC = Chunk<T>::N;
+    __shared__ float red[8][32][VEC + 1];
+    const int lc = threadIdx.x & 31, lr = threadIdx.x >> 5;
+    const int64_t nchunk = K / VEC;
+    const int64_t c = (int64_t)blockIdx.x * 32 + lc;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < M ? r0 + rows_per_block : M;
+    float mx[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) mx[e] = 0.0f;
+    if (c < nchunk) {
+        for (int64_t r = r0 + lr; r < r1; r += 8) {
+            V v = *reinterpret_cast<const V*>(X + r * K + c * VEC);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) mx[e] = __builtin_fmaxf(mx[e], __builtin_fabsf((float)v[e]));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) red[lr][lc][e] = mx[e];
+    __syncthreads();
+    if (lr == 0 && c < nchunk) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float m = red[0][lc][e];
+            for (int r = 1; r < 8; ++r) m = __builtin_fmaxf(m, red[r][lc][e]);
+            atomicMax(&amax_bits[c * VEC + e], __float_as_uint(m));
+        }
+    }
+}
+
+hipError_t launch_colmax(const void* X, sq_dtype dt, int64_t M, int64_t K, uint32_t* amax_bits, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    const int vec = dt == SQ_F16 ? 8 : 4;
+    const int64_t nchunk = K / vec;
+    int64_t rpb = 256;
+    if ((M + rpb - 1) / rpb > 65535) rpb = (M + 65534) / 65535;   // grid.y limit
+    dim3 grid((unsigned)((nchunk + 31) / 32), (unsigned)((M + rpb - 1) / rpb));
+    if (dt == SQ_F16)
+        hipLaunchKernelGGL(colmax_kernel<_Float16>, grid, dim3(256), 0, st, (const _Float16*)X, M, K, rpb, amax_bits);
+    else
+        hipLaunchKernelGGL(colmax_kernel<float>, grid, dim3(256), 0, st, (const float*)X, M, K, rpb, amax_bits);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Smoothing factors: s_j = max(a_j,1e-8)^alpha / max(w_j,1e-8)^(1-alpha) in fp64.
+// ---------------------------------------------------------------------------
+__global__ void smooth_pow_kernel(const float* __restrict__ act_max, float* __restrict__ s_wmax, int64_t K,
+                                  float alpha) {
+    int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (j >= K) return;
+    float a = act_max[j];
+    float w = s_wmax[j];
+    a = a > 1e-8f ? a : 1e-8f;
+    w = w > 1e-8f ? w : 1e-8f;
+    double al = (double)alpha;
+    s_wmax[j] = (float)(pow((double)a, al) / pow((double)w, 1.0 - al));
+}
+
+hipError_t launch_smooth_pow(const float* act_max, float* s_wmax, int64_t K, float alpha, hipStream_t st) {
+    hipLaunchKernelGGL(smooth_pow_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, act_max, s_wmax, K,
+                       alpha);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor weight quantization: pass 1 global max of |W * s|, pass 2 codes.
+// ---------------------------------------------------------------------------
+template <typename T, bool SMOOTH>
+__global__ __launch_bounds__(256) void tensor_max_kernel(const T* __restrict__ W, int64_t nchunks, int64_t kchunks,
+                                                         const float* __restrict__ s, uint32_t* __restrict__ gmax) {
+    using V = typename Chunk<T>::V;
+    constexpr int VEC = Chunk<T>::N;
+    __shared__ float red[4];
+    float m = 0.0f;
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
+        V v = reinterpret_cast<const V*>(W)[c];
+        int64_t jc = c % kchunks;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float x = (float)v[e];
+            if constexpr (SMOOTH) x = x * s[jc * VEC + e];
+            m = __builtin_fmaxf(m, __builtin_fabsf(x));
+        }
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+        atomicMax(gmax, __float_as_uint(a));
+    }
+}
+
+template <typename T, bool SMOOTH>
+__global__ __launch_bounds__(256) void tensor_code_kernel(const T* __restrict__ W, int64_t nchunks, int64_t kchunks,
+                                                          const float* __restrict__ s,
+                                                          const uint32_t* __restrict__ gmax,
+                                                          int8_t* __restrict__ Wq, float* __restrict__ w_scale) {
+    using V = typename Chunk<T>::V;
+    constexpr int VEC = Chunk<T>::N;
+    const float sc = __uint_as_float(*gmax) / 127.0f;
+    const double rx = sc != 0.0f ? 1.0 / (double)sc : 0.0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *w_scale = sc;
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
+        V v = reinterpret_cast<const V*>(W)[c];
+        int64_t jc = c % kchunks;
+        int q[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float x = (float)v[e];
+            if constexpr (SMOOTH) x = x * s[jc * VEC + e];
+            q[e] = sc == 0.0f ? 0 : code_of(div_rcp64(x, rx, sc));
+        }
+        CodeStore<VEC>::store(Wq + c * VEC, q);
+    }
+}
+
+template <typename T>
+static hipError_t quant_tensor_t(const T* W, int64_t N, int64_t K, const float* s, int8_t* Wq, float* w_scale,
+                                 uint32_t* gmax, hipStream_t st) {
+    constexpr int VEC = Chunk<T>::N;
+    const int64_t kchunks = K / VEC, nchunks = N * kchunks;
+    int64_t blocks = (nchunks + 255) / 256;
+    const int64_t cap = (int64_t)dev_info().cus * 8;
+    if (blocks > cap) blocks = cap;
+    if (s) {
+        hipLaunchKernelGGL((tensor_max_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
+        hipLaunchKernelGGL((tensor_code_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
+    } else {
+        hipLaunchKernelGGL((tensor_max_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
+        hipLaunchKernelGGL((tensor_code_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor(const void* W, sq_dtype dt, int64_t N, int64_t K, const float* s, int8_t* Wq,
+                               float* w_scale, uint32_t* gmax_bits, hipStream_t st) {
+    if (dt == SQ_F16) return quant_tensor_t((const _Float16*)W, N, K, s, Wq, w_scale, gmax_bits, st);
+    return quant_tensor_t((const float*)W, N, K, s, Wq, w_scale, gmax_bits, st);
+}
+
+}  // namespace sq

@@ -1,0 +1,166 @@
+// C ABI of libsq: argument validation on the host, then kernel launches on the
+// caller's stream.  No allocation, no host synchronization, no device-to-host copy.
+#include "sq_internal.h"
+
+using namespace sq;
+
+namespace {
+
+constexpr int64_t kMaxK = 131056;   // 127^2 * K < 2^31, K % 16 == 0
+constexpr int64_t kMaxMN = (int64_t)1 << 30;
+
+bool bad_shape(int64_t M, int64_t N, int64_t K) {
+    return M < 1 || N < 1 || K < 16 || K > kMaxK || (K % 16) != 0 || M > kMaxMN || N > kMaxMN;
+}
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+bool bad_dtype(int d) { return d != SQ_F32 && d != SQ_F16; }
+
+sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+#define SQ_TRY(call)                                  \
+    do {                                              \
+        hipError_t e_ = (call);                       \
+        if (e_ != hipSuccess) return SQ_ERR_HIP;      \
+    } while (0)
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// LLM.int8() workspace layout (byte offsets), sized for K outlier columns.
+struct OutlierLayout {
+    size_t cmax, pos, idx, count, xs, xq, xo, wo, total;
+};
+OutlierLayout outlier_layout(int64_t M, int64_t N, int64_t K) {
+    OutlierLayout L;
+    size_t o = 0;
+    L.cmax = o;  o = align256(o + 4 * (size_t)K);
+    L.pos = o;   o = align256(o + 4 * (size_t)K);
+    L.idx = o;   o = align256(o + 4 * (size_t)K);
+    L.count = o; o = align256(o + 16);
+    L.xs = o;    o = align256(o + 4 * (size_t)M);
+    L.xq = o;    o = align256(o + (size_t)M * (size_t)K);
+    L.xo = o;    o = align256(o + 2 * (size_t)M * (size_t)K);
+    L.wo = o;    o = align256(o + 2 * (size_t)N * (size_t)K);
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sq_status_string(sq_status st) {
+    switch (st) {
+        case SQ_OK: return "SQ_OK";
+        case SQ_ERR_NULL: return "SQ_ERR_NULL: a required pointer is NULL";
+        case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: M, N >= 1 and 16 <= K <= 131056 with K % 16 == 0 are required";
+        case SQ_ERR_ALIGN: return "SQ_ERR_ALIGN: pointers must be 16-byte aligned";
+        case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: unsupported dtype or granularity";
+        case SQ_ERR_VALUE: return "SQ_ERR_VALUE: alpha must be in [0,1]; threshold finite and >= 0";
+        case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
+        case SQ_ERR_HIP: return "SQ_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown sq_status";
+}
+
+size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
+    if (op == SQ_OP_QUANT_WEIGHT) {
+        if (bad_shape(1, N, K)) return 0;
+        return 256;
+    }
+    if (op == SQ_OP_OUTLIER) {
+        if (bad_shape(M, N, K)) return 0;
+        return outlier_layout(M, N, K).total;
+    }
+    return 0;
+}
+
+sq_status sq_smooth_scales(const void* X_cal, sq_dtype xdt, int64_t M_cal, const void* W, sq_dtype wdt, int64_t N,
+                           int64_t K, float alpha, float* act_max, float* s, hipStream_t stream) {
+    if (!act_max) return SQ_ERR_NULL;
+    if (M_cal > 0 && !X_cal) return SQ_ERR_NULL;
+    if (W && !s) return SQ_ERR_NULL;
+    if (M_cal < 0 || bad_shape(M_cal > 0 ? M_cal : 1, W ? N : 1, K)) return SQ_ERR_SHAPE;
+    if ((M_cal > 0 && bad_dtype(xdt)) || (W && bad_dtype(wdt))) return SQ_ERR_DTYPE;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_VALUE;
+    if (misaligned(act_max) || (X_cal && misaligned(X_cal)) || (W && misaligned(W)) || (s && misaligned(s)))
+        return SQ_ERR_ALIGN;
+    if (M_cal > 0) SQ_TRY(launch_colmax(X_cal, xdt, M_cal, K, reinterpret_cast<uint32_t*>(act_max), stream));
+    if (W) {
+        SQ_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(s), K, 0u, stream));
+        SQ_TRY(launch_colmax(W, wdt, N, K, reinterpret_cast<uint32_t*>(s), stream));
+        SQ_TRY(launch_smooth_pow(act_max, s, K, alpha, stream));
+    }
+    return SQ_OK;
+}
+
+sq_status sq_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, int8_t* Xq,
+                                float* x_scale, hipStream_t stream) {
+    if (!X || !Xq || !x_scale) return SQ_ERR_NULL;
+    if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt)) return SQ_ERR_DTYPE;
+    if (misaligned(X) || misaligned(Xq) || misaligned(x_scale) || (s && misaligned(s))) return SQ_ERR_ALIGN;
+    return hip_status(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, Xq, x_scale, nullptr, nullptr, stream));
+}
+
+sq_status sq_quantize_weight(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s, sq_wgran g,
+                             int8_t* Wq, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!W || !Wq || !w_scale) return SQ_ERR_NULL;
+    if (bad_shape(1, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(wdt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if (misaligned(W) || misaligned(Wq) || misaligned(w_scale) || (s && misaligned(s))) return SQ_ERR_ALIGN;
+    if (g == SQ_PER_CHANNEL)
+        return hip_status(launch_quant_rows(W, wdt, N, K, s, s ? 2 : 0, Wq, w_scale, nullptr, nullptr, stream));
+    if (!ws || ws_bytes < sq_workspace_size(SQ_OP_QUANT_WEIGHT, 0, N, K)) return SQ_ERR_WORKSPACE;
+    if (misaligned(ws)) return SQ_ERR_ALIGN;
+    uint32_t* gmax = reinterpret_cast<uint32_t*>(ws);
+    SQ_TRY(launch_fill_u32(gmax, 1, 0u, stream));
+    return hip_status(launch_quant_tensor(W, wdt, N, K, s, Wq, w_scale, gmax, stream));
+}
+
+sq_status w8a8_gemm_dequant(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                            sq_wgran g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                            int32_t* acc_out, hipStream_t stream) {
+    if (!Xq || !x_scale || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(ydt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if (misaligned(Xq) || misaligned(x_scale) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) ||
+        (bias && misaligned(bias)) || (acc_out && misaligned(acc_out)))
+        return SQ_ERR_ALIGN;
+    const int stride = g == SQ_PER_CHANNEL ? 1 : 0;
+    if (M <= 16)
+        return hip_status(launch_gemv(Xq, x_scale, Wq, w_scale, stride, bias, M, N, K, Y, ydt, acc_out, nullptr, stream));
+    return hip_status(launch_gemm(Xq, x_scale, Wq, w_scale, stride, bias, M, N, K, Y, ydt, acc_out, nullptr, stream));
+}
+
+sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, const float* w_scale, const float* bias,
+                              int64_t M, int64_t N, int64_t K, float threshold, void* Y, void* ws, size_t ws_bytes,
+                              int32_t* n_outliers, int32_t* outlier_idx, int32_t* acc_out, hipStream_t stream) {
+    if (!X || !W16 || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
+    if (!(threshold >= 0.0f)) return SQ_ERR_VALUE;
+    if (!ws || ws_bytes < sq_workspace_size(SQ_OP_OUTLIER, M, N, K)) return SQ_ERR_WORKSPACE;
+    if (misaligned(X) || misaligned(W16) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) ||
+        misaligned(ws) || (bias && misaligned(bias)) || (acc_out && misaligned(acc_out)) ||
+        (outlier_idx && misaligned(outlier_idx)) || (n_outliers && ((uintptr_t)n_outliers & 3u)))
+        return SQ_ERR_ALIGN;
+    const OutlierLayout L = outlier_layout(M, N, K);
+    char* base = static_cast<char*>(ws);
+    uint32_t* cmax = reinterpret_cast<uint32_t*>(base + L.cmax);
+    int32_t* pos = reinterpret_cast<int32_t*>(base + L.pos);
+    int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
+    int32_t* count = reinterpret_cast<int32_t*>(base + L.count);
+    float* xs = reinterpret_cast<float*>(base + L.xs);
+    int8_t* xq = reinterpret_cast<int8_t*>(base + L.xq);
+    _Float16* xo = reinterpret_cast<_Float16*>(base + L.xo);
+    _Float16* wo = reinterpret_cast<_Float16*>(base + L.wo);
+
+    SQ_TRY(launch_fill_u32(cmax, K, 0u, stream));
+    SQ_TRY(launch_colmax(X, SQ_F16, M, K, cmax, stream));
+    SQ_TRY(launch_outlier_compact(cmax, K, threshold, idx, pos, count, n_outliers, outlier_idx, stream));
+    SQ_TRY(launch_quant_rows(X, SQ_F16, M, K, nullptr, 0, xq, xs, pos, xo, stream));
+    SQ_TRY(launch_gather_cols(static_cast<const _Float16*>(W16), N, K, idx, count, wo, stream));
+    SideArgs side{xo, wo, count, K};
+    return hip_status(launch_gemm(xq, xs, Wq, w_scale, 1, bias, M, N, K, Y, SQ_F16, acc_out, &side, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal declarations shared by the HIP sources of libsq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sq.h"
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+namespace sq {
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// Correctly rounded fp32 quotient a/b from rb = RN64(1/(double)b).
+// t = RN64(a * rb) is within 2^-51.9 (relative) of a/b, while a quotient of two
+// binary32 numbers in the normal range lies at least 2^-49 (relative) away from
+// every binary32 rounding midpoint and is never one itself; so rounding t to
+// binary32 gives the same result as the IEEE division.  Quotients below the
+// normal range take the IEEE division itself.
+__device__ __forceinline__ float div_rcp64(float a, double rb, float b) {
+    float q = (float)((double)a * rb);
+    if (__builtin_fabsf(q) < 1.17549435e-38f && a != 0.0f) q = a / b;
+    return q;
+}
+
+// Integer code: round half to even (v_rndne_f32), clamp to [-128, 127].
+__device__ __forceinline__ int code_of(float v) {
+    float r = __builtin_rintf(v);
+    r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+
+// Device properties cached once per device.
+struct DevInfo {
+    int cus;
+    int xcds;
+};
+const DevInfo& dev_info();
+
+// Fill n 32-bit words with a value (kernel, so it is safe inside stream capture).
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+
+// Per-row smoothing + absmax quantization (activations per token, weights per channel).
+// mode 0: no smoothing; 1: x / s_j; 2: x * s_j.  pos/Xo (LLM.int8() only): pos[j] >= 0
+// marks an outlier column, whose value is copied to Xo[m*K + pos[j]] and whose code is 0.
+hipError_t launch_quant_rows(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s,
+                             int mode, int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo,
+                             hipStream_t st);
+
+// Running column absolute maximum: amax_bits[j] = max(amax_bits[j], bits(max_m |X[m,j]|)),
+// where amax_bits holds non-negative floats as their bit patterns (monotone as uint32).
+hipError_t launch_colmax(const void* X, sq_dtype dt, int64_t M, int64_t K, uint32_t* amax_bits,
+                         hipStream_t st);
+
+// s_j from act_max and the W column maxima held in s (overwritten in place).
+hipError_t launch_smooth_pow(const float* act_max, float* s_wmax, int64_t K, float alpha,
+                             hipStream_t st);
+
+// Per-tensor weight quantization: global max then codes.
+hipError_t launch_quant_tensor(const void* W, sq_dtype dt, int64_t N, int64_t K, const float* s,
+                               int8_t* Wq, float* w_scale, uint32_t* gmax_bits, hipStream_t st);
+
+// int8 GEMM + dequant epilogue (M > 16).  side != nullptr adds the LLM.int8() fp16 side
+// product over the first *count columns of Xo [M x ldo] and Wo [N x ldo].
+struct SideArgs {
+    const _Float16* Xo;
+    const _Float16* Wo;
+    const int32_t* count;
+    int64_t ldo;
+};
+hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
+                       int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                       sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+
+// Weight-streaming decode kernel, M <= 16.
+hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
+                       int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                       sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+
+// LLM.int8(): outlier columns from the column maxima (bit patterns), ascending list,
+// per-column slot (or -1), device-side count; optional copies to user buffers.
+hipError_t launch_outlier_compact(const uint32_t* cmax_bits, int64_t K, float threshold,
+                                  int32_t* idx, int32_t* pos, int32_t* count, int32_t* user_count,
+                                  int32_t* user_idx, hipStream_t st);
+
+// Wo[n, t] = W16[n, idx[t]] for t < *count.
+hipError_t launch_gather_cols(const _Float16* W16, int64_t N, int64_t K, const int32_t* idx,
+                              const int32_t* count, _Float16* Wo, hipStream_t st);
+
+}  // namespace sq

@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU (no GPU, no kernel launch): it loads, exports
+every entry point the header declares, sizes workspaces, and rejects every bad
+argument with the documented status before touching the device."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sq.h")
+LIB = os.path.join(ROOT, "int8_quantization_amd", "libsq.so")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, VALUE, WORKSPACE, HIP = range(8)
+P = 0x100000          # a 16-byte-aligned address that is never dereferenced
+MIS = 0x100004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import int8_quantization_amd.build as b
+        b.build()
+    lib = C.CDLL(LIB)
+    I64, F, I, SZ, V = C.c_int64, C.c_float, C.c_int, C.c_size_t, C.c_void_p
+    lib.sq_status_string.restype = C.c_char_p
+    lib.sq_status_string.argtypes = [I]
+    lib.sq_workspace_size.restype = SZ
+    lib.sq_workspace_size.argtypes = [I, I64, I64, I64]
+    lib.sq_smooth_scales.argtypes = [V, I, I64, V, I, I64, I64, F, V, V, V]
+    lib.sq_quantize_per_token.argtypes = [V, I, I64, I64, V, V, V, V]
+    lib.sq_quantize_weight.argtypes = [V, I, I64, I64, V, I, V, V, V, SZ, V]
+    lib.w8a8_gemm_dequant.argtypes = [V, V, V, V, I, V, I64, I64, I64, V, I, V, V]
+    lib.int8_outlier_matmul.argtypes = [V, V, V, V, V, I64, I64, I64, F, V, V, SZ, V, V, V, V]
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"sq_smooth_scales", "sq_quantize_per_token", "sq_quantize_weight", "w8a8_gemm_dequant",
+            "int8_outlier_matmul", "sq_workspace_size", "sq_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_python_binding_exports_same_names():
+    import int8_quantization_amd as sq
+    for n in declared_functions():
+        assert callable(getattr(sq, n)), n
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.sq_status_string(code).decode()
+        assert s.startswith("SQ_")
+    assert "unknown" in lib.sq_status_string(99).decode()
+
+
+def test_workspace_sizes(lib):
+    assert lib.sq_workspace_size(0, 0, 10, 16) == 256
+    M, N, K = 4096, 8192, 8192
+    ws = lib.sq_workspace_size(1, M, N, K)
+    assert ws >= (M + N) * K * 2 + M * K + 4 * M + 12 * K
+    assert ws < (M + N) * K * 2 + M * K + 4 * M + 12 * K + 4096
+    assert lib.sq_workspace_size(1, M, N, 17) == 0
+    assert lib.sq_workspace_size(7, M, N, K) == 0
+
+
+def test_quantize_per_token_validation(lib):
+    f = lib.sq_quantize_per_token
+    assert f(None, 1, 4, 64, None, P, P, None) == NULL
+    assert f(P, 1, 4, 64, None, None, P, None) == NULL
+    assert f(P, 1, 0, 64, None, P, P, None) == SHAPE
+    assert f(P, 1, 4, 60, None, P, P, None) == SHAPE
+    assert f(P, 1, 4, 0, None, P, P, None) == SHAPE
+    assert f(P, 1, 4, 131072, None, P, P, None) == SHAPE
+    assert f(P, 3, 4, 64, None, P, P, None) == DTYPE
+    assert f(MIS, 1, 4, 64, None, P, P, None) == ALIGN
+    assert f(P, 1, 4, 64, MIS, P, P, None) == ALIGN
+
+
+def test_smooth_scales_validation(lib):
+    f = lib.sq_smooth_scales
+    assert f(P, 1, 8, P, 1, 4, 64, 0.5, None, P, None) == NULL
+    assert f(None, 1, 8, P, 1, 4, 64, 0.5, P, P, None) == NULL
+    assert f(P, 1, 8, P, 1, 4, 64, 0.5, P, None, None) == NULL
+    assert f(P, 1, 8, P, 1, 4, 72, 0.5, P, P, None) == SHAPE
+    assert f(P, 1, -1, P, 1, 4, 64, 0.5, P, P, None) == SHAPE
+    assert f(P, 5, 8, P, 1, 4, 64, 0.5, P, P, None) == DTYPE
+    assert f(P, 1, 8, P, 1, 4, 64, 1.5, P, P, None) == VALUE
+    assert f(P, 1, 8, P, 1, 4, 64, -0.1, P, P, None) == VALUE
+    assert f(P, 1, 8, P, 1, 4, 64, math.nan, P, P, None) == VALUE
+    assert f(P, 1, 8, P, 1, 4, 64, 0.5, MIS, P, None) == ALIGN
+
+
+def test_quantize_weight_validation(lib):
+    f = lib.sq_quantize_weight
+    assert f(None, 1, 8, 64, None, 0, P, P, None, 0, None) == NULL
+    assert f(P, 1, 8, 64, None, 0, None, P, None, 0, None) == NULL
+    assert f(P, 1, 8, 24, None, 0, P, P, None, 0, None) == SHAPE
+    assert f(P, 1, 8, 64, None, 2, P, P, None, 0, None) == DTYPE
+    assert f(P, 9, 8, 64, None, 0, P, P, None, 0, None) == DTYPE
+    assert f(P, 1, 8, 64, None, 1, P, P, None, 0, None) == WORKSPACE
+    assert f(P, 1, 8, 64, None, 1, P, P, P, 16, None) == WORKSPACE
+    assert f(P, 1, 8, 64, None, 1, P, P, MIS, 4096, None) == ALIGN
+    assert f(P, 1, 8, 64, MIS, 0, P, P, None, 0, None) == ALIGN
+
+
+def test_gemm_validation(lib):
+    f = lib.w8a8_gemm_dequant
+    assert f(P, P, P, P, 0, None, 32, 32, 64, None, 1, None, None) == NULL
+    assert f(None, P, P, P, 0, None, 32, 32, 64, P, 1, None, None) == NULL
+    assert f(P, P, P, P, 0, None, 32, 0, 64, P, 1, None, None) == SHAPE
+    assert f(P, P, P, P, 0, None, 32, 32, 65, P, 1, None, None) == SHAPE
+    assert f(P, P, P, P, 3, None, 32, 32, 64, P, 1, None, None) == DTYPE
+    assert f(P, P, P, P, 0, None, 32, 32, 64, P, 2, None, None) == DTYPE
+    assert f(P, P, P, P, 0, MIS, 32, 32, 64, P, 1, None, None) == ALIGN
+    assert f(P, P, P, P, 0, None, 32, 32, 64, P, 1, MIS, None) == ALIGN
+
+
+def test_outlier_validation(lib):
+    f = lib.int8_outlier_matmul
+    need = lib.sq_workspace_size(1, 32, 32, 64)
+    assert f(P, P, P, P, None, 32, 32, 64, 6.0, None, P, need, None, None, None, None) == NULL
+    assert f(P, P, P, P, None, 32, 32, 48 + 1, 6.0, P, P, need, None, None, None, None) == SHAPE
+    assert f(P, P, P, P, None, 32, 32, 64, -1.0, P, P, need, None, None, None, None) == VALUE
+    assert f(P, P, P, P, None, 32, 32, 64, math.nan, P, P, need, None, None, None, None) == VALUE
+    assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, None, need, None, None, None, None) == WORKSPACE
+    assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, P, need - 1, None, None, None, None) == WORKSPACE
+    assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, P, need, P + 2, None, None, None) == ALIGN
+    assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, P, need, None, MIS, None, None) == ALIGN

@@ -1,0 +1,329 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: int8 codes, scales, int32 accumulators, the outlier count and list are
+bit-exact; the smoothing factor is within 2 ulp (fp64 pow on two different
+libraries); W8A8 outputs are additionally bit-exact because both sides take the
+same fp32 steps in the same order, and every output must be within the stated
+tolerance (1e-3 relative for fp32, 1e-2 for fp16, with a floor of that fraction
+of mean|y|).  Every output buffer carries canary guard bands.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import Guarded, assert_bits_equal, assert_close, dev, sample_positions
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import int8_quantization_amd as sq
+    return sq
+
+
+def _f(dt):
+    return {np.float16: torch.float16, np.float32: torch.float32}[dt]
+
+
+def _ulps32(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+def gpu_quantize_rows(sq, X, s):
+    M, K = X.shape
+    Xq = Guarded((M, K), torch.int8)
+    xs = Guarded((M,), torch.float32)
+    sq.sq_quantize_per_token(dev(X), None if s is None else dev(s), Xq.t, xs.t)
+    torch.cuda.synchronize()
+    return Xq.np(), xs.np()
+
+
+def gpu_quantize_weight(sq, W, s, gran):
+    N, K = W.shape
+    Wq = Guarded((N, K), torch.int8)
+    ws = Guarded((N if gran == 0 else 1,), torch.float32)
+    wsp = torch.empty(sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, N, K), dtype=torch.uint8, device="cuda")
+    sq.sq_quantize_weight(dev(W), None if s is None else dev(s), gran, Wq.t, ws.t, wsp)
+    torch.cuda.synchronize()
+    return Wq.np(), ws.np()
+
+
+# ---------------------------------------------------------------------------
+# a4: fused smoothing + per-token quantization
+# ---------------------------------------------------------------------------
+QUANT_CASES = [
+    (1, 16, np.float32, False),
+    (3, 48, np.float16, True),
+    (17, 4096, np.float16, True),
+    (130, 4112, np.float16, True),
+    (5, 20480, np.float16, True),       # three 16-byte chunks per thread
+    (3, 24576, np.float16, False),
+    (2, 40960, np.float16, True),       # longer than the register-resident path
+    (1000, 512, np.float32, True),      # many rows per block
+    (4, 16384, np.float32, True),       # fp32 beyond the register-resident path
+    (9, 8192, np.float32, False),
+]
+
+
+@pytest.mark.parametrize("M,K,dt,smooth", QUANT_CASES)
+def test_quantize_per_token(sq, orc, M, K, dt, smooth):
+    X, W, _ = workloads.random_layer(100 + M + K, M, K, 8, dt, n_outliers=min(4, K // 8))
+    s = orc.smooth_scales(X, W, 0.5)[1] if smooth else None
+    got = gpu_quantize_rows(sq, X, s)
+    ref = orc.quantize_per_token(X, s)
+    assert_bits_equal(got[1], ref[1], "x_scale")
+    assert_bits_equal(got[0], ref[0], "Xq")
+
+
+def test_quantize_special_rows(sq, orc):
+    """zero rows, exact .5 ties at scale 1, fp32 subnormals (the IEEE-division
+    branch of the reciprocal path), a single non-zero element."""
+    K = 64
+    X = np.random.default_rng(9).standard_normal((6, K)).astype(np.float32)
+    X[0] = 0.0
+    X[1] = 0.5 * np.arange(-K // 2, K // 2, dtype=np.float32)
+    X[1, 0] = 127.0
+    X[2] = 1e-40
+    X[2, 5] = 3e-39
+    X[3] = 0.0
+    X[3, 17] = -2.5
+    X[4] *= 1e30
+    s = np.full(K, 3.0, np.float32)
+    for ss in (None, s):
+        got = gpu_quantize_rows(sq, X, ss)
+        ref = orc.quantize_per_token(X, ss)
+        assert_bits_equal(got[1], ref[1], "x_scale")
+        assert_bits_equal(got[0], ref[0], "Xq")
+
+
+def test_quantize_deterministic(sq):
+    X, _, _ = workloads.random_layer(5, 300, 4096, 8, np.float16, n_outliers=10)
+    outs = [gpu_quantize_rows(sq, X, None) for _ in range(3)]
+    for o in outs[1:]:
+        assert_bits_equal(o[0], outs[0][0], "Xq repeat")
+        assert_bits_equal(o[1], outs[0][1], "x_scale repeat")
+
+
+# ---------------------------------------------------------------------------
+# a1-a2: calibration maximum and smoothing factors
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("alpha", [0.5, 0.0, 1.0, 0.7])
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_smooth_scales(sq, orc, alpha, dt):
+    X, W, _ = workloads.random_layer(7, 300, 1040, 70, dt, n_outliers=5)
+    X[:, 3] = 0
+    act = torch.zeros(1040, dtype=torch.float32, device="cuda")
+    s = Guarded((1040,), torch.float32)
+    sq.sq_smooth_scales(dev(X[:128]), dev(W), alpha, act, s.t)     # two calibration batches
+    sq.sq_smooth_scales(dev(X[128:]), dev(W), alpha, act, s.t)
+    torch.cuda.synchronize()
+    a_ref, s_ref = orc.smooth_scales(X[128:], W, alpha, act_max=orc.smooth_scales(X[:128], W, alpha)[0])
+    assert_bits_equal(act.cpu().numpy(), a_ref, "act_max")
+    assert _ulps32(s.np(), s_ref).max() <= 2
+
+
+# ---------------------------------------------------------------------------
+# a3: weight smoothing + quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K", [(1, 16), (70, 144), (300, 4096), (5, 20480), (3, 40960)])
+@pytest.mark.parametrize("gran", [0, 1])
+@pytest.mark.parametrize("dt,smooth", [(np.float16, True), (np.float32, True), (np.float16, False)])
+def test_quantize_weight(sq, orc, N, K, gran, dt, smooth):
+    X, W, _ = workloads.random_layer(N * 7 + K, 16, K, N, dt, n_outliers=min(3, K // 8))
+    s = orc.smooth_scales(X, W, 0.5)[1] if smooth else None
+    got = gpu_quantize_weight(sq, W, s, gran)
+    ref = orc.quantize_weight(W, s, gran)
+    assert_bits_equal(got[1], ref[1], "w_scale")
+    assert_bits_equal(got[0], ref[0], "Wq")
+
+
+# ---------------------------------------------------------------------------
+# a5-a7: int8 GEMM + dequant epilogue (tile kernel for M > 16, decode kernel below)
+# ---------------------------------------------------------------------------
+def _gemm_case(seed, M, N, K, gran):
+    rng = np.random.default_rng(seed)
+    Xq = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    Wq = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    Xq[0, :] = -128                       # extreme accumulators
+    Wq[N - 1, :] = -128
+    xs = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, N if gran == 0 else 1).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    return Xq, xs, Wq, ws, bias
+
+
+def gpu_gemm(sq, Xq, xs, Wq, ws, gran, bias, out_dt):
+    M, N = Xq.shape[0], Wq.shape[0]
+    Y = Guarded((M, N), _f(out_dt))
+    acc = Guarded((M, N), torch.int32)
+    sq.w8a8_gemm_dequant(dev(Xq), dev(xs), dev(Wq), dev(ws), gran, None if bias is None else dev(bias), Y.t,
+                         acc.t)
+    torch.cuda.synchronize()
+    return acc.np(), Y.np()
+
+
+GEMM_CASES = [
+    # M, N, K   (M <= 16: decode kernel; else tile kernel)
+    (1, 1, 16), (1, 1000, 8192), (4, 1000, 144), (7, 33, 4096), (16, 4100, 8192),
+    (17, 32, 16), (33, 70, 144), (200, 300, 1040), (256, 256, 256), (300, 520, 4112),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+@pytest.mark.parametrize("gran,use_bias,out_dt", [(0, False, np.float16), (1, True, np.float32),
+                                                  (0, True, np.float32)])
+def test_gemm_dequant(sq, orc, M, N, K, gran, use_bias, out_dt):
+    Xq, xs, Wq, ws, bias = _gemm_case(M * 31 + N + K, M, N, K, gran)
+    bias = bias if use_bias else None
+    acc, Y = gpu_gemm(sq, Xq, xs, Wq, ws, gran, bias, out_dt)
+    ref_acc = orc.gemm_i8(Xq, Wq)
+    assert_bits_equal(acc, ref_acc, "acc")
+    y = orc.dequant(ref_acc, xs, ws, gran, bias)
+    ref = y if out_dt == np.float32 else orc.float_to_half(y)
+    assert_close(Y, ref, 1e-3 if out_dt == np.float32 else 1e-2)
+    assert_bits_equal(Y, ref, "Y")
+
+
+@pytest.mark.parametrize("M,N,K", [(2048 + 37, 8192, 256), (4096, 4096 + 40, 272)])
+def test_gemm_large_tiles_sampled(sq, orc, M, N, K):
+    """Problems big enough for the 256 x 256 tile configuration, ragged edges."""
+    Xq, xs, Wq, ws, bias = _gemm_case(77, M, N, K, 0)
+    acc, Y = gpu_gemm(sq, Xq, xs, Wq, ws, 0, None, np.float16)
+    rows, cols = sample_positions(M, N, 20000)
+    ref_acc = orc.gemm_i8_sampled(Xq, Wq, rows, cols)
+    assert_bits_equal(acc[rows, cols], ref_acc, "acc (sampled)")
+    ref = orc.float_to_half(orc.dequant_sampled(ref_acc, xs, ws, 0, None, rows, cols))
+    assert_bits_equal(Y[rows, cols], ref, "Y (sampled)")
+    # every row of one full tile row and tile column, exhaustively
+    r = np.arange(M, dtype=np.int64)
+    for c in (0, N - 1):
+        cc = np.full(M, c, np.int64)
+        assert_bits_equal(acc[r, cc], orc.gemm_i8_sampled(Xq, Wq, r, cc), "acc column")
+
+
+def test_gemm_deterministic(sq):
+    Xq, xs, Wq, ws, _ = _gemm_case(3, 640, 1024, 2048, 0)
+    outs = [gpu_gemm(sq, Xq, xs, Wq, ws, 0, None, np.float16) for _ in range(3)]
+    for a, y in outs[1:]:
+        assert_bits_equal(a, outs[0][0], "acc repeat")
+        assert_bits_equal(y, outs[0][1], "Y repeat")
+
+
+# ---------------------------------------------------------------------------
+# a8: LLM.int8() decomposition
+# ---------------------------------------------------------------------------
+def gpu_outlier(sq, X, W16, Wq, ws, bias, thr):
+    M, K = X.shape
+    N = W16.shape[0]
+    Y = Guarded((M, N), torch.float16)
+    acc = Guarded((M, N), torch.int32)
+    cnt = Guarded((1,), torch.int32, fill=-7)
+    idx = Guarded((K,), torch.int32, fill=-7)
+    wsp = torch.empty(sq.sq_workspace_size(sq.SQ_OP_OUTLIER, M, N, K), dtype=torch.uint8, device="cuda")
+    wsp.fill_(0xFF)   # the workspace starts as garbage (NaN halves) on purpose
+    sq.int8_outlier_matmul(dev(X), dev(W16), dev(Wq), dev(ws), None if bias is None else dev(bias), thr, Y.t,
+                           wsp, cnt.t, idx.t, acc.t)
+    torch.cuda.synchronize()
+    c = int(cnt.np()[0])
+    return c, idx.np()[:c], acc.np(), Y.np()
+
+
+@pytest.mark.parametrize("M,N,K,n_out,thr", [
+    (48, 40, 256, 3, 6.0), (300, 520, 1024, 7, 6.0), (17, 64, 512, 20, 6.0),
+    (64, 96, 256, 3, float("inf")), (40, 72, 128, 0, 0.0), (5, 33, 160, 2, 6.0),
+])
+def test_outlier_matmul(sq, orc, M, N, K, n_out, thr):
+    X, W16, _ = workloads.random_layer(M + N + K, M, K, N, np.float16, n_outliers=n_out, factor=20.0)
+    if thr == 0.0:
+        X = np.where(X == 0, np.float16(0.5), X)
+    bias = np.random.default_rng(1).standard_normal(N).astype(np.float32)
+    Wq, ws = orc.quantize_weight(W16, None, 0)
+    c, idx, acc, Y = gpu_outlier(sq, X, W16, Wq, ws, bias, thr)
+    mask, ref_idx, Xq, xs, ref_acc, ref_Y = orc.llm_int8_linear(X, W16, Wq, ws, thr, bias)
+    assert c == ref_idx.size
+    assert_bits_equal(idx, ref_idx, "outlier idx")
+    assert_bits_equal(acc, ref_acc, "acc")
+    assert_close(Y, ref_Y, 1e-2)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size (sampled where the oracle would be slow)
+# ---------------------------------------------------------------------------
+def _w8a8_full(sq, orc, wl, wname, rows=None, n_samp=4000):
+    X = wl.X if rows is None else wl.X[:rows]
+    W = wl.weights[wname]
+    M, K = X.shape
+    N = W.shape[0]
+    # a1-a2 on the GPU against the oracle (s within 2 ulp); both sides then use the oracle's s
+    act = torch.zeros(K, dtype=torch.float32, device="cuda")
+    s_gpu = torch.empty(K, dtype=torch.float32, device="cuda")
+    sq.sq_smooth_scales(dev(wl.calib), dev(W), wl.alpha, act, s_gpu)
+    a_ref, s = orc.smooth_scales(wl.calib, W, wl.alpha)
+    torch.cuda.synchronize()
+    assert_bits_equal(act.cpu().numpy(), a_ref, "act_max")
+    assert _ulps32(s_gpu.cpu().numpy(), s).max() <= 2
+    # a3
+    Wq, ws = gpu_quantize_weight(sq, W, s, wl.gran)
+    Wq_r, ws_r = orc.quantize_weight(W, s, wl.gran)
+    assert_bits_equal(ws, ws_r, "w_scale")
+    assert_bits_equal(Wq, Wq_r, "Wq")
+    # a4
+    Xq, xs = gpu_quantize_rows(sq, X, s)
+    Xq_r, xs_r = orc.quantize_per_token(X, s)
+    assert_bits_equal(xs, xs_r, "x_scale")
+    assert_bits_equal(Xq, Xq_r, "Xq")
+    # a5-a6 (a7 when M <= 16)
+    acc, Y = gpu_gemm(sq, Xq, xs, Wq, ws, wl.gran, None, wl.out_dtype)
+    r, c = sample_positions(M, N, n_samp)
+    acc_r = orc.gemm_i8_sampled(Xq_r, Wq_r, r, c)
+    assert_bits_equal(acc[r, c], acc_r, "acc (sampled)")
+    y = orc.dequant_sampled(acc_r, xs_r, ws_r, wl.gran, None, r, c)
+    ref = y if wl.out_dtype == np.float32 else orc.float_to_half(y)
+    assert_close(Y[r, c], ref, 1e-3 if wl.out_dtype == np.float32 else 1e-2)
+    assert_bits_equal(Y[r, c], ref, "Y (sampled)")
+
+
+def test_full_single_w8a8(sq, orc):
+    _w8a8_full(sq, orc, workloads.single_w8a8(), "w", n_samp=8192)
+
+
+@pytest.mark.parametrize("wname", ["qkv", "up"])
+def test_full_prefill_7b(sq, orc, wname):
+    _w8a8_full(sq, orc, workloads.prefill_7b(which=(wname,)), wname)
+
+
+def test_full_decode_70b(sq, orc):
+    wl = workloads.decode_70b()
+    for m in wl.decode_rows:
+        _w8a8_full(sq, orc, wl, "w", rows=m)
+
+
+def test_full_slice_530b(sq, orc):
+    _w8a8_full(sq, orc, workloads.slice_530b(), "w")
+
+
+def test_full_llm_int8(sq, orc):
+    wl = workloads.llm_int8_4096()
+    X, W16 = wl.X, wl.weights["w"]
+    M, K = X.shape
+    N = W16.shape[0]
+    Wq, ws = gpu_quantize_weight(sq, W16, None, 0)
+    Wq_r, ws_r = orc.quantize_weight(W16, None, 0)
+    assert_bits_equal(Wq, Wq_r, "Wq")
+    assert_bits_equal(ws, ws_r, "w_scale")
+    c, idx, acc, Y = gpu_outlier(sq, X, W16, Wq, ws, None, wl.threshold)
+    mask, ref_idx = orc.outlier_columns(X, wl.threshold)
+    assert c == ref_idx.size and set(wl.outlier_idx.tolist()) <= set(ref_idx.tolist())
+    assert_bits_equal(idx, ref_idx, "outlier idx")
+    Xq_r, xs_r = orc.quantize_per_token(X, None, skip=mask)
+    r, cc = sample_positions(M, N, 4000)
+    acc_r = orc.gemm_i8_sampled(Xq_r, Wq_r, r, cc)
+    assert_bits_equal(acc[r, cc], acc_r, "acc (sampled)")
+    y = orc.dequant_sampled(acc_r, xs_r, ws_r, 0, None, r, cc)
+    side = orc.side_product_sampled(X, W16, ref_idx, r, cc)
+    assert_close(Y[r, cc], orc.combine_to_half(y, side), 1e-2)
