@@ -10,16 +10,20 @@
 // c ^ (r & 7), so the fragment reads (lane -> row lane%32, chunk lane/32) of a
 // wave hit distinct banks.
 //
-// MFMA operand use: lane l supplies 16 k-consecutive bytes of A row (l % 32) and
-// of B row (l % 32), k-chunk (l / 32); A and B use the same k placement, so any
+// MFMA operand use: lane l supplies 16 k-consecutive bytes of a weight row
+// (l % 32) as the instruction's A operand and of an activation row (l % 32) as
+// its B operand, k-chunk (l / 32); both use the same k placement, so any
 // internal pairing of k slots the instruction applies is the same on both sides
 // and the dot product is exact.  Result lane l, register r holds
-// D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+// D[8*(r/4) + 4*(l/32) + r%4][l % 32] = (output column, output row), so each
+// lane owns runs of four consecutive output columns.
 //
 // LLM.int8() ["LLM.int8()技术解析", section 3.1]: when a side product is
 // requested, the dequantized tile becomes the C input of
 // v_mfma_f32_32x32x16_f16 over the gathered fp16 outlier columns, so the fp16
 // result adds onto the int8 result inside the same kernel.
+#include <type_traits>
+
 #include "sq_internal.h"
 
 namespace sq {
@@ -28,20 +32,48 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// LDS slot swizzle: 16-byte chunk c of tile row r is stored at slot c ^ ((r >> SWZ) & 7).
+#ifndef SQ_GEMM_SWZ
+#define SQ_GEMM_SWZ 1
+#endif
+
+// Waits and barriers.  __syncthreads() would also make the compiler wait for
+// every outstanding load before the barrier; these helpers wait for exactly
+// what the pipeline needs, with the s_waitcnt builtin (which the compiler's
+// own wait tracking sees), and the empty asm statements keep LDS accesses from
+// being moved across them.
+__device__ __forceinline__ void wait_all_loads() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0), vm/exp counts unconstrained
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int BM, int BN, bool OUT_F16, bool SIDE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
     void* __restrict__ Yv, int32_t* __restrict__ acc_out, const _Float16* __restrict__ Xo,
     const _Float16* __restrict__ Wo, const int32_t* __restrict__ cnt, int64_t ldo, int tiles_m, int tiles_n) {
-    constexpr int BK = 128;
+    constexpr int BK = 128;                  // bytes of K per stage: one cache line per row
+    constexpr int S = 2;                     // LDS stages
+    constexpr int KS = BK / 32;              // MFMA k-steps per stage
     constexpr int WTM = BM / 2, WTN = BN / 2;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int KCH = BK / 16;
-    constexpr int A_CH = BM * KCH / kThreads;
-    constexpr int B_CH = BN * KCH / kThreads;
     constexpr int STAGE = (BM + BN) * BK;
-    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+    constexpr int NBLK = (BM + BN) / 8;      // 1 KB DMA blocks (8 rows) per stage
+    constexpr int L = NBLK / 4;              // DMA instructions per wave per stage
+    static_assert(NBLK % 4 == 0, "stage must split evenly over 4 waves");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[S * STAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -65,39 +97,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int tn = (t % per_group) / gsz;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // global -> register staging
-    v4i ra[A_CH], rb[B_CH];
-    auto gload = [&](int k0) {
+    // LDS layout of a stage: A rows [0, BM) then B rows, 128 bytes each; the
+    // 16-byte chunk c of row r sits at slot c ^ swz(r).
+    auto swz = [](int r) { return (r >> SQ_GEMM_SWZ) & 7; };
+
+    // DMA addressing: wave w fills 1 KB blocks w, w+4, ...; lane l writes row
+    // (block*8 + l/8), slot l%8, so it fetches logical chunk (l%8) ^ swz(row).
+    // Rows past M (N) are clamped: they only feed outputs that are never stored.
+    const int8_t* src[L];
+    int ldsoff[L];
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int id = tid + i * kThreads;
-            const int row = id / KCH, kc = id % KCH;
-            const int gr = m0 + row, gk = k0 + kc * 16;
-            if (gr < M && gk < K) ra[i] = *reinterpret_cast<const v4i*>(A + (int64_t)gr * K + gk);
-            else ra[i] = v4i{0, 0, 0, 0};
-        }
+    for (int i = 0; i < L; ++i) {
+        const int blk = wave + 4 * i;
+        const bool isA = blk < BM / 8;
+        const int row = (isA ? blk : blk - BM / 8) * 8 + (lane >> 3);
+        const int kc = (lane & 7) ^ swz(row);
+        int g = (isA ? m0 : n0) + row;
+        const int lim = isA ? M : N;
+        g = g < lim ? g : lim - 1;
+        src[i] = (isA ? A : B) + (int64_t)g * K + kc * 16;
+        ldsoff[i] = blk * 1024;
+    }
+    auto dma = [&](int stage, int k0) {
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int id = tid + i * kThreads;
-            const int row = id / KCH, kc = id % KCH;
-            const int gr = n0 + row, gk = k0 + kc * 16;
-            if (gr < N && gk < K) rb[i] = *reinterpret_cast<const v4i*>(B + (int64_t)gr * K + gk);
-            else rb[i] = v4i{0, 0, 0, 0};
-        }
+        for (int i = 0; i < L; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), (void*)(lds + stage * STAGE + ldsoff[i]), 16,
+                                             0, 0);
     };
-    auto lstore = [&](int buf) {
-        int8_t* base = lds + buf * STAGE;
+    // Partial K tile (K % 128 != 0): through registers with zero fill.
+    auto tail_tile = [&](int stage, int k0) {
+        const int kc = tid & 7, r0 = tid >> 3;    // chunk tid%8 of rows tid/8 + 32 i
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int id = tid + i * kThreads;
-            const int row = id / KCH, kc = id % KCH;
-            *reinterpret_cast<v4i*>(base + row * BK + ((kc ^ (row & 7)) << 4)) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int id = tid + i * kThreads;
-            const int row = id / KCH, kc = id % KCH;
-            *reinterpret_cast<v4i*>(base + BM * BK + row * BK + ((kc ^ (row & 7)) << 4)) = rb[i];
+        for (int i = 0; i < (BM + BN) / 32; ++i) {
+            const int rr = r0 + 32 * i;
+            const bool isA = rr < BM;
+            const int row = isA ? rr : rr - BM;
+            int g = (isA ? m0 : n0) + row;
+            const int lim = isA ? M : N;
+            g = g < lim ? g : lim - 1;
+            const int8_t* p = (isA ? A : B) + (int64_t)g * K + k0 + kc * 16;
+            const v4i v = (k0 + kc * 16 < K) ? *reinterpret_cast<const v4i*>(p) : v4i{0, 0, 0, 0};
+            *reinterpret_cast<v4i*>(lds + stage * STAGE + rr * BK + ((kc ^ swz(row)) << 4)) = v;
         }
     };
 
@@ -107,102 +147,193 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
 
-    const int nk = (K + BK - 1) / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
     const int lrow = lane & 31, lk = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const int8_t* As = lds + buf * STAGE;
+    v4i af[2][TM], bf[2][TN];
+    auto fload = [&](int stage, int ks, int slot) {
+        const int c = ks * 2 + lk;
+        const int8_t* As = lds + stage * STAGE;
         const int8_t* Bs = As + BM * BK;
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            const int kc = ks * 2 + lk;
-            v4i af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 32 + lrow;
-                af[i] = *reinterpret_cast<const v4i*>(As + row * BK + ((kc ^ (row & 7)) << 4));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int row = wn * WTN + j * 32 + lrow;
-                bf[j] = *reinterpret_cast<const v4i*>(Bs + row * BK + ((kc ^ (row & 7)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + lrow;
+            af[slot][i] = *reinterpret_cast<const v4i*>(As + row * BK + ((c ^ swz(row)) << 4));
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue, one 32 x 32 tile at a time (keeps register pressure at the
-    // accumulators): y = ((float)acc * xs[m]) * ws[n] (+ bias[n]) [+ fp16 side]
-    const int rbase = m0 + wm * WTM + 4 * lk;   // + i*32 + 8*(r/4) + r%4
-    const int cbase = n0 + wn * WTN + lrow;     // + j*32
-    const int side_cnt = SIDE ? *cnt : 0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = cbase + j * 32;
-            const bool cok = col < N;
-            const float wsv = cok ? ws[(int64_t)col * ws_stride] : 0.0f;
-            const float bv = (bias != nullptr && cok) ? bias[col] : 0.0f;
-            v16f y;
+            const int row = wn * WTN + j * 32 + lrow;
+            bf[slot][j] = *reinterpret_cast<const v4i*>(Bs + row * BK + ((c ^ swz(row)) << 4));
+        }
+    };
+    auto mfmas = [&](int slot) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-                const float xsv = row < M ? xs[row] : 0.0f;
-                float v = (float)acc[i][j][r];
-                v = v * xsv;
-                v = v * wsv;
-                if (bias != nullptr) v = v + bv;
-                y[r] = v;
-            }
-            if (acc_out != nullptr && cok) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < M) acc_out[(int64_t)row * N + col] = acc[i][j][r];
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[slot][j], af[slot][i], acc[i][j], 0, 0, 0);
+    };
+
+    // Tile order: [partial tail], 0, 1, ..., nfull-1.  Tile j lives in stage j % 2.
+    const int nfull = K / BK;
+    const bool has_tail = (K % BK) != 0;
+    const int nk = nfull + (has_tail ? 1 : 0);
+    auto kofs = [&](int j) { return (has_tail ? (j == 0 ? nfull : j - 1) : j) * BK; };
+    if (has_tail) tail_tile(0, kofs(0));
+    else dma(0, kofs(0));
+    wait_all_loads();
+    block_barrier();
+    fload(0, 0, 0);
+
+    for (int j = 0; j < nk; ++j) {
+        const int st = j & 1;
+        const bool more = j + 1 < nk;
+        // the other stage held tile j-1, which every wave finished reading
+        // before the previous barrier
+        if (more) dma(st ^ 1, kofs(j + 1));
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            fload(st, ks + 1, (ks + 1) & 1);
+            mfmas(ks & 1);
+        }
+        if (more) {
+            // tile j+1 landed for every wave, and tile j's last fragments are in registers
+            wait_all_loads();
+            block_barrier();
+            fload(st ^ 1, 0, 0);
+        }
+        mfmas((KS - 1) & 1);
+    }
+
+    // ---- epilogue, staged through LDS.
+    // With the weight fragment as the instruction's A operand, lane l, register
+    // 4a+b of tile (i, j) holds output row  wm*WTM + i*32 + l%32  and column
+    // wn*WTN + j*32 + 8a + 4(l/32) + b  (runs of four consecutive columns).
+    //   y = ((float)acc * xs[m]) * ws[n] (+ bias[n])   [+ fp16 side product]
+    // Each wave writes its y values, already in the output dtype, into an LDS
+    // copy of the block tile (16-byte chunks XOR-swizzled by row); the block then
+    // writes the tile out with 16-byte stores, row by row.  fp32 output goes in
+    // two halves of the tile rows (the LDS ring holds half a 256 x 256 fp32 tile).
+    constexpr int OB = OUT_F16 ? 2 : 4;                  // output bytes
+    constexpr int HALVES = OUT_F16 ? 1 : 2;
+    constexpr int TMH = TM / HALVES;                     // tiles per wave per half
+    constexpr int HROWS = BM / HALVES;                   // tile rows per half
+    constexpr int RB = BN * OB;                          // LDS bytes per tile row
+    constexpr int CH16 = RB / 16;                        // 16-byte chunks per row
+    static_assert(HROWS * RB <= S * STAGE, "epilogue tile must fit the LDS ring");
+    constexpr int SWM = CH16 % 16 == 0 ? 15 : (CH16 % 8 == 0 ? 7 : (CH16 % 4 == 0 ? 3 : 0));   // XOR mask
+    __shared__ float sxs[BM], sws[BN], sbias[BN];
+    auto lofs = [&](int r, int cbyte) {                  // LDS byte offset of (row, byte in row)
+        return r * RB + ((((cbyte >> 4) ^ (r & SWM))) << 4) + (cbyte & 15);
+    };
+
+    wait_all_loads();
+    block_barrier();                                      // ring no longer read
+    for (int r = tid; r < BM; r += kThreads) {
+        const int m = m0 + r;
+        sxs[r] = xs[m < M ? m : M - 1];
+    }
+    for (int c = tid; c < BN; c += kThreads) {
+        const int n = n0 + c < N ? n0 + c : N - 1;
+        sws[c] = ws[(int64_t)n * ws_stride];
+        sbias[c] = bias != nullptr ? bias[n] : 0.0f;
+    }
+    const int side_cnt = SIDE ? *cnt : 0;
+    wait_all_loads();
+    block_barrier();
+
+    for (int h = 0; h < HALVES; ++h) {
+        // write phase
+#pragma unroll
+        for (int ii = 0; ii < TMH; ++ii) {
+            const int i = h * TMH + ii;
+            const int lr = wm * (TMH * 32) + ii * 32 + lrow;      // LDS row
+            const int mloc = wm * WTM + i * 32 + lrow;           // tile row
+            const float xsv = sxs[mloc];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                v16f y;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int nloc = wn * WTN + j * 32 + 8 * a + 4 * lk;
+                    const v4f w4 = *reinterpret_cast<const v4f*>(&sws[nloc]);
+                    const v4f b4 = *reinterpret_cast<const v4f*>(&sbias[nloc]);
+                    int iv[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        // read the accumulator register directly, one value at a time
+                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(iv[b]) : "a"(acc[i][j][4 * a + b]));
+                        float v = (float)iv[b];
+                        v = v * xsv;
+                        v = v * w4[b];
+                        if (bias != nullptr) v = v + b4[b];
+                        y[4 * a + b] = v;
+                    }
+                    if (acc_out != nullptr) {
+                        const int m = m0 + mloc;
+                        const int n = n0 + nloc;
+                        if (m < M)
+                            for (int b = 0; b < 4; ++b)
+                                if (n + b < N) acc_out[(int64_t)m * N + n + b] = iv[b];
+                    }
+                }
+                if constexpr (SIDE) {
+                    // fp16 side product over the gathered outlier columns, same operand roles
+                    const int arow = m0 + mloc;
+                    const int bcol = n0 + wn * WTN + j * 32 + lrow;
+                    for (int t0 = 0; t0 < side_cnt; t0 += 16) {
+                        const int tk = t0 + 8 * lk;   // this lane's 8 k-slots
+                        h8 xa{}, wb{};
+                        if (arow < M) {
+                            const _Float16* p = Xo + (int64_t)arow * ldo + tk;
+                            if (tk + 8 <= side_cnt) xa = *reinterpret_cast<const h8*>(p);
+                            else
+                                for (int e = 0; e < 8; ++e) xa[e] = tk + e < side_cnt ? p[e] : (_Float16)0.0f;
+                        }
+                        if (bcol < N) {
+                            const _Float16* p = Wo + (int64_t)bcol * ldo + tk;
+                            if (tk + 8 <= side_cnt) wb = *reinterpret_cast<const h8*>(p);
+                            else
+                                for (int e = 0; e < 8; ++e) wb[e] = tk + e < side_cnt ? p[e] : (_Float16)0.0f;
+                        }
+                        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb, xa, y, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int cb = (wn * WTN + j * 32 + 8 * a + 4 * lk) * OB;
+                    if constexpr (OUT_F16) {
+                        *reinterpret_cast<h4*>(lds + lofs(lr, cb)) =
+                            h4{(_Float16)y[4 * a], (_Float16)y[4 * a + 1], (_Float16)y[4 * a + 2], (_Float16)y[4 * a + 3]};
+                    } else {
+                        *reinterpret_cast<v4f*>(lds + lofs(lr, cb)) = v4f{y[4 * a], y[4 * a + 1], y[4 * a + 2], y[4 * a + 3]};
+                    }
                 }
             }
-            if constexpr (SIDE) {
-                const int arow = m0 + wm * WTM + i * 32 + lrow;
-                const int bcol = n0 + wn * WTN + j * 32 + lrow;
-                for (int t0 = 0; t0 < side_cnt; t0 += 16) {
-                    const int tk = t0 + 8 * lk;   // this lane's 8 k-slots
-                    h8 xa{}, wb{};
-                    if (arow < M) {
-                        const _Float16* p = Xo + (int64_t)arow * ldo + tk;
-                        if (tk + 8 <= side_cnt) xa = *reinterpret_cast<const h8*>(p);
-                        else
-                            for (int e = 0; e < 8; ++e) xa[e] = tk + e < side_cnt ? p[e] : (_Float16)0.0f;
-                    }
-                    if (bcol < N) {
-                        const _Float16* p = Wo + (int64_t)bcol * ldo + tk;
-                        if (tk + 8 <= side_cnt) wb = *reinterpret_cast<const h8*>(p);
-                        else
-                            for (int e = 0; e < 8; ++e) wb[e] = tk + e < side_cnt ? p[e] : (_Float16)0.0f;
-                    }
-                    y = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, y, 0, 0, 0);
-                }
+        }
+        wait_lds();
+        block_barrier();
+        // copy phase: 16-byte chunks, consecutive threads along a row
+        const bool vec = (N * OB) % 16 == 0;
+        for (int q = tid; q < HROWS * CH16; q += kThreads) {
+            const int lr = q / CH16, c = q % CH16;
+            const int wmq = lr / (TMH * 32), rem = lr % (TMH * 32);
+            const int m = m0 + wmq * WTM + (h * TMH + rem / 32) * 32 + rem % 32;
+            if (m >= M) continue;
+            const int n = n0 + c * (16 / OB);
+            const v4i v = *reinterpret_cast<const v4i*>(lds + lofs(lr, c * 16));
+            char* dst = reinterpret_cast<char*>(Yv) + ((int64_t)m * N + n) * OB;
+            if (vec && n + 16 / OB <= N) {
+                *reinterpret_cast<v4i*>(dst) = v;
+            } else {
+                const char* src = reinterpret_cast<const char*>(&v);
+                for (int e = 0; e < 16 / OB; ++e)
+                    if (n + e < N)
+                        for (int bb = 0; bb < OB; ++bb) dst[e * OB + bb] = src[e * OB + bb];
             }
-            if (!cok) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-                if (row >= M) continue;
-                if constexpr (OUT_F16)
-                    reinterpret_cast<_Float16*>(Yv)[(int64_t)row * N + col] = (_Float16)y[r];
-                else
-                    reinterpret_cast<float*>(Yv)[(int64_t)row * N + col] = y[r];
-            }
+        }
+        if (h + 1 < HALVES) {
+            wait_lds();
+            block_barrier();
         }
     }
 }
@@ -238,10 +369,26 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
-    // Large problems: 256 x 256 tiles; otherwise 128 x 128 to keep more blocks.
-    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (big_tiles >= (int64_t)dev_info().cus)
-        return dispatch<256, 256>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
+    // Pick the tile shape whose last round of blocks is fullest: each block
+    // holds one CU, so time ~ ceil(tiles / CUs) * tile area.
+    const int64_t cus = dev_info().cus;
+    struct Cand { int bm, bn; };
+    const Cand cands[] = {{256, 256}, {256, 192}, {128, 128}};
+    int best = 2;
+    double best_cost = 1e300;
+    for (int c = 0; c < 3; ++c) {
+        const int64_t tiles = ((M + cands[c].bm - 1) / cands[c].bm) * ((N + cands[c].bn - 1) / cands[c].bn);
+        const int64_t rounds = (tiles + cus - 1) / cus;
+        // 128 x 128 tiles run two blocks per CU at lower MFMA efficiency
+        const double eff = cands[c].bm == 128 ? 0.5 : 1.0;
+        const double cost = (double)rounds * cands[c].bm * cands[c].bn / eff / (cands[c].bm == 128 ? 2.0 : 1.0);
+        if (cost < best_cost * 0.999) {
+            best_cost = cost;
+            best = c;
+        }
+    }
+    if (best == 0) return dispatch<256, 256>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
+    if (best == 1) return dispatch<256, 192>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
     return dispatch<128, 128>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
 }
 
