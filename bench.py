@@ -270,7 +270,8 @@ def main():
             "mfma_frac_incl_quant": round(tops / PEAK_INT8_TOPS, 4),
             "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                          "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                         "kernel": "gemm_i8_kernel<256,256,fp16>", "gemm_us_per_launch": round(r["gemm_ms"] * 1e3, 2),
+                         "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue)",
+                         "gemm_us_per_launch": round(r["gemm_ms"] * 1e3, 2),
                          "algorithmic_ops_per_launch": r["gemm_ops_per_launch"]},
         }
         if not args.no_cpu_baseline:

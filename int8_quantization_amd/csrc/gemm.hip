@@ -369,19 +369,19 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
-    // Pick the tile shape whose last round of blocks is fullest: each block
-    // holds one CU, so time ~ ceil(tiles / CUs) * tile area.
+    // Pick the tile shape with the least estimated time: a 256-row tile takes a
+    // whole CU, so time ~ ceil(tiles / CUs) * area; 128 x 128 tiles run two per
+    // CU at about half the per-CU rate (twice the operand traffic per MFMA).
     const int64_t cus = dev_info().cus;
-    struct Cand { int bm, bn; };
-    const Cand cands[] = {{256, 256}, {256, 192}, {128, 128}};
-    int best = 2;
+    struct Cand { int bm, bn, per_cu; double rate; };
+    const Cand cands[] = {{256, 256, 1, 1.0}, {256, 192, 1, 1.0}, {128, 128, 2, 0.5}};
+    int best = 0;
     double best_cost = 1e300;
     for (int c = 0; c < 3; ++c) {
         const int64_t tiles = ((M + cands[c].bm - 1) / cands[c].bm) * ((N + cands[c].bn - 1) / cands[c].bn);
-        const int64_t rounds = (tiles + cus - 1) / cus;
-        // 128 x 128 tiles run two blocks per CU at lower MFMA efficiency
-        const double eff = cands[c].bm == 128 ? 0.5 : 1.0;
-        const double cost = (double)rounds * cands[c].bm * cands[c].bn / eff / (cands[c].bm == 128 ? 2.0 : 1.0);
+        const int64_t slots = cus * cands[c].per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double cost = (double)rounds * cands[c].per_cu * cands[c].bm * cands[c].bn / cands[c].rate;
         if (cost < best_cost * 0.999) {
             best_cost = cost;
             best = c;

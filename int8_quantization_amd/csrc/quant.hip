@@ -8,6 +8,7 @@
 // All of these are HBM-bound: 16-byte coalesced loads, wave-shuffle reductions,
 // packed int8 stores.
 #include <mutex>
+#include <type_traits>
 
 #include "sq_internal.h"
 
@@ -59,6 +60,7 @@ template <> struct Chunk<float> {
     using V = v4f;
     static constexpr int N = 4;
 };
+template <typename T, int VEC> struct VecOf { typedef T V __attribute__((ext_vector_type(VEC))); };
 
 template <int VEC> struct CodeStore;
 template <> struct CodeStore<8> {
@@ -80,110 +82,138 @@ template <> struct CodeStore<4> {
 // ---------------------------------------------------------------------------
 // Fused smoothing + per-row quantization, register-resident rows.
 //
-// A block of T threads owns whole rows; thread t owns the 16-byte chunks
-// t, t+T, ... (CH of them) of every row it visits, so the per-column constants
-// (reciprocal of s_j, or s_j, or the outlier slot) are computed once per block
-// and kept in registers, and blocks loop over rows m = blockIdx.x + i*gridDim.x
-// with the next row's loads issued before the current row's reduction.
+// A block holds G row groups of TPG threads; thread t of a group owns the
+// 16-byte chunks t, t+TPG, ... (CH of them) of every row the group visits.
+// The per-column constants (fp64 reciprocal of s_j, or s_j, or the outlier
+// slot) are computed once per block and kept in registers while the block
+// walks rows m = (blockIdx.x + i*gridDim.x)*G + g; the next row's loads are
+// issued before the current row's reduction.
 //   mode 0: x' = x;   mode 1: x' = fl32(x / s_j);   mode 2: x' = fl32(x * s_j)
 //   xs = fl32(max |x'| / 127) over non-outlier columns
 //   q  = clamp(rne(fl32(x' / xs)), -128, 127), 0 for outlier columns or xs == 0
+// Both divisions are exact fp32 quotients computed as RN32(RN64(a * RN64(1/b)))
+// (see div_rcp64).  A quotient below the fp32 normal range takes the IEEE
+// division for x / s_j (only possible for fp32 inputs or s_j > 2^100); for
+// x' / xs such a quotient is below 0.5 and its code is 0 either way.
 // ---------------------------------------------------------------------------
-template <typename T, int CH, int MODE, bool OUTL>
+template <typename T, int VEC, int CH, int MODE, bool OUTL>
 __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X, int64_t M, int64_t K,
                                                         const float* __restrict__ s, int8_t* __restrict__ Xq,
                                                         float* __restrict__ scale, const int32_t* __restrict__ pos,
-                                                        _Float16* __restrict__ Xo) {
-    using V = typename Chunk<T>::V;
-    constexpr int VEC = Chunk<T>::N;
+                                                        _Float16* __restrict__ Xo, int tpg, int G) {
+    using V = typename VecOf<T, VEC>::V;
     __shared__ float red[2][16];
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int wave = tid >> 6, lane = tid & 63, nwaves = nthr >> 6;
+    const int g = threadIdx.x / tpg;          // row group
+    const int tid = threadIdx.x - g * tpg;    // thread within the group
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w0 = (g * tpg) >> 6, nw = tpg >> 6;   // this group's waves
     const int64_t nchunk = K / VEC;
 
-    double rs[MODE == 1 ? CH : 1][VEC];
-    float sv[MODE == 2 ? CH : 1][VEC];
-    int pv[OUTL ? CH : 1][VEC];
+
     bool valid[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        int64_t c = tid + (int64_t)i * nthr;
-        valid[i] = c < nchunk;
-        int64_t cc = valid[i] ? c : 0;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            if constexpr (MODE == 1) rs[i][e] = 1.0 / (double)s[cc * VEC + e];
-            if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
-            if constexpr (OUTL) pv[i][e] = valid[i] ? pos[cc * VEC + e] : -1;
-        }
-    }
-
-    V rc[CH], rn[CH];
+    for (int i = 0; i < CH; ++i) valid[i] = tid + (int64_t)i * tpg < nchunk;
+    // Rows are prefetched PF iterations ahead (PF = 2 when registers allow).
+    constexpr int PF = (CH <= 2) ? 2 : 1;
+    V buf[PF + 1][CH];
     auto load_row = [&](int64_t row, V* r) {
         const V* src = reinterpret_cast<const V*>(X + row * K);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            int64_t c = tid + (int64_t)i * nthr;
-            if (valid[i]) r[i] = src[c];
+            const int64_t c = tid + (int64_t)i * tpg;
+            if (valid[i] && row < M) r[i] = src[c];
             else r[i] = V{};
         }
     };
 
-    int64_t m = blockIdx.x;
-    if (m < M) load_row(m, rc);
-    int it = 0;
-    for (; m < M; m += gridDim.x, ++it) {
+    const int64_t step = (int64_t)gridDim.x * G;
+    int64_t m = (int64_t)blockIdx.x * G + g;
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_row(m + p * step, buf[p]);
+    // per-column constants, computed while the first rows are in flight
+    double rs[MODE == 1 ? CH : 1][VEC];
+    float sv[MODE == 2 ? CH : 1][VEC];
+    int pv[OUTL ? CH : 1][VEC];
+    bool guard = false;                       // some x/s_j may fall below the normal range
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int64_t c = tid + (int64_t)i * tpg;
+        const int64_t cc = valid[i] ? c : 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (MODE == 1) {
+                const float sj = s[cc * VEC + e];
+                rs[i][e] = 1.0 / (double)sj;
+                guard = guard || !(sj < 0x1p100f);
+            }
+            if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
+            if constexpr (OUTL) pv[i][e] = valid[i] ? pos[cc * VEC + e] : -1;
+        }
+    }
+    if constexpr (sizeof(T) == 4) guard = true;   // fp32 inputs can be subnormal
+    // every group runs the same number of iterations (barriers are block wide)
+    const int64_t first = (int64_t)blockIdx.x * G;
+    const int64_t iters = first < M ? (M - first + step - 1) / step : 0;
+    for (int64_t it = 0; it < iters; ++it, m += step) {
+        load_row(m + PF * step, buf[PF]);       // in flight during this whole row
+        const bool live = m < M;
+        V* rc = buf[0];
         float xv[CH][VEC];
         float amax = 0.0f;
+        auto pass1 = [&](auto guarded) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            int64_t c = tid + (int64_t)i * nthr;
+            for (int i = 0; i < CH; ++i) {
+                const int64_t c = tid + (int64_t)i * tpg;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float x = (float)rc[i][e];
-                if constexpr (MODE == 1) {
-                    float q = (float)((double)x * rs[i][e]);
-                    if (__builtin_fabsf(q) < 1.17549435e-38f && x != 0.0f) q = x / s[c * VEC + e];
-                    x = q;
+                for (int e = 0; e < VEC; ++e) {
+                    float x = (float)rc[i][e];
+                    if constexpr (MODE == 1) {
+                        float q = (float)((double)x * rs[i][e]);
+                        if constexpr (decltype(guarded)::value)
+                            if (__builtin_fabsf(q) < 1.17549435e-38f && x != 0.0f) q = x / s[c * VEC + e];
+                        x = q;
+                    }
+                    if constexpr (MODE == 2) x = x * sv[i][e];
+                    xv[i][e] = x;
+                    bool skip = false;
+                    if constexpr (OUTL) {
+                        skip = pv[i][e] >= 0;
+                        if (skip && live) Xo[m * K + pv[i][e]] = (_Float16)rc[i][e];
+                    }
+                    if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
                 }
-                if constexpr (MODE == 2) x = x * sv[i][e];
-                xv[i][e] = x;
-                bool skip = false;
-                if constexpr (OUTL) {
-                    skip = pv[i][e] >= 0;
-                    if (skip) Xo[m * K + pv[i][e]] = (_Float16)rc[i][e];
-                }
-                if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
             }
-        }
-        int64_t mn = m + gridDim.x;
-        if (mn < M) load_row(mn, rn);
+        };
+        if (MODE == 1 && guard) pass1(std::true_type{});
+        else pass1(std::false_type{});
 
         amax = wave_max(amax);
         if (lane == 0) red[it & 1][wave] = amax;
         __syncthreads();
-        float a = red[it & 1][0];
-        for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[it & 1][w]);
+        float a = red[it & 1][w0];
+        for (int w = 1; w < nw; ++w) a = __builtin_fmaxf(a, red[it & 1][w0 + w]);
         const float xs = a / 127.0f;
-        if (tid == 0) scale[m] = xs;
-        const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
-
+        if (live) {
+            if (tid == 0) scale[m] = xs;
+            const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            if (!valid[i]) continue;
-            int64_t c = tid + (int64_t)i * nthr;
-            int q[VEC];
+            for (int i = 0; i < CH; ++i) {
+                if (!valid[i]) continue;
+                const int64_t c = tid + (int64_t)i * tpg;
+                int q[VEC];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                bool zero = xs == 0.0f;
-                if constexpr (OUTL) zero = zero || pv[i][e] >= 0;
-                q[e] = zero ? 0 : code_of(div_rcp64(xv[i][e], rx, xs));
+                for (int e = 0; e < VEC; ++e) {
+                    bool zero = xs == 0.0f;
+                    if constexpr (OUTL) zero = zero || pv[i][e] >= 0;
+                    q[e] = zero ? 0 : code_of((float)((double)xv[i][e] * rx));
+                }
+                CodeStore<VEC>::store(Xq + m * K + c * VEC, q);
             }
-            CodeStore<VEC>::store(Xq + m * K + c * VEC, q);
         }
 #pragma unroll
-        for (int i = 0; i < CH; ++i) rc[i] = rn[i];
+        for (int p = 0; p < PF; ++p)
+#pragma unroll
+            for (int i = 0; i < CH; ++i) buf[p][i] = buf[p + 1][i];
     }
 }
 
@@ -239,48 +269,41 @@ static int blocks_per_cu(Kern k, int threads) {
     return nb;
 }
 
+template <typename T, int VEC, int CH, int MODE, bool OUTL>
+static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
+                              const int32_t* pos, _Float16* Xo, hipStream_t st) {
+    const int64_t nchunk = K / VEC;
+    const int tpg = (int)((((nchunk + CH - 1) / CH) + 63) / 64 * 64);   // threads per row group
+    const int G = 1024 / tpg;                                          // row groups per block
+    const int threads = G * tpg;
+    auto k = quant_rows_fast<T, VEC, CH, MODE, OUTL>;
+    static int nb_cache[1025] = {0};
+    int nb = nb_cache[threads];
+    if (nb == 0) nb_cache[threads] = nb = blocks_per_cu(k, threads);
+    const int64_t rows_blocks = (M + G - 1) / G;
+    const int64_t g = (int64_t)dev_info().cus * nb;
+    hipLaunchKernelGGL(k, dim3((unsigned)(g < rows_blocks ? g : rows_blocks)), dim3(threads), 0, st, X, M, K, s, Xq,
+                       scale, pos, Xo, tpg, G);
+    return hipGetLastError();
+}
+
+// Register-resident variants by row length (elements per thread <= 20), else the
+// two-pass fallback.
 template <typename T, int MODE, bool OUTL>
 static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
                                const int32_t* pos, _Float16* Xo, hipStream_t st) {
-    constexpr int VEC = Chunk<T>::N;
-    const int64_t nchunk = K / VEC;
-    int threads = (int)((nchunk + 63) / 64 * 64);
-    int ch = 1;
-    if (threads > 1024) {
-        ch = (int)((nchunk + 1023) / 1024);
-        threads = 1024;
+    if constexpr (sizeof(T) == 2) {
+        if (K <= 1024) return launch_fast<T, 8, 1, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 16384) return launch_fast<T, 8, 2, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 20480) return launch_fast<T, 4, 5, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+    } else {
+        if (K <= 4096) return launch_fast<T, 4, 1, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 8192) return launch_fast<T, 4, 2, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 12288) return launch_fast<T, 4, 3, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
     }
-    if (threads < 64) threads = 64;
-    const int cus = dev_info().cus;
-    auto grid_for = [&](auto kern) {
-        static int cache[1025] = {0};  // per thread count, for this instantiation
-        int nb = cache[threads];
-        if (nb == 0) cache[threads] = nb = blocks_per_cu(kern, threads);
-        int64_t g = (int64_t)cus * nb;
-        return (unsigned)(g < M ? g : M);
-    };
-    switch (ch) {
-        case 1: {
-            auto k = quant_rows_fast<T, 1, MODE, OUTL>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(threads), 0, st, X, M, K, s, Xq, scale, pos, Xo);
-            break;
-        }
-        case 2: {
-            auto k = quant_rows_fast<T, 2, MODE, OUTL>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(threads), 0, st, X, M, K, s, Xq, scale, pos, Xo);
-            break;
-        }
-        case 3: {
-            auto k = quant_rows_fast<T, 3, MODE, OUTL>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(threads), 0, st, X, M, K, s, Xq, scale, pos, Xo);
-            break;
-        }
-        default: {
-            auto k = quant_rows_generic<T, MODE, OUTL>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
-            break;
-        }
-    }
+    auto k = quant_rows_generic<T, MODE, OUTL>;
+    const int64_t g = (int64_t)dev_info().cus * 2;
+    hipLaunchKernelGGL(k, dim3((unsigned)(g < M ? g : M)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
     return hipGetLastError();
 }
 

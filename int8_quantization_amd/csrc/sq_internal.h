@@ -33,8 +33,7 @@ __device__ __forceinline__ float div_rcp64(float a, double rb, float b) {
 
 // Integer code: round half to even (v_rndne_f32), clamp to [-128, 127].
 __device__ __forceinline__ int code_of(float v) {
-    float r = __builtin_rintf(v);
-    r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+    const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(v), -128.0f, 127.0f);
     return (int)r;
 }
 
