@@ -30,7 +30,15 @@ namespace sq {
 
 namespace {
 
-constexpr int kThreads = 256;
+// Wave grids of the two large tile shapes (waves = WM x WN, 2 waves per SIMD at 8).
+#ifndef SQ_W256_WM
+#define SQ_W256_WM 2
+#define SQ_W256_WN 4
+#endif
+#ifndef SQ_W192_WM
+#define SQ_W192_WM 4
+#define SQ_W192_WN 2
+#endif
 
 // LDS slot swizzle: 16-byte chunk c of tile row r is stored at slot c ^ ((r >> SWZ) & 7).
 #ifndef SQ_GEMM_SWZ
@@ -58,8 +66,8 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, bool OUT_F16, bool SIDE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
+template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
     void* __restrict__ Yv, int32_t* __restrict__ acc_out, const _Float16* __restrict__ Xo,
@@ -67,17 +75,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     constexpr int BK = 128;                  // bytes of K per stage: one cache line per row
     constexpr int S = 2;                     // LDS stages
     constexpr int KS = BK / 32;              // MFMA k-steps per stage
-    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int NW = WM * WN;              // waves, in a WM x WN grid over the tile
+    constexpr int NT = 64 * NW;              // threads
+    constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile must be a multiple of 32");
     constexpr int STAGE = (BM + BN) * BK;
     constexpr int NBLK = (BM + BN) / 8;      // 1 KB DMA blocks (8 rows) per stage
-    constexpr int L = NBLK / 4;              // DMA instructions per wave per stage
-    static_assert(NBLK % 4 == 0, "stage must split evenly over 4 waves");
+    constexpr int L = NBLK / NW;             // DMA instructions per wave per stage
+    static_assert(NBLK % NW == 0, "stage must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) int8_t lds[S * STAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     // Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
     // contiguous range of logical tiles, ordered in groups of 8 tile-rows so the
@@ -101,14 +112,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     // 16-byte chunk c of row r sits at slot c ^ swz(r).
     auto swz = [](int r) { return (r >> SQ_GEMM_SWZ) & 7; };
 
-    // DMA addressing: wave w fills 1 KB blocks w, w+4, ...; lane l writes row
+    // DMA addressing: wave w fills 1 KB blocks w, w+NW, ...; lane l writes row
     // (block*8 + l/8), slot l%8, so it fetches logical chunk (l%8) ^ swz(row).
     // Rows past M (N) are clamped: they only feed outputs that are never stored.
     const int8_t* src[L];
     int ldsoff[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const int blk = wave + 4 * i;
+        const int blk = wave + NW * i;
         const bool isA = blk < BM / 8;
         const int row = (isA ? blk : blk - BM / 8) * 8 + (lane >> 3);
         const int kc = (lane & 7) ^ swz(row);
@@ -126,10 +137,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     };
     // Partial K tile (K % 128 != 0): through registers with zero fill.
     auto tail_tile = [&](int stage, int k0) {
-        const int kc = tid & 7, r0 = tid >> 3;    // chunk tid%8 of rows tid/8 + 32 i
+        const int kc = tid & 7, r0 = tid >> 3;    // chunk tid%8 of rows tid/8 + (NT/8) i
 #pragma unroll
-        for (int i = 0; i < (BM + BN) / 32; ++i) {
-            const int rr = r0 + 32 * i;
+        for (int i = 0; i < (BM + BN) / (NT / 8); ++i) {
+            const int rr = r0 + (NT / 8) * i;
             const bool isA = rr < BM;
             const int row = isA ? rr : rr - BM;
             int g = (isA ? m0 : n0) + row;
@@ -227,11 +238,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 
     wait_all_loads();
     block_barrier();                                      // ring no longer read
-    for (int r = tid; r < BM; r += kThreads) {
+    for (int r = tid; r < BM; r += NT) {
         const int m = m0 + r;
         sxs[r] = xs[m < M ? m : M - 1];
     }
-    for (int c = tid; c < BN; c += kThreads) {
+    for (int c = tid; c < BN; c += NT) {
         const int n = n0 + c < N ? n0 + c : N - 1;
         sws[c] = ws[(int64_t)n * ws_stride];
         sbias[c] = bias != nullptr ? bias[n] : 0.0f;
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         block_barrier();
         // copy phase: 16-byte chunks, consecutive threads along a row
         const bool vec = (N * OB) % 16 == 0;
-        for (int q = tid; q < HROWS * CH16; q += kThreads) {
+        for (int q = tid; q < HROWS * CH16; q += NT) {
             const int lr = q / CH16, c = q % CH16;
             const int wmq = lr / (TMH * 32), rem = lr % (TMH * 32);
             const int m = m0 + wmq * WTM + (h * TMH + rem / 32) * 32 + rem % 32;
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN, bool OUT_F16, bool SIDE>
+template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
 hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int32_t* acc_out, const SideArgs* side,
                hipStream_t st) {
@@ -347,21 +358,22 @@ hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float*
     const _Float16* Wo = side ? side->Wo : nullptr;
     const int32_t* cnt = side ? side->count : nullptr;
     const int64_t ldo = side ? side->ldo : 0;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, OUT_F16, SIDE>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, st,
-                       Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out, Xo, Wo, cnt, ldo, tm, tn);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE>), dim3((unsigned)(tm * tn)),
+                       dim3(64 * WM * WN), 0, st, Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out,
+                       Xo, Wo, cnt, ldo, tm, tn);
     return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                     const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
                     const SideArgs* side, hipStream_t st) {
     if (ydt == SQ_F16) {
-        if (side) return run<BM, BN, true, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
-        return run<BM, BN, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+        if (side) return run<BM, BN, WM, WN, true, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+        return run<BM, BN, WM, WN, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
     }
-    if (side) return run<BM, BN, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
-    return run<BM, BN, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+    if (side) return run<BM, BN, WM, WN, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+    return run<BM, BN, WM, WN, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
 }
 
 }  // namespace
@@ -387,9 +399,13 @@ hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
             best = c;
         }
     }
-    if (best == 0) return dispatch<256, 256>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
-    if (best == 1) return dispatch<256, 192>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
-    return dispatch<128, 128>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
+    if (best == 0)
+        return dispatch<256, 256, SQ_W256_WM, SQ_W256_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out,
+                                                          side, st);
+    if (best == 1)
+        return dispatch<256, 192, SQ_W192_WM, SQ_W192_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out,
+                                                          side, st);
+    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
 }
 
 }  // namespace sq
