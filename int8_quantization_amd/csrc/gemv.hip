@@ -1,72 +1,231 @@
 // Decode (skinny-M, M <= 16) int8 GEMM + dequant for gfx950.
 //
-// At M <= 16 the layer streams N x K int8 weight bytes once and reuses each of
-// them at most 16 times, so it is bound by HBM bandwidth, not by the matrix
-// cores.  A 256-thread block owns 16 output features; its 4 waves interleave
-// over 64-byte k blocks (wave w takes blocks w, w+4, ...), each lane loading 16
-// contiguous bytes of one weight row and of one activation row, and one
-// v_mfma_i32_16x16x64_i8 per k block folds all M tokens at once (rows >= M are
-// zero).  Eight k blocks are in flight per wave.  The four partial int32 tiles
-// are summed through LDS and the dequant epilogue
-// ["量化基础与INT8", INT8推理流程: acc * x_scale * w_scale] runs on wave 0.
-// Result lane l, register i holds D[4*(l/16) + i][l % 16] = (token, feature).
+// At M <= 16 the layer streams the N x K int8 weight bytes once and reuses each
+// of them at most 16 times, so it is bound by HBM bandwidth, not by the matrix
+// cores ["量化基础与INT8", INT8推理流程: int32 accumulation, then
+// acc * x_scale * w_scale].  Two things decide the bandwidth on MI355X: the
+// shape of each wave-wide load (HBM streams best when one load instruction
+// covers few rows with long contiguous runs; the 16-row x 64-byte operand shape
+// of v_mfma_i32_16x16x64_i8 reads measurably slower than 4 rows x 256 bytes),
+// and the order in which the chip walks the matrix (a compact front of rows in
+// flight beats every block streaming its own far-apart rows).
+//
+// Load shape.  With RPI rows per load (4 or 8), lane l reads 16 bytes of weight
+// row l % RPI at k0 + 16 * (l / RPI): one instruction covers RPI rows x
+// 1024 / RPI contiguous bytes.  The activation fragment uses the same pattern
+// with tokens in place of rows.  Fed as the A (activations) and B (weights)
+// operands of v_mfma_i32_16x16x64_i8, output (t, c) pairs A lanes 16g + t with
+// B lanes 16g + c; both hold the same k bytes exactly when t / RPI == c / RPI,
+// so those outputs are partial dot products of token t % RPI with row c % RPI
+// over the 16-byte chunks {(t / RPI) + (16 / RPI) * g}.  Summing them over the
+// 16 / RPI diagonal blocks gives the full product over the span; the other
+// outputs are ignored.  The matrix cores do 4x (RPI 4) or 2x (RPI 8) the
+// arithmetic of a dense layout, which they have to spare at this M.
+//
+// Work split.  A block of 8 waves owns tiles of TROWS = RG * RPI weight rows;
+// wave w owns a contiguous slice of every row's k range, so its activation
+// fragments are the same for every tile and stay in registers when they fit
+// (HOIST), else they are reloaded per k chunk (from L2).  Blocks are persistent
+// and take tiles blockIdx.x, blockIdx.x + gridDim.x, ..., so the rows in flight
+// across the chip form a compact front.  Each wave loads the next tile (or
+// chunk) before running the MFMAs of the current one; the 8 partial tiles are
+// summed through LDS and the dequant epilogue stores Y (and acc).
 #include "sq_internal.h"
 
 namespace sq {
 
 namespace {
 
-template <bool OUT_F16>
-__global__ __launch_bounds__(256) void gemv_i8_kernel(const int8_t* __restrict__ Xq, const float* __restrict__ xs,
-                                                      const int8_t* __restrict__ Wq, const float* __restrict__ ws,
-                                                      int ws_stride, const float* __restrict__ bias, int M, int N,
-                                                      int K, void* __restrict__ Yv, int32_t* __restrict__ acc_out) {
-    constexpr int U = 8;
+constexpr int kWaves = 8;
+
+// Row groups per tile and persistent blocks per CU, measured on 70B-class decode shapes: for M <= 4
+// with the activations held in registers (A) or reloaded per k chunk (AC), for M <= 8 (B) and
+// for M <= 16 (C).
+#ifndef SQ_GV_A_RG
+#define SQ_GV_A_RG 1
+#endif
+#ifndef SQ_GV_A_PCU
+#define SQ_GV_A_PCU 3
+#endif
+#ifndef SQ_GV_AC_RG
+#define SQ_GV_AC_RG 2
+#endif
+#ifndef SQ_GV_AC_PCU
+#define SQ_GV_AC_PCU 2
+#endif
+#ifndef SQ_GV_B_RG
+#define SQ_GV_B_RG 2
+#endif
+#ifndef SQ_GV_B_PCU
+#define SQ_GV_B_PCU 1
+#endif
+#ifndef SQ_GV_C_PCU
+#define SQ_GV_C_PCU 1
+#endif
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int RPI, int TG, int RG, int PER, bool HOIST, bool OUT_F16>
+__global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
+    const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
+    void* __restrict__ Yv, int32_t* __restrict__ acc_out) {
+    constexpr int SPAN = 1024 / RPI;      // bytes of one row per load instruction
+    constexpr int TROWS = RG * RPI;       // weight rows per tile
+    constexpr int NB = 16 / RPI;          // diagonal blocks of one MFMA output
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
-    const bool nval = n0 + r < N, mval = r < M;
-    const int8_t* wrow = Wq + (int64_t)(nval ? n0 + r : 0) * K;
-    const int8_t* xrow = Xq + (int64_t)(mval ? r : 0) * K;
-    const int nkb = (K + 63) / 64;
+    const int lrow = lane % RPI, lchunk = lane / RPI;
 
-    v4i acc = {0, 0, 0, 0};
-    for (int kb0 = wave; kb0 < nkb; kb0 += 4 * U) {
-        v4i wv[U], xv[U];
+    // This wave's k steps (SPAN bytes each): [s_begin, s_end), in chunks of PER.
+    const int S = (K + SPAN - 1) / SPAN;
+    const int per = (S + kWaves - 1) / kWaves;
+    const int s_begin = wave * per;
+    const int s_end = min(S, s_begin + per);
+    const int nch = HOIST ? 1 : (per + PER - 1) / PER;
+    const int ntiles = (N + TROWS - 1) / TROWS;
+    const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+    const int nunits = my_tiles * nch;
+
+    // Loads go through buffer resources (record counts pass through readfirstlane so that the
+    // descriptors stay in scalar registers): an offset outside the resource's record range reads as zero
+    // without touching memory.  So every unit issues a fixed number of loads (the compiler's wait counts
+    // stay exact while the next unit is in flight), steps past this wave's slice or past K cost nothing,
+    // and the rows past N in the last tile read as zeros (their outputs are not stored).
+    constexpr uint32_t kOut = 0x80000000u;   // beyond every record count used here (< 2^31)
+    auto kpos = [&](int ch, int s) -> int {  // this lane's byte column at step s of chunk ch, or -1
+        const int step = s_begin + ch * PER + s;
+        const int k = step * SPAN + 16 * lchunk;
+        return (step < s_end && k < K) ? k : -1;
+    };
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(Xq), (short)0, __builtin_amdgcn_readfirstlane(M * K), 0x00020000);
+    struct Buf {
+        v4i w[RG][PER];
+        v4i x[PER][TG];
+        float wsv, bv;
+    };
+    auto load_x = [&](int ch, v4i (&x)[PER][TG]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kb = kb0 + 4 * u;
-            const int k = kb * 64 + g * 16;
-            const bool kval = kb < nkb && k < K;
-            wv[u] = (kval && nval) ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + k))
-                                   : v4i{0, 0, 0, 0};
-            xv[u] = (kval && mval) ? *reinterpret_cast<const v4i*>(xrow + k) : v4i{0, 0, 0, 0};
+        for (int s = 0; s < PER; ++s) {
+            const int k = kpos(ch, s);
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) {
+                const int m = tg * RPI + lrow;
+                const uint32_t off = (k >= 0 && m < M) ? (uint32_t)(m * K + k) : kOut;
+                x[s][tg] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            }
         }
+    };
+    // Epilogue role of this thread: output (token em, tile row ej) when active.
+    const bool eact = (int)threadIdx.x < M * TROWS;
+    const int em = eact ? (int)threadIdx.x / TROWS : 0, ej = (int)threadIdx.x % TROWS;
+    const float xsv = xs[em];
+    const float* bsrc = bias != nullptr ? bias : ws;
+    auto load_unit = [&](int unit, Buf& b) {
+        const int tile = blockIdx.x + (unit / nch) * gridDim.x;
+        const int ch = unit % nch;
+        if (!HOIST) load_x(ch, b.x);
+        const int rows = max(0, min(TROWS, N - tile * TROWS));   // 0 past the last tile
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int8_t*>(Wq + (int64_t)tile * TROWS * K), (short)0,
+            __builtin_amdgcn_readfirstlane(rows * K), 0x00020000);
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv[u], wv[u], acc, 0, 0, 0);
-    }
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int s = 0; s < PER; ++s) {
+                const int k = kpos(ch, s);
+                const uint32_t off = k >= 0 ? (uint32_t)((rg * RPI + lrow) * K + k) : kOut;
+                b.w[rg][s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2));
+            }
+        const int n = min(tile * TROWS + ej, N - 1);
+        b.wsv = ws[(int64_t)n * ws_stride];
+        b.bv = bsrc[bias != nullptr ? n : 0];
+    };
 
-    __shared__ v4i part[4][64];
-    part[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    const v4i tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-    const int n = n0 + r;
-    if (n >= N) return;
-    const float wsv = ws[(int64_t)n * ws_stride];
-    const float bv = bias != nullptr ? bias[n] : 0.0f;
+    __shared__ v4i part[2][kWaves][RG][TG][64];
+    v4i acc[RG][TG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m >= M) continue;
-        float y = (float)tot[i];
-        y = y * xs[m];
-        y = y * wsv;
-        if (bias != nullptr) y = y + bv;
-        if constexpr (OUT_F16) reinterpret_cast<_Float16*>(Yv)[(int64_t)m * N + n] = (_Float16)y;
-        else reinterpret_cast<float*>(Yv)[(int64_t)m * N + n] = y;
-        if (acc_out != nullptr) acc_out[(int64_t)m * N + n] = tot[i];
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) acc[rg][tg] = v4i{0, 0, 0, 0};
+
+    // One unit: MFMAs over a chunk, then (last chunk of a tile) the cross-wave sum and epilogue.
+    auto run_unit = [&](int unit, const Buf& b, const v4i (&x)[PER][TG]) {
+#pragma unroll
+        for (int s = 0; s < PER; ++s)
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int tg = 0; tg < TG; ++tg)
+                    acc[rg][tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[s][tg], b.w[rg][s], acc[rg][tg], 0, 0, 0);
+        const int ti = unit / nch;
+        if (unit % nch != nch - 1) return;
+        const int par = ti & 1;
+        // MFMA output lane l, register r = D[4 * (l / 16) + r][l % 16]; stored as [c][t] (16 B per lane).
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) {
+                part[par][wave][rg][tg][(lane & 15) * 4 + (lane >> 4)] = acc[rg][tg];
+                acc[rg][tg] = v4i{0, 0, 0, 0};
+            }
+        // The other parity's buffer is only rewritten after every wave has passed the next barrier,
+        // i.e. after every reader of this tile's buffer has finished with it.
+        lds_barrier();
+        const int n = (blockIdx.x + ti * gridDim.x) * TROWS + ej;
+        if (eact && n < N) {
+            const int rg = ej / RPI, jj = ej % RPI, tg = em / RPI, mm = em % RPI;
+            const int* pb = reinterpret_cast<const int*>(&part[par][0][rg][tg][0]);
+            int sum = 0;
+#pragma unroll
+            for (int w8 = 0; w8 < kWaves; ++w8)
+#pragma unroll
+                for (int bk = 0; bk < NB; ++bk) sum += pb[w8 * (RG * TG * 256) + (bk * RPI + jj) * 16 + bk * RPI + mm];
+            float y = (float)sum;
+            y = y * xsv;
+            y = y * b.wsv;
+            if (bias != nullptr) y = y + b.bv;
+            if constexpr (OUT_F16) reinterpret_cast<_Float16*>(Yv)[(int64_t)em * N + n] = (_Float16)y;
+            else reinterpret_cast<float*>(Yv)[(int64_t)em * N + n] = y;
+            if (acc_out != nullptr) acc_out[(int64_t)em * N + n] = sum;
+        }
+    };
+
+    Buf ba, bb;
+    if (HOIST) load_x(0, ba.x);
+    if (nunits > 0) load_unit(0, ba);
+    // Drain the prologue loads so that the waits inside the loop count only the loads in flight there.
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    // Ping-pong between two buffers.  The next unit is always loaded, also past the end (every load of
+    // a tile past the last one is out of range and touches no memory), so both halves are straight-line
+    // code and each MFMA waits only for its own operands.
+    int u = 0;
+    while (u < nunits) {
+        load_unit(u + 1, bb);
+        run_unit(u, ba, ba.x);
+        if (++u >= nunits) break;
+        load_unit(u + 1, ba);
+        run_unit(u, bb, HOIST ? ba.x : bb.x);
+        ++u;
     }
+}
+
+template <int RPI, int TG, int RG, int PER, bool HOIST>
+hipError_t launch_cfg(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
+                      const float* bias, int M, int N, int K, void* Y, sq_dtype ydt, int32_t* acc_out, int grid,
+                      hipStream_t st) {
+    if (ydt == SQ_F16)
+        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true>), dim3(grid), dim3(64 * kWaves), 0, st,
+                           Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
+    else
+        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false>), dim3(grid), dim3(64 * kWaves), 0, st,
+                           Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -75,14 +234,41 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
     (void)side;
-    const unsigned blocks = (unsigned)((N + 15) / 16);
-    if (ydt == SQ_F16)
-        hipLaunchKernelGGL(gemv_i8_kernel<true>, dim3(blocks), dim3(256), 0, st, Xq, xs, Wq, ws, ws_stride, bias,
-                           (int)M, (int)N, (int)K, Y, acc_out);
-    else
-        hipLaunchKernelGGL(gemv_i8_kernel<false>, dim3(blocks), dim3(256), 0, st, Xq, xs, Wq, ws, ws_stride, bias,
-                           (int)M, (int)N, (int)K, Y, acc_out);
-    return hipGetLastError();
+    const int cus = dev_info().cus;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    // Steps per wave for a load span of `span` bytes; the register-resident chunk is the next power of two.
+    auto per_of = [&](int span) { return ((k + span - 1) / span + kWaves - 1) / kWaves; };
+    auto grid_of = [&](int trows, int per_cu) {
+        const int64_t tiles = (N + trows - 1) / trows;
+        return (int)(tiles < (int64_t)per_cu * cus ? tiles : (int64_t)per_cu * cus);
+    };
+#define SQ_GEMV(RPI, TG, RG, PER, HOIST, PER_CU) \
+    launch_cfg<RPI, TG, RG, PER, HOIST>(Xq, xs, Wq, ws, ws_stride, bias, m, n, k, Y, ydt, acc_out, \
+                                        grid_of(RG * RPI, PER_CU), st)
+    if (M <= 4) {
+        // 4 rows x 256 bytes per load, one token group.
+        const int per = per_of(256);
+        if (per <= 1) return SQ_GEMV(4, 1, SQ_GV_A_RG, 1, true, SQ_GV_A_PCU);
+        if (per <= 2) return SQ_GEMV(4, 1, SQ_GV_A_RG, 2, true, SQ_GV_A_PCU);
+        if (per <= 4) return SQ_GEMV(4, 1, SQ_GV_A_RG, 4, true, SQ_GV_A_PCU);
+        if (per <= 8) return SQ_GEMV(4, 1, SQ_GV_A_RG, 8, true, SQ_GV_A_PCU);
+        return SQ_GEMV(4, 1, SQ_GV_AC_RG, 8, false, SQ_GV_AC_PCU);
+    }
+    if (M <= 8) {
+        // 8 rows x 128 bytes per load, one token group of 8.
+        const int per = per_of(128);
+        if (per <= 2) return SQ_GEMV(8, 1, SQ_GV_B_RG, 2, true, SQ_GV_B_PCU);
+        if (per <= 4) return SQ_GEMV(8, 1, SQ_GV_B_RG, 4, true, SQ_GV_B_PCU);
+        if (per <= 8) return SQ_GEMV(8, 1, SQ_GV_B_RG, 8, true, SQ_GV_B_PCU);
+        return SQ_GEMV(8, 1, SQ_GV_B_RG, 8, false, SQ_GV_B_PCU);
+    }
+    // 8 rows x 128 bytes per load, two token groups.
+    const int per = per_of(128);
+    if (per <= 2) return SQ_GEMV(8, 2, 2, 2, true, SQ_GV_C_PCU);
+    if (per <= 4) return SQ_GEMV(8, 2, 2, 4, true, SQ_GV_C_PCU);
+    if (per <= 8) return SQ_GEMV(8, 2, 2, 8, true, SQ_GV_C_PCU);
+    return SQ_GEMV(8, 2, 2, 4, false, SQ_GV_C_PCU);
+#undef SQ_GEMV
 }
 
 }  // namespace sq
