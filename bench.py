@@ -78,11 +78,14 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
 
-def time_steps(torch, step, steps, warmup):
+def time_steps(torch, step, steps, warmup, kernel_events=True):
+    """ms per step over `steps` steps after `warmup`, and the mean duration of
+    the launches the step brackets with its timer (None when kernel_events is
+    False: then no per-kernel events sit in the timed region)."""
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    timer = Timer(torch) if kernel_events else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -90,7 +93,7 @@ def time_steps(torch, step, steps, warmup):
         step(timer)
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, timer.mean_ms()
+    return t0.elapsed_time(t1) / steps, (timer.mean_ms() if timer else None)
 
 
 def prepare_weight(torch, sq, d, X_cal, W, alpha, gran):
@@ -158,12 +161,17 @@ def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
             g = lambda: sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
             timer.around(g) if timer else g()
 
-        ms, gemv_ms = time_steps(torch, step, steps, warmup)
+        # the step alone (no per-kernel events in the timed region), then the GEMV launches on their own
+        ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
+        _, gemv_ms = time_steps(torch, step, steps, 2)
         nbytes = N * K + 4 * N + 2 * M * K + 2 * M * K + 4 * M + 2 * M * N
+        gemv_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
         out[f"M{M}"] = dict(ms_per_step=ms, GBps=nbytes / (ms * 1e-3) / 1e9,
                             hbm_frac=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             gemv_us=gemv_ms * 1e3,
-                            gemv_GBps=(N * K + 4 * N + M * K + 2 * M * N) / (gemv_ms * 1e-3) / 1e9)
+                            gemv_GBps=gemv_bytes / (gemv_ms * 1e-3) / 1e9,
+                            gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    out["gemv_traffic_bytes_per_launch"] = traffic_for("gemv_decode_70b", GEMV_SRC)
     return out
 
 

@@ -3,12 +3,18 @@
 // accumulation then acc * x_scale * w_scale; "SmoothQuant量化实战", section 3.4].
 //
 // Layout: Xq [M x K] and Wq [N x K] row-major int8, both K-contiguous ("NT"),
-// Y [M x N].  A 256-thread block (4 waves in a 2 x 2 grid) computes a BM x BN
-// tile with v_mfma_i32_32x32x32_i8; K is walked in BK = 128-byte tiles staged in
-// LDS, double buffered (global -> registers for tile k+1 while tile k feeds the
-// MFMAs).  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at slot
-// c ^ (r & 7), so the fragment reads (lane -> row lane%32, chunk lane/32) of a
-// wave hit distinct banks.
+// Y [M x N].  A block of 8 waves (WM x WN grid, two waves per SIMD) computes a
+// BM x BN tile with v_mfma_i32_32x32x32_i8.  K is walked in BK = 128-byte
+// tiles (one cache line per row) held in two LDS stages: while the MFMAs read
+// stage j, global_load_lds (LDS DMA, 1 KB = 8 rows x 128 B per wave
+// instruction) fills stage j+1 straight from global memory, with no register
+// staging.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at slot
+// c ^ ((r >> SWZ) & 7), so the fragment reads (lane -> row lane%32, chunk
+// lane/32) of a wave hit distinct banks.  A K that is not a multiple of 128
+// starts with one partial tile staged through registers with zero fill.
+// Blocks are dealt to the 8 XCDs round-robin; the tile order gives each XCD a
+// contiguous range of tiles, grouped 8 tile-rows deep, so that concurrently
+// running tiles share operand panels in that XCD's L2.
 //
 // MFMA operand use: lane l supplies 16 k-consecutive bytes of a weight row
 // (l % 32) as the instruction's A operand and of an activation row (l % 32) as
@@ -17,6 +23,11 @@
 // and the dot product is exact.  Result lane l, register r holds
 // D[8*(r/4) + 4*(l/32) + r%4][l % 32] = (output column, output row), so each
 // lane owns runs of four consecutive output columns.
+//
+// Epilogue: the accumulators are dequantized per (row, column) in the order
+// int32 -> fp32, * x_scale[row], * w_scale[col], + bias[col], converted to the
+// output type and written to LDS, then copied out with 16-byte row-contiguous
+// stores.
 //
 // LLM.int8() ["LLM.int8()技术解析", section 3.1]: when a side product is
 // requested, the dequantized tile becomes the C input of
