@@ -6,7 +6,7 @@
 // Y [M x N].  A block of 8 waves (WM x WN grid, two waves per SIMD) computes a
 // BM x BN tile with v_mfma_i32_32x32x32_i8.  K is walked in BK = 128-byte
 // tiles (one cache line per row) held in two LDS stages: while the MFMAs read
-// stage j, global_load_lds (LDS DMA, 1 KB = 8 rows x 128 B per wave
+// stage j, buffer_load ... lds (LDS DMA, 1 KB = 8 rows x 128 B per wave
 // instruction) fills stage j+1 straight from global memory, with no register
 // staging.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at slot
 // c ^ ((r >> SWZ) & 7), so the fragment reads (lane -> row lane%32, chunk
@@ -77,6 +77,13 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// 16 bytes per lane from a buffer resource straight into LDS: the wave's
+// 1 KB lands at ldsp (held in M0), lane l at ldsp + 16 l.  Offsets outside the
+// resource's record range read as zeros.
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int8_t* ldsp, uint32_t voff, int k0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)ldsp, 16, voff, k0, 0, 0);
+}
+
 template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     __shared__ __attribute__((aligned(1024))) int8_t lds[S * STAGE];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave index is uniform
     const int wm = wave / WN, wn = wave % WN;
 
     // Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
@@ -125,8 +132,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 
     // DMA addressing: wave w fills 1 KB blocks w, w+NW, ...; lane l writes row
     // (block*8 + l/8), slot l%8, so it fetches logical chunk (l%8) ^ swz(row).
-    // Rows past M (N) are clamped: they only feed outputs that are never stored.
-    const int8_t* src[L];
+    // The loads go through buffer resources over the tile's A and B rows: each
+    // lane's byte offset inside them is fixed, the K position travels in the
+    // scalar offset (no per-tile vector address arithmetic in the MFMA waves),
+    // and rows past M (N) are outside the record range and read as zeros (they
+    // only feed outputs that are never stored).
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(A + (int64_t)m0 * K), (short)0,
+        __builtin_amdgcn_readfirstlane((M - m0 < BM ? M - m0 : BM) * K), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(B + (int64_t)n0 * K), (short)0,
+        __builtin_amdgcn_readfirstlane((N - n0 < BN ? N - n0 : BN) * K), 0x00020000);
+    uint32_t voff[L];
     int ldsoff[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -134,17 +151,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         const bool isA = blk < BM / 8;
         const int row = (isA ? blk : blk - BM / 8) * 8 + (lane >> 3);
         const int kc = (lane & 7) ^ swz(row);
-        int g = (isA ? m0 : n0) + row;
-        const int lim = isA ? M : N;
-        g = g < lim ? g : lim - 1;
-        src[i] = (isA ? A : B) + (int64_t)g * K + kc * 16;
+        voff[i] = (uint32_t)(row * K + kc * 16);
         ldsoff[i] = blk * 1024;
     }
     auto dma = [&](int stage, int k0) {
 #pragma unroll
         for (int i = 0; i < L; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), (void*)(lds + stage * STAGE + ldsoff[i]), 16,
-                                             0, 0);
+            dma_to_lds(wave + NW * i < BM / 8 ? rA : rB, lds + stage * STAGE + ldsoff[i], voff[i], k0);
     };
     // Partial K tile (K % 128 != 0): through registers with zero fill.
     auto tail_tile = [&](int stage, int k0) {
@@ -383,7 +396,8 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
         if (side) return run<BM, BN, WM, WN, true, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
         return run<BM, BN, WM, WN, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
     }
-    if (side) return run<BM, BN, WM, WN, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+    // The LLM.int8() side product comes with fp16 output only (int8_outlier_matmul writes fp16).
+    if (side) return hipErrorInvalidValue;
     return run<BM, BN, WM, WN, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
 }
 
