@@ -170,6 +170,9 @@ def gpu_gemm(sq, Xq, xs, Wq, ws, gran, bias, out_dt):
 GEMM_CASES = [
     # M, N, K   (M <= 16: decode kernel; else tile kernel)
     (1, 1, 16), (1, 1000, 8192), (4, 1000, 144), (7, 33, 4096), (16, 4100, 8192),
+    # decode kernel with the activation slice reloaded per k chunk (K beyond what a wave keeps in
+    # registers), ragged N and K
+    (2, 301, 20496), (8, 130, 12304), (16, 257, 12288), (3, 4100, 16400),
     (17, 32, 16), (33, 70, 144), (200, 300, 1040), (256, 256, 256), (300, 520, 4112),
 ]
 
