@@ -96,6 +96,15 @@ template <> struct CodeStore<4> {
 // division for x / s_j (only possible for fp32 inputs or s_j > 2^100); for
 // x' / xs such a quotient is below 0.5 and its code is 0 either way.
 // ---------------------------------------------------------------------------
+// Barrier for LDS traffic only: __syncthreads() would also wait for every
+// outstanding global load, i.e. drain the row prefetch.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <typename T, int VEC, int CH, int MODE, bool OUTL>
 __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X, int64_t M, int64_t K,
                                                         const float* __restrict__ s, int8_t* __restrict__ Xq,
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
 
         amax = wave_max(amax);
         if (lane == 0) red[it & 1][wave] = amax;
-        __syncthreads();
+        lds_barrier();
         float a = red[it & 1][w0];
         for (int w = 1; w < nw; ++w) a = __builtin_fmaxf(a, red[it & 1][w0 + w]);
         const float xs = a / 127.0f;
@@ -293,7 +302,10 @@ template <typename T, int MODE, bool OUTL>
 static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
                                const int32_t* pos, _Float16* Xo, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        if (K <= 1024) return launch_fast<T, 8, 1, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+        // one 16-byte chunk per thread (one row per block) when there are few rows: the per-block
+        // setup is then split over the most threads
+        if (K <= 1024 || (K <= 8192 && M <= dev_info().cus))
+            return launch_fast<T, 8, 1, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
         if (K <= 16384) return launch_fast<T, 8, 2, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
         if (K <= 20480) return launch_fast<T, 4, 5, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
     } else {
