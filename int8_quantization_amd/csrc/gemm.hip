@@ -105,6 +105,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     __shared__ __attribute__((aligned(1024))) int8_t lds[S * STAGE];
 
     const int tid = threadIdx.x;
+    const int side_cnt = SIDE ? *cnt : 0;   // LLM.int8() outlier columns (count on the device)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave index is uniform
     const int wm = wave / WN, wn = wave % WN;
 
@@ -271,7 +272,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         sws[c] = ws[(int64_t)n * ws_stride];
         sbias[c] = bias != nullptr ? bias[n] : 0.0f;
     }
-    const int side_cnt = SIDE ? *cnt : 0;
+    // LLM.int8() side operands of this wave's rows and columns for the first 16 outlier columns,
+    // loaded in one batch so their latencies overlap (more than 16 columns load per chunk below).
+    auto side_frag = [&](const _Float16* p, bool ok, int tk) {
+        h8 v{};
+        if (ok) {
+            if (tk + 8 <= side_cnt) v = *reinterpret_cast<const h8*>(p + tk);
+            else
+                for (int e = 0; e < 8; ++e) v[e] = tk + e < side_cnt ? p[tk + e] : (_Float16)0.0f;
+        }
+        return v;
+    };
+    h8 xpre[SIDE ? TM : 1], wpre[SIDE ? TN : 1];
+    if constexpr (SIDE) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int arow = m0 + wm * WTM + i * 32 + lrow;
+            xpre[i] = side_frag(Xo + (int64_t)(arow < M ? arow : 0) * ldo, arow < M && side_cnt > 0, 8 * lk);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int bcol = n0 + wn * WTN + j * 32 + lrow;
+            wpre[j] = side_frag(Wo + (int64_t)(bcol < N ? bcol : 0) * ldo, bcol < N && side_cnt > 0, 8 * lk);
+        }
+    }
     wait_all_loads();
     block_barrier();
 
@@ -315,21 +339,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                     // fp16 side product over the gathered outlier columns, same operand roles
                     const int arow = m0 + mloc;
                     const int bcol = n0 + wn * WTN + j * 32 + lrow;
-                    for (int t0 = 0; t0 < side_cnt; t0 += 16) {
+                    if (side_cnt > 0) y = __builtin_amdgcn_mfma_f32_32x32x16_f16(wpre[j], xpre[i], y, 0, 0, 0);
+                    for (int t0 = 16; t0 < side_cnt; t0 += 16) {
                         const int tk = t0 + 8 * lk;   // this lane's 8 k-slots
-                        h8 xa{}, wb{};
-                        if (arow < M) {
-                            const _Float16* p = Xo + (int64_t)arow * ldo + tk;
-                            if (tk + 8 <= side_cnt) xa = *reinterpret_cast<const h8*>(p);
-                            else
-                                for (int e = 0; e < 8; ++e) xa[e] = tk + e < side_cnt ? p[e] : (_Float16)0.0f;
-                        }
-                        if (bcol < N) {
-                            const _Float16* p = Wo + (int64_t)bcol * ldo + tk;
-                            if (tk + 8 <= side_cnt) wb = *reinterpret_cast<const h8*>(p);
-                            else
-                                for (int e = 0; e < 8; ++e) wb[e] = tk + e < side_cnt ? p[e] : (_Float16)0.0f;
-                        }
+                        const h8 xa = side_frag(Xo + (int64_t)(arow < M ? arow : 0) * ldo, arow < M, tk);
+                        const h8 wb = side_frag(Wo + (int64_t)(bcol < N ? bcol : 0) * ldo, bcol < N, tk);
                         y = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb, xa, y, 0, 0, 0);
                     }
                 }
