@@ -142,7 +142,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
     // per-column constants, computed while the first rows are in flight
     double rs[MODE == 1 ? CH : 1][VEC];
     float sv[MODE == 2 ? CH : 1][VEC];
-    int pv[OUTL ? CH : 1][VEC];
+    unsigned omask[OUTL ? CH : 1];            // bit e: element e of the chunk is an outlier column
     bool guard = false;                       // some x/s_j may fall below the normal range
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -156,7 +156,10 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
                 guard = guard || !(sj < 0x1p100f);
             }
             if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
-            if constexpr (OUTL) pv[i][e] = valid[i] ? pos[cc * VEC + e] : -1;
+            if constexpr (OUTL) {
+                if (e == 0) omask[i] = 0;
+                if (valid[i] && pos[cc * VEC + e] >= 0) omask[i] |= 1u << e;
+            }
         }
     }
     if constexpr (sizeof(T) == 4) guard = true;   // fp32 inputs can be subnormal
@@ -186,8 +189,8 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
                     xv[i][e] = x;
                     bool skip = false;
                     if constexpr (OUTL) {
-                        skip = pv[i][e] >= 0;
-                        if (skip && live) Xo[m * K + pv[i][e]] = (_Float16)rc[i][e];
+                        skip = (omask[i] >> e) & 1u;
+                        if (skip && live) Xo[m * K + pos[c * VEC + e]] = (_Float16)rc[i][e];
                     }
                     if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
                 }
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     bool zero = xs == 0.0f;
-                    if constexpr (OUTL) zero = zero || pv[i][e] >= 0;
+                    if constexpr (OUTL) zero = zero || ((omask[i] >> e) & 1u);
                     q[e] = zero ? 0 : code_of((float)((double)xv[i][e] * rx));
                 }
                 CodeStore<VEC>::store(Xq + m * K + c * VEC, q);
