@@ -67,6 +67,8 @@ QUANT_CASES = [
     (1000, 512, np.float32, True),      # many rows per block
     (4, 16384, np.float32, True),       # fp32 beyond the register-resident path
     (9, 8192, np.float32, False),
+    (2, 131056, np.float16, True),      # the largest K the library accepts
+    (1, 131056, np.float32, False),
 ]
 
 
@@ -174,6 +176,9 @@ GEMM_CASES = [
     # registers), ragged N and K
     (2, 301, 20496), (8, 130, 12304), (16, 257, 12288), (3, 4100, 16400),
     (17, 32, 16), (33, 70, 144), (200, 300, 1040), (256, 256, 256), (300, 520, 4112),
+    # the largest K the library accepts: (-128)*(-128)*K = 2147221504 still fits int32; the tile
+    # kernel also gets a partial last K tile (131056 % 128 = 112)
+    (1, 70, 131056), (20, 40, 131056),
 ]
 
 
