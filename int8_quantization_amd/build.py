@@ -39,6 +39,15 @@ def _compile(src: str) -> str:
     return obj
 
 
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one source, with the library's flags (for ISA checks)."""
+    cmd = [HIPCC, *FLAGS, "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    return r.stdout
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 4)))

@@ -12,9 +12,16 @@
 // c ^ ((r >> SWZ) & 7), so the fragment reads (lane -> row lane%32, chunk
 // lane/32) of a wave hit distinct banks.  A K that is not a multiple of 128
 // starts with one partial tile staged through registers with zero fill.
+// The DMA is issued from inline asm: the compiler models the builtin form as an
+// LDS store of unknown address and then waits for it before every later LDS
+// read, which would serialize the prefetch with the fragment reads; here the
+// pipeline's own waits and barriers order it.
 // Blocks are dealt to the 8 XCDs round-robin; the tile order gives each XCD a
 // contiguous range of tiles, grouped 8 tile-rows deep, so that concurrently
 // running tiles share operand panels in that XCD's L2.
+// A tile count that would leave a partial last round of large tiles is split by
+// output columns: the full rounds cover the leading tile columns and the rest
+// goes out as a second launch with its own (smaller) tiles.
 //
 // MFMA operand use: lane l supplies 16 k-consecutive bytes of a weight row
 // (l % 32) as the instruction's A operand and of an activation row (l % 32) as
@@ -33,6 +40,7 @@
 // requested, the dequantized tile becomes the C input of
 // v_mfma_f32_32x32x16_f16 over the gathered fp16 outlier columns, so the fp16
 // result adds onto the int8 result inside the same kernel.
+#include <algorithm>
 #include <type_traits>
 
 #include "sq_internal.h"
@@ -77,11 +85,22 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from a buffer resource straight into LDS: the wave's
-// 1 KB lands at ldsp (held in M0), lane l at ldsp + 16 l.  Offsets outside the
-// resource's record range read as zeros.
-__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int8_t* ldsp, uint32_t voff, int k0) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)ldsp, 16, voff, k0, 0, 0);
+// 16 bytes per lane from a buffer resource straight into LDS: the wave's 1 KB
+// lands at LDS byte address lds_addr (through M0), lane l at lds_addr + 16 l.
+// Offsets outside the resource's record range read as zeros.  The resource is
+// the four descriptor words in scalar registers.  M0 is written here only: the
+// kernels that use this helper leave M0 to it (a CPU test checks their ISA).
+__device__ __forceinline__ void dma_to_lds(const v4i& rsrc, uint32_t lds_addr, uint32_t voff, int k0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds_addr), "v"(voff), "s"(rsrc), "s"(k0)
+                 : "memory");
+}
+
+// Buffer resource over [p, p + nrec) bytes, raw (unformatted) 32-bit records.
+__device__ __forceinline__ v4i buffer_desc(const int8_t* p, int nrec) {
+    const uint64_t a = (uint64_t)p;
+    return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(a >> 32)),
+               __builtin_amdgcn_readfirstlane(nrec), 0x00020000};
 }
 
 template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
@@ -89,7 +108,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
     void* __restrict__ Yv, int32_t* __restrict__ acc_out, const _Float16* __restrict__ Xo,
-    const _Float16* __restrict__ Wo, const int32_t* __restrict__ cnt, int64_t ldo, int tiles_m, int tiles_n) {
+    const _Float16* __restrict__ Wo, const int32_t* __restrict__ cnt, int64_t ldo, int64_t ldy, int tiles_m,
+    int tiles_n) {
     constexpr int BK = 128;                  // bytes of K per stage: one cache line per row
     constexpr int S = 2;                     // LDS stages
     constexpr int KS = BK / 32;              // MFMA k-steps per stage
@@ -138,12 +158,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // scalar offset (no per-tile vector address arithmetic in the MFMA waves),
     // and rows past M (N) are outside the record range and read as zeros (they
     // only feed outputs that are never stored).
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(A + (int64_t)m0 * K), (short)0,
-        __builtin_amdgcn_readfirstlane((M - m0 < BM ? M - m0 : BM) * K), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(B + (int64_t)n0 * K), (short)0,
-        __builtin_amdgcn_readfirstlane((N - n0 < BN ? N - n0 : BN) * K), 0x00020000);
+    const v4i rA = buffer_desc(A + (int64_t)m0 * K, (M - m0 < BM ? M - m0 : BM) * K);
+    const v4i rB = buffer_desc(B + (int64_t)n0 * K, (N - n0 < BN ? N - n0 : BN) * K);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
     uint32_t voff[L];
     int ldsoff[L];
 #pragma unroll
@@ -158,7 +175,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     auto dma = [&](int stage, int k0) {
 #pragma unroll
         for (int i = 0; i < L; ++i)
-            dma_to_lds(wave + NW * i < BM / 8 ? rA : rB, lds + stage * STAGE + ldsoff[i], voff[i], k0);
+            dma_to_lds(wave + NW * i < BM / 8 ? rA : rB,
+                       __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE + ldsoff[i]), voff[i], k0);
     };
     // Partial K tile (K % 128 != 0): through registers with zero fill.
     auto tail_tile = [&](int stage, int k0) {
@@ -215,29 +233,60 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     auto kofs = [&](int j) { return (has_tail ? (j == 0 ? nfull : j - 1) : j) * BK; };
     if (has_tail) tail_tile(0, kofs(0));
     else dma(0, kofs(0));
+    // Dequantization scales of the tile's rows and columns, loaded while the first
+    // K tile is in flight (the prologue barrier publishes them).
+    __shared__ float sxs[BM], sws[BN], sbias[BN];
+    for (int r = tid; r < BM; r += NT) {
+        const int m = m0 + r;
+        sxs[r] = xs[m < M ? m : M - 1];
+    }
+    for (int c = tid; c < BN; c += NT) {
+        const int n = n0 + c < N ? n0 + c : N - 1;
+        sws[c] = ws[(int64_t)n * ws_stride];
+        sbias[c] = bias != nullptr ? bias[n] : 0.0f;
+    }
+    // The epilogue's kernel arguments go to registers now: scalar loads still in
+    // flight when the loop starts would make the compiler's fragment waits in it
+    // conservative (it cannot order them against the LDS reads).
+    asm volatile("" ::"s"(Yv), "s"(acc_out), "s"(ws_stride));
     wait_all_loads();
     block_barrier();
     fload(0, 0, 0);
 
-    for (int j = 0; j < nk; ++j) {
-        const int st = j & 1;
-        const bool more = j + 1 < nk;
-        // the other stage held tile j-1, which every wave finished reading
-        // before the previous barrier
-        if (more) dma(st ^ 1, kofs(j + 1));
+    // Scheduling fence between k-steps (fragment reads, then the MFMAs of the step
+    // before): measured faster for the 256-column tile, while the compiler's own
+    // interleaving is faster for the others.
+    auto fence = [] {
+        if constexpr (BN == 256) __builtin_amdgcn_sched_barrier(0);
+    };
+    auto steps = [&](int st) {   // k-steps 0 .. KS-2 of the tile in stage st
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             fload(st, ks + 1, (ks + 1) & 1);
+            fence();
             mfmas(ks & 1);
+            fence();
         }
-        if (more) {
-            // tile j+1 landed for every wave, and tile j's last fragments are in registers
-            wait_all_loads();
-            block_barrier();
-            fload(st ^ 1, 0, 0);
-        }
+    };
+    // Every tile but the last prefetches its successor and ends in the barrier;
+    // the last runs after the loop, so the loop body has a single shape.
+    for (int j = 0; j + 1 < nk; ++j) {
+        const int st = j & 1;
+        // the other stage held tile j-1, which every wave finished reading before
+        // the previous barrier
+        dma(st ^ 1, kofs(j + 1));
+        fence();
+        steps(st);
+        // tile j+1 landed for every wave, and tile j's last fragments are in registers
+        wait_all_loads();
+        block_barrier();
+        fload(st ^ 1, 0, 0);
+        fence();
         mfmas((KS - 1) & 1);
+        fence();
     }
+    steps((nk - 1) & 1);
+    mfmas((KS - 1) & 1);
 
     // ---- epilogue, staged through LDS.
     // With the weight fragment as the instruction's A operand, lane l, register
@@ -256,22 +305,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     constexpr int CH16 = RB / 16;                        // 16-byte chunks per row
     static_assert(HROWS * RB <= S * STAGE, "epilogue tile must fit the LDS ring");
     constexpr int SWM = CH16 % 16 == 0 ? 15 : (CH16 % 8 == 0 ? 7 : (CH16 % 4 == 0 ? 3 : 0));   // XOR mask
-    __shared__ float sxs[BM], sws[BN], sbias[BN];
     auto lofs = [&](int r, int cbyte) {                  // LDS byte offset of (row, byte in row)
         return r * RB + ((((cbyte >> 4) ^ (r & SWM))) << 4) + (cbyte & 15);
     };
 
     wait_all_loads();
     block_barrier();                                      // ring no longer read
-    for (int r = tid; r < BM; r += NT) {
-        const int m = m0 + r;
-        sxs[r] = xs[m < M ? m : M - 1];
-    }
-    for (int c = tid; c < BN; c += NT) {
-        const int n = n0 + c < N ? n0 + c : N - 1;
-        sws[c] = ws[(int64_t)n * ws_stride];
-        sbias[c] = bias != nullptr ? bias[n] : 0.0f;
-    }
     // LLM.int8() side operands of this wave's rows and columns for the first 16 outlier columns,
     // loaded in one batch so their latencies overlap (more than 16 columns load per chunk below).
     auto side_frag = [&](const _Float16* p, bool ok, int tk) {
@@ -296,8 +335,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             wpre[j] = side_frag(Wo + (int64_t)(bcol < N ? bcol : 0) * ldo, bcol < N && side_cnt > 0, 8 * lk);
         }
     }
-    wait_all_loads();
-    block_barrier();
+    if constexpr (SIDE) wait_all_loads();
 
     for (int h = 0; h < HALVES; ++h) {
         // write phase
@@ -332,7 +370,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                         const int n = n0 + nloc;
                         if (m < M)
                             for (int b = 0; b < 4; ++b)
-                                if (n + b < N) acc_out[(int64_t)m * N + n + b] = iv[b];
+                                if (n + b < N) acc_out[(int64_t)m * ldy + n + b] = iv[b];
                     }
                 }
                 if constexpr (SIDE) {
@@ -362,7 +400,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         wait_lds();
         block_barrier();
         // copy phase: 16-byte chunks, consecutive threads along a row
-        const bool vec = (N * OB) % 16 == 0;
+        const bool vec = (ldy * OB) % 16 == 0;
         for (int q = tid; q < HROWS * CH16; q += NT) {
             const int lr = q / CH16, c = q % CH16;
             const int wmq = lr / (TMH * 32), rem = lr % (TMH * 32);
@@ -370,7 +408,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             if (m >= M) continue;
             const int n = n0 + c * (16 / OB);
             const v4i v = *reinterpret_cast<const v4i*>(lds + lofs(lr, c * 16));
-            char* dst = reinterpret_cast<char*>(Yv) + ((int64_t)m * N + n) * OB;
+            char* dst = reinterpret_cast<char*>(Yv) + ((int64_t)m * ldy + n) * OB;
             if (vec && n + 16 / OB <= N) {
                 *reinterpret_cast<v4i*>(dst) = v;
             } else {
@@ -389,8 +427,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 
 template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
 hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-               const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int32_t* acc_out, const SideArgs* side,
-               hipStream_t st) {
+               const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int32_t* acc_out,
+               const SideArgs* side, hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const _Float16* Xo = side ? side->Xo : nullptr;
     const _Float16* Wo = side ? side->Wo : nullptr;
@@ -398,21 +436,82 @@ hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float*
     const int64_t ldo = side ? side->ldo : 0;
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE>), dim3((unsigned)(tm * tn)),
                        dim3(64 * WM * WN), 0, st, Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out,
-                       Xo, Wo, cnt, ldo, tm, tn);
+                       Xo, Wo, cnt, ldo, ldy, tm, tn);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                    const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
-                    const SideArgs* side, hipStream_t st) {
+                    const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, sq_dtype ydt,
+                    int32_t* acc_out, const SideArgs* side, hipStream_t st) {
     if (ydt == SQ_F16) {
-        if (side) return run<BM, BN, WM, WN, true, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
-        return run<BM, BN, WM, WN, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+        if (side)
+            return run<BM, BN, WM, WN, true, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side,
+                                                   st);
+        return run<BM, BN, WM, WN, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side, st);
     }
     // The LLM.int8() side product comes with fp16 output only (int8_outlier_matmul writes fp16).
     if (side) return hipErrorInvalidValue;
-    return run<BM, BN, WM, WN, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, side, st);
+    return run<BM, BN, WM, WN, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side, st);
+}
+
+// Output columns [0, N) of a product whose output rows are ldy elements apart.
+// Tile shape: the least estimated time, rounds * (area per CU) / rate with
+// rounds = ceil(tiles / tile slots); a 256-row tile takes a whole CU, 128 x 128
+// tiles run two per CU at about three quarters of the per-CU rate (measured on
+// the 530B-slice shape).  When large tiles would leave a partial last round, the
+// full rounds take the leading tile columns and the remaining columns go out as
+// a second launch that picks its own tiles, if that is estimated faster.
+hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
+                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, sq_dtype ydt,
+                       int32_t* acc_out, const SideArgs* side, hipStream_t st, bool may_split) {
+    const int64_t cus = dev_info().cus;
+    struct Cand { int bm, bn, per_cu; double rate; };
+    constexpr Cand cands[] = {{256, 256, 1, 1.0}, {256, 192, 1, 1.0}, {128, 128, 2, 0.75}};
+    auto cost_of = [&](const Cand& c, int64_t n) {
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
+        const int64_t slots = cus * c.per_cu;
+        return (double)((tiles + slots - 1) / slots) * c.per_cu * c.bm * c.bn / c.rate;
+    };
+    int best = 0;
+    double best_cost = 1e300;
+    for (int c = 0; c < 3; ++c) {
+        const double cost = cost_of(cands[c], N);
+        if (cost < best_cost * 0.999) {
+            best_cost = cost;
+            best = c;
+        }
+    }
+    const Cand& b = cands[best];
+    const int64_t tm = (M + b.bm - 1) / b.bm, tn = (N + b.bn - 1) / b.bn;
+    const int64_t full = (tm * tn) / (cus * b.per_cu);            // full rounds
+    const int64_t tn_main = full * cus * b.per_cu / tm;            // tile columns they cover
+    if (may_split && full >= 1 && tn_main >= 1 && tn_main < tn) {
+        const int64_t n_main = tn_main * b.bn;
+        double tail_cost = 1e300;
+        for (const Cand& c : cands) tail_cost = std::min(tail_cost, cost_of(c, N - n_main));
+        if (full * b.per_cu * b.bm * b.bn / b.rate + tail_cost < 0.95 * best_cost) {
+            const hipError_t e =
+                launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, n_main, K, Y, ldy, ydt, acc_out, side, st, false);
+            if (e != hipSuccess) return e;
+            SideArgs side2{};
+            if (side) {
+                side2 = *side;
+                side2.Wo = side->Wo + n_main * side->ldo;     // outlier weight rows of the remaining columns
+            }
+            return launch_cols(Xq, xs, Wq + n_main * K, ws + n_main * ws_stride, ws_stride,
+                               bias ? bias + n_main : nullptr, M, N - n_main, K,
+                               static_cast<char*>(Y) + n_main * (ydt == SQ_F16 ? 2 : 4), ldy, ydt,
+                               acc_out ? acc_out + n_main : nullptr, side ? &side2 : nullptr, st, false);
+        }
+    }
+    if (best == 0)
+        return dispatch<256, 256, SQ_W256_WM, SQ_W256_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt,
+                                                          acc_out, side, st);
+    if (best == 1)
+        return dispatch<256, 192, SQ_W192_WM, SQ_W192_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt,
+                                                          acc_out, side, st);
+    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt, acc_out, side, st);
 }
 
 }  // namespace
@@ -420,31 +519,7 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
-    // Pick the tile shape with the least estimated time: a 256-row tile takes a
-    // whole CU, so time ~ ceil(tiles / CUs) * area; 128 x 128 tiles run two per
-    // CU at about half the per-CU rate (twice the operand traffic per MFMA).
-    const int64_t cus = dev_info().cus;
-    struct Cand { int bm, bn, per_cu; double rate; };
-    const Cand cands[] = {{256, 256, 1, 1.0}, {256, 192, 1, 1.0}, {128, 128, 2, 0.5}};
-    int best = 0;
-    double best_cost = 1e300;
-    for (int c = 0; c < 3; ++c) {
-        const int64_t tiles = ((M + cands[c].bm - 1) / cands[c].bm) * ((N + cands[c].bn - 1) / cands[c].bn);
-        const int64_t slots = cus * cands[c].per_cu;
-        const int64_t rounds = (tiles + slots - 1) / slots;
-        const double cost = (double)rounds * cands[c].per_cu * cands[c].bm * cands[c].bn / cands[c].rate;
-        if (cost < best_cost * 0.999) {
-            best_cost = cost;
-            best = c;
-        }
-    }
-    if (best == 0)
-        return dispatch<256, 256, SQ_W256_WM, SQ_W256_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out,
-                                                          side, st);
-    if (best == 1)
-        return dispatch<256, 192, SQ_W192_WM, SQ_W192_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out,
-                                                          side, st);
-    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, side, st);
+    return launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, N, ydt, acc_out, side, st, true);
 }
 
 }  // namespace sq

@@ -1,0 +1,79 @@
+"""Checks on the gfx950 ISA the library's sources compile to (hipcc runs on the
+CPU; nothing is launched).  They guard assumptions the kernels make about code
+generation that no numerical test would catch reliably."""
+import re
+
+import pytest
+
+from int8_quantization_amd import build as B
+
+
+def kernels(asm):
+    """{kernel symbol: list of its instruction lines}, in order."""
+    out, name = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name = m.group(1)
+            out[name] = []
+            continue
+        if name is not None:
+            if line.strip().startswith("s_endpgm"):
+                out[name].append(line)
+                name = None
+            else:
+                out[name].append(line)
+    return out
+
+
+@pytest.fixture(scope="module")
+def gemm_asm():
+    return B.device_asm("gemm.hip")
+
+
+def test_gemm_m0_only_written_by_the_dma_asm(gemm_asm):
+    """The tile kernel's operand DMA is issued from inline asm that loads M0
+    itself; nothing the compiler emits may depend on M0 surviving it, so M0 must
+    be written (and buffer ... lds issued) only inside those asm blocks."""
+    ks = {k: v for k, v in kernels(gemm_asm).items() if "gemm_i8_kernel" in k}
+    assert len(ks) >= 6
+    for name, lines in ks.items():
+        inside, n_dma = False, 0
+        for l in lines:
+            t = l.strip()
+            if t.startswith(";;#ASMSTART"):
+                inside = True
+                prev = None
+                continue
+            if t.startswith(";;#ASMEND"):
+                inside = False
+                continue
+            if not t or t.startswith(";") or t.startswith("."):
+                continue
+            ops = t.split(None, 1)
+            writes_m0 = len(ops) > 1 and ops[1].split(",")[0].strip() == "m0"
+            is_lds_dma = " lds" in t and t.startswith("buffer_load")
+            if not inside:
+                assert not writes_m0, f"{name}: compiler writes M0: {t}"
+                assert not is_lds_dma, f"{name}: LDS DMA outside the asm helper: {t}"
+            elif is_lds_dma:
+                n_dma += 1
+        assert n_dma > 0, name
+
+
+def test_gemm_kernels_do_not_spill(gemm_asm):
+    """Scratch use in the tile kernels means register spills in the MFMA loop."""
+    meta = re.findall(r"\.name:\s+(_Z\w+gemm_i8_kernel\w*)\s*\n(?:.*\n)*?\s+\.private_segment_fixed_size:\s+(\d+)",
+                      gemm_asm)
+    sizes = dict(meta)
+    assert len(sizes) >= 6
+    for name, size in sizes.items():
+        assert int(size) == 0, f"{name} uses {size} bytes of scratch"
+
+
+@pytest.mark.parametrize("src", B.SOURCES)
+def test_no_packed_fp32_instructions(src):
+    """The library is built with packed fp32 disabled; no v_pk_{add,mul,fma}_f32 may appear."""
+    asm = B.device_asm(src)
+    bad = re.findall(r"^\s*v_pk_(?:add|mul|fma)_f32\b.*$", asm, re.M)
+    assert not bad, bad[:3]

@@ -214,6 +214,30 @@ def test_gemm_large_tiles_sampled(sq, orc, M, N, K):
         assert_bits_equal(acc[r, cc], orc.gemm_i8_sampled(Xq, Wq, r, cc), "acc column")
 
 
+@pytest.mark.parametrize("gran,use_bias,out_dt", [(0, False, np.float16), (1, True, np.float32)])
+def test_gemm_column_split_sampled(sq, orc, gran, use_bias, out_dt):
+    """4096 x 10240 makes 640 tiles of 256 x 256, two and a half rounds on 256 CUs:
+    the launch gives the two full rounds the leading 8192 output columns and runs
+    the rest as a second launch with smaller tiles over offset weight rows,
+    scales, bias and output columns (the output row stride stays N)."""
+    M, N, K = 4096, 10240, 144
+    Xq, xs, Wq, ws, bias = _gemm_case(91, M, N, K, gran)
+    bias = bias if use_bias else None
+    acc, Y = gpu_gemm(sq, Xq, xs, Wq, ws, gran, bias, out_dt)
+    half = (lambda y: y) if out_dt == np.float32 else orc.float_to_half
+    rows, cols = sample_positions(M, N, 20000)
+    ref_acc = orc.gemm_i8_sampled(Xq, Wq, rows, cols)
+    assert_bits_equal(acc[rows, cols], ref_acc, "acc (sampled)")
+    assert_bits_equal(Y[rows, cols], half(orc.dequant_sampled(ref_acc, xs, ws, gran, bias, rows, cols)), "Y (sampled)")
+    # every row of the columns on both sides of the split and at the edges
+    r = np.arange(M, dtype=np.int64)
+    for c in (0, 8191, 8192, 8193, N - 1):
+        cc = np.full(M, c, np.int64)
+        a = orc.gemm_i8_sampled(Xq, Wq, r, cc)
+        assert_bits_equal(acc[r, cc], a, f"acc column {c}")
+        assert_bits_equal(Y[r, cc], half(orc.dequant_sampled(a, xs, ws, gran, bias, r, cc)), f"Y column {c}")
+
+
 def test_gemm_deterministic(sq):
     Xq, xs, Wq, ws, _ = _gemm_case(3, 640, 1024, 2048, 0)
     outs = [gpu_gemm(sq, Xq, xs, Wq, ws, 0, None, np.float16) for _ in range(3)]
@@ -257,6 +281,30 @@ def test_outlier_matmul(sq, orc, M, N, K, n_out, thr):
     assert_bits_equal(idx, ref_idx, "outlier idx")
     assert_bits_equal(acc, ref_acc, "acc")
     assert_close(Y, ref_Y, 1e-2)
+
+
+def test_outlier_matmul_column_split_sampled(sq, orc):
+    """LLM.int8() at a shape whose int8 GEMM splits its output columns over two
+    launches: the second launch reads the gathered outlier weight rows from the
+    split column on."""
+    M, N, K = 4096, 10240, 160
+    X, W16, _ = workloads.random_layer(17, M, K, N, np.float16, n_outliers=5, factor=20.0)
+    Wq, ws = gpu_quantize_weight(sq, W16, None, 0)
+    Wq_r, ws_r = orc.quantize_weight(W16, None, 0)
+    assert_bits_equal(Wq, Wq_r, "Wq")
+    c, idx, acc, Y = gpu_outlier(sq, X, W16, Wq, ws, None, 6.0)
+    mask, ref_idx = orc.outlier_columns(X, 6.0)
+    assert c == ref_idx.size and c >= 5
+    assert_bits_equal(idx, ref_idx, "outlier idx")
+    Xq_r, xs_r = orc.quantize_per_token(X, None, skip=mask)
+    r, cc = sample_positions(M, N, 4000)
+    r = np.concatenate([r, np.arange(M, dtype=np.int64), np.arange(M, dtype=np.int64)])
+    cc = np.concatenate([cc, np.full(M, 8191, np.int64), np.full(M, 8192, np.int64)])
+    acc_r = orc.gemm_i8_sampled(Xq_r, Wq_r, r, cc)
+    assert_bits_equal(acc[r, cc], acc_r, "acc (sampled)")
+    y = orc.dequant_sampled(acc_r, xs_r, ws_r, 0, None, r, cc)
+    side = orc.side_product_sampled(X, W16, ref_idx, r, cc)
+    assert_close(Y[r, cc], orc.combine_to_half(y, side), 1e-2)
 
 
 # ---------------------------------------------------------------------------
