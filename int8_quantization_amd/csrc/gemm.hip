@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     for (int c = tid; c < BN; c += NT) {
         const int n = n0 + c < N ? n0 + c : N - 1;
         sws[c] = ws[(int64_t)n * ws_stride];
-        sbias[c] = bias != nullptr ? bias[n] : 0.0f;
+        sbias[c] = bias != nullptr ? bias[n] : -0.0f;   // x + (-0.0) == x for every x
     }
     // The epilogue's kernel arguments go to registers now: scalar loads still in
     // flight when the loop starts would make the compiler's fragment waits in it
@@ -337,14 +337,55 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     }
     if constexpr (SIDE) wait_all_loads();
 
+    // This lane's row and column scales for the whole epilogue, read from LDS in
+    // one batch (one latency instead of one per accumulator group); the optional
+    // bias is read where it is added.  The LLM.int8() variant has no registers to
+    // spare for them and reads the column scales per accumulator group.
+    constexpr bool HOIST = !SIDE;
+    float xsr[TM];
+    v4f wsr[HOIST ? TN : 1][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) xsr[i] = sxs[wm * WTM + i * 32 + lrow];
+    if constexpr (HOIST) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                wsr[j][a] = *reinterpret_cast<const v4f*>(&sws[wn * WTN + j * 32 + 8 * a + 4 * lk]);
+    }
+
+    // int32 accumulators, when requested (parity checks): straight from the
+    // accumulator registers, 16 bytes per lane per group of four columns
+    if (acc_out != nullptr) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WTM + i * 32 + lrow;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int n = n0 + wn * WTN + j * 32 + 8 * a + 4 * lk;
+                    int iv[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(iv[b]) : "a"(acc[i][j][4 * a + b]));
+                    if (m < M)
+                        for (int b = 0; b < 4; ++b)
+                            if (n + b < N) acc_out[(int64_t)m * ldy + n + b] = iv[b];
+                }
+        }
+    }
+
+#pragma unroll
     for (int h = 0; h < HALVES; ++h) {
-        // write phase
+        // write phase: branch-free per accumulator tile (the bias add is unconditional,
+        // the int32 accumulator output has its own pass)
 #pragma unroll
         for (int ii = 0; ii < TMH; ++ii) {
             const int i = h * TMH + ii;
             const int lr = wm * (TMH * 32) + ii * 32 + lrow;      // LDS row
             const int mloc = wm * WTM + i * 32 + lrow;           // tile row
-            const float xsv = sxs[mloc];
+            const float xsv = xsr[i];
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -352,7 +393,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const int nloc = wn * WTN + j * 32 + 8 * a + 4 * lk;
-                    const v4f w4 = *reinterpret_cast<const v4f*>(&sws[nloc]);
+                    const v4f w4 = HOIST ? wsr[HOIST ? j : 0][a] : *reinterpret_cast<const v4f*>(&sws[nloc]);
                     const v4f b4 = *reinterpret_cast<const v4f*>(&sbias[nloc]);
                     int iv[4];
 #pragma unroll
@@ -362,15 +403,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                         float v = (float)iv[b];
                         v = v * xsv;
                         v = v * w4[b];
-                        if (bias != nullptr) v = v + b4[b];
+                        v = v + b4[b];      // -0.0 without a bias: an exact identity
                         y[4 * a + b] = v;
-                    }
-                    if (acc_out != nullptr) {
-                        const int m = m0 + mloc;
-                        const int n = n0 + nloc;
-                        if (m < M)
-                            for (int b = 0; b < 4; ++b)
-                                if (n + b < N) acc_out[(int64_t)m * ldy + n + b] = iv[b];
                     }
                 }
                 if constexpr (SIDE) {
@@ -389,8 +423,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                 for (int a = 0; a < 4; ++a) {
                     const int cb = (wn * WTN + j * 32 + 8 * a + 4 * lk) * OB;
                     if constexpr (OUT_F16) {
-                        *reinterpret_cast<h4*>(lds + lofs(lr, cb)) =
-                            h4{(_Float16)y[4 * a], (_Float16)y[4 * a + 1], (_Float16)y[4 * a + 2], (_Float16)y[4 * a + 3]};
+                        // two round-to-nearest-even pair conversions (v_cvt_pk_f16_f32), stored as two dwords
+                        typedef float f2 __attribute__((ext_vector_type(2)));
+                        typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
+                        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+                        const hf2 lo = __builtin_convertvector(f2{y[4 * a], y[4 * a + 1]}, hf2);
+                        const hf2 hi = __builtin_convertvector(f2{y[4 * a + 2], y[4 * a + 3]}, hf2);
+                        *reinterpret_cast<u2*>(lds + lofs(lr, cb)) =
+                            u2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
                     } else {
                         *reinterpret_cast<v4f*>(lds + lofs(lr, cb)) = v4f{y[4 * a], y[4 * a + 1], y[4 * a + 2], y[4 * a + 3]};
                     }
@@ -399,23 +439,49 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         }
         wait_lds();
         block_barrier();
-        // copy phase: 16-byte chunks, consecutive threads along a row
+        // copy phase: 16-byte chunks, consecutive threads along a row; a thread
+        // issues its LDS reads in batches of up to 8 before the batch's stores
+        constexpr int NQ = HROWS * CH16 / NT;
+        static_assert(NQ * NT == HROWS * CH16, "copy phase must split evenly over the threads");
+        constexpr int QB = [] {   // largest divisor of NQ up to 8
+            for (int d = 8; d > 1; --d)
+                if (NQ % d == 0) return d;
+            return 1;
+        }();
+        static_assert(NQ % QB == 0, "copy batches must split evenly");
         const bool vec = (ldy * OB) % 16 == 0;
-        for (int q = tid; q < HROWS * CH16; q += NT) {
-            const int lr = q / CH16, c = q % CH16;
-            const int wmq = lr / (TMH * 32), rem = lr % (TMH * 32);
-            const int m = m0 + wmq * WTM + (h * TMH + rem / 32) * 32 + rem % 32;
-            if (m >= M) continue;
-            const int n = n0 + c * (16 / OB);
-            const v4i v = *reinterpret_cast<const v4i*>(lds + lofs(lr, c * 16));
-            char* dst = reinterpret_cast<char*>(Yv) + ((int64_t)m * ldy + n) * OB;
-            if (vec && n + 16 / OB <= N) {
-                *reinterpret_cast<v4i*>(dst) = v;
-            } else {
-                const char* src = reinterpret_cast<const char*>(&v);
-                for (int e = 0; e < 16 / OB; ++e)
-                    if (n + e < N)
-                        for (int bb = 0; bb < OB; ++bb) dst[e * OB + bb] = src[e * OB + bb];
+#pragma unroll
+        for (int k0 = 0; k0 < NQ; k0 += QB) {
+            v4i cv[QB];
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+                const int q = tid + (k0 + k) * NT;
+                cv[k] = *reinterpret_cast<const v4i*>(lds + lofs(q / CH16, (q % CH16) * 16));
+            }
+#pragma unroll
+            for (int k = 0; k < QB; ++k) {
+                const int q = tid + (k0 + k) * NT;
+                const int lr = q / CH16, c = q % CH16;
+                const int wmq = lr / (TMH * 32), rem = lr % (TMH * 32);
+                const int m = m0 + wmq * WTM + (h * TMH + rem / 32) * 32 + rem % 32;
+                if (m < M) {
+                    const int n = n0 + c * (16 / OB);
+                    char* dst = reinterpret_cast<char*>(Yv) + ((int64_t)m * ldy + n) * OB;
+                    if (vec && n + 16 / OB <= N) {
+                        *reinterpret_cast<v4i*>(dst) = cv[k];
+                    } else {
+                        // ragged edge or unaligned rows: element stores (constant indices keep
+                        // the chunk in registers)
+#pragma unroll
+                        for (int e = 0; e < 16 / OB; ++e) {
+                            if (n + e >= N) continue;
+                            if constexpr (OB == 4)
+                                reinterpret_cast<uint32_t*>(dst)[e] = (uint32_t)cv[k][e];
+                            else
+                                reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)((uint32_t)cv[k][e / 2] >> (16 * (e % 2)));
+                        }
+                    }
+                }
             }
         }
         if (h + 1 < HALVES) {
