@@ -46,6 +46,10 @@ def _load():
         "orc_outlier_columns": (I64, [P, I64, I64, F, P, P]),
         "orc_side_product_sampled": (None, [P, P, I64, P, I64, P, P, I64, P]),
         "orc_combine_to_half": (None, [P, P, I64, P]),
+        "orc_layernorm_stats": (None, [P, I64, I64, F, P, P, P, P]),
+        "orc_layernorm": (None, [P, I64, I64, P, P, F, P]),
+        "orc_layernorm_quantize": (None, [P, I64, I64, P, P, F, P, P]),
+        "orc_fold_layernorm": (None, [P, P, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -248,3 +252,58 @@ def llm_int8_linear(X16, W16, Wq, w_scale, threshold, bias=None, rows=None):
     cc = np.tile(np.arange(N, dtype=np.int64), M)
     side = side_product_sampled(Xr, W16, idx, rr, cc).reshape(M, N)
     return mask, idx, Xq, xs, acc, combine_to_half(y, side)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm with the smoothing folded in, fused with per-token quantization
+# ("SmoothQuant量化实战", sections 2.3, 4.2, 4.5).  Binary16 inputs; exact
+# integer row statistics (see sq_oracle.c for the reading).
+# ---------------------------------------------------------------------------
+def _half_bits(X16):
+    X16 = np.ascontiguousarray(X16, dtype=np.float16)
+    return X16.view(np.uint16)
+
+
+def fold_layernorm(gamma, beta, s):
+    """gamma' = fl32(gamma / s), beta' = fl32(beta / s) (beta may be None)."""
+    g = _as(gamma, np.float32)
+    b = None if beta is None else _as(beta, np.float32)
+    sv = _as(s, np.float32)
+    K = g.size
+    go = np.empty(K, np.float32)
+    bo = None if b is None else np.empty(K, np.float32)
+    _load().orc_fold_layernorm(_ptr(g), _ptr(b), _ptr(sv), K, _ptr(go), _ptr(bo))
+    return go, bo
+
+
+def layernorm_stats(X16, eps):
+    """(mu32, rstd32, mu64, var64) per row."""
+    h = _half_bits(X16)
+    M, K = h.shape
+    mu32, r32 = np.empty(M, np.float32), np.empty(M, np.float32)
+    mu64, var64 = np.empty(M, np.float64), np.empty(M, np.float64)
+    _load().orc_layernorm_stats(_ptr(h), M, K, float(eps), _ptr(mu32), _ptr(r32), _ptr(mu64), _ptr(var64))
+    return mu32, r32, mu64, var64
+
+
+def layernorm(X16, gamma, beta, eps):
+    """LayerNorm output y (fp32 [M, K]) with the (folded) weights."""
+    h = _half_bits(X16)
+    M, K = h.shape
+    g = _as(gamma, np.float32)
+    b = None if beta is None else _as(beta, np.float32)
+    Y = np.empty((M, K), np.float32)
+    _load().orc_layernorm(_ptr(h), M, K, _ptr(g), _ptr(b), float(eps), _ptr(Y))
+    return Y
+
+
+def layernorm_quantize(X16, gamma, beta, eps):
+    """The fused forward step: (Xq int8 [M, K], x_scale fp32 [M])."""
+    h = _half_bits(X16)
+    M, K = h.shape
+    g = _as(gamma, np.float32)
+    b = None if beta is None else _as(beta, np.float32)
+    Xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    _load().orc_layernorm_quantize(_ptr(h), M, K, _ptr(g), _ptr(b), float(eps), _ptr(Xq), _ptr(xs))
+    return Xq, xs

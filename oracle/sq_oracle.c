@@ -21,6 +21,8 @@
  *    compute_smooth_scale with the 1e-8 floors (section 3.3), the calibration
  *    running max (section 3.2), the W8A8 forward (section 3.4), bias kept in
  *    floating point (section 4.5).
+ *  - the same SmoothQuant page, sections 2.3, 4.2 and 4.5: the per-channel
+ *    division by s can be absorbed into the preceding LayerNorm's output.
  *  - "LLM.int8()技术解析：8位量化如何优化大语言模型计算": column-wise absmax,
  *    columns above a threshold handled in fp16, the rest in int8, results
  *    combined (sections 2.1 and 3.1).
@@ -365,4 +367,93 @@ void orc_side_product_sampled(const uint16_t* X16, const uint16_t* W16, int64_t 
 void orc_combine_to_half(const float* y_int8, const double* side, int64_t n, uint16_t* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_float_to_half((float)((double)y_int8[i] + side[i]));
+}
+
+/* ------------------------------------------------------------------ */
+/* LayerNorm with the smoothing folded in, then per-token quantization  */
+/* (SmoothQuant page, sections 2.3, 4.2 and 4.5: the per-channel        */
+/* division X/s is absorbed into the preceding LayerNorm's output).     */
+/*                                                                      */
+/* Reading (the pages give no LayerNorm precision): binary16 inputs     */
+/* only.  Each finite x is n * 2^-24 with an integer n (|n| < 2^40), so  */
+/* the row sums S1 = sum n and S2 = sum n^2 are exact integers and the   */
+/* statistics do not depend on summation order:                         */
+/*   mu   = fl64( fl64(S1) / (K * 2^24) )                               */
+/*   var  = fl64( fl64(K*S2 - S1^2) / (K^2 * 2^48) )   (population var) */
+/*   rstd = fl64( 1 / fl64(sqrt( fl64(var + eps) )) )                    */
+/*   z_j  = fl32( fl32(x_j - fl32(mu)) * fl32(rstd) )                    */
+/*   y_j  = fl32( fl32(z_j * g_j) + b_j )   (no add when there is no b)  */
+/* with g = gamma/s and b = beta/s folded offline, each one fl32 divide. */
+/* ------------------------------------------------------------------ */
+
+/* the integer n with x = n * 2^-24 for a finite binary16 x */
+static int64_t half_to_int24(uint16_t h)
+{
+    int64_t e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    int64_t n = e ? (1024 + m) << (e - 1) : m;
+    return (h & 0x8000u) ? -n : n;
+}
+
+void orc_layernorm_stats(const uint16_t* X, int64_t M, int64_t K, float eps, float* mu32, float* rstd32,
+                         double* mu64, double* var64)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t s1 = 0;
+        __int128 s2 = 0;
+        for (int64_t j = 0; j < K; ++j) {
+            int64_t n = half_to_int24(X[m * K + j]);
+            s1 += n;
+            s2 += (__int128)n * n;
+        }
+        __int128 v = (__int128)K * s2 - (__int128)s1 * s1;        /* K^2 times the variance, scaled */
+        double mu = (double)s1 / ((double)K * 0x1p24);
+        double var = (double)v / (((double)K * (double)K) * 0x1p48);
+        double rstd = 1.0 / sqrt(var + (double)eps);
+        mu32[m] = (float)mu;
+        rstd32[m] = (float)rstd;
+        if (mu64) mu64[m] = mu;
+        if (var64) var64[m] = var;
+    }
+}
+
+/* y = LayerNorm output with the folded weights, fp32 [M x K]; beta may be NULL */
+void orc_layernorm(const uint16_t* X, int64_t M, int64_t K, const float* gamma, const float* beta, float eps,
+                   float* Y)
+{
+    float* mu = (float*)malloc((size_t)M * sizeof(float));
+    float* r = (float*)malloc((size_t)M * sizeof(float));
+    orc_layernorm_stats(X, M, K, eps, mu, r, NULL, NULL);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; ++j) {
+            float x = orc_half_to_float(X[m * K + j]);
+            float z = (x - mu[m]) * r[m];
+            float y = z * gamma[j];
+            if (beta) y = y + beta[j];
+            Y[m * K + j] = y;
+        }
+    free(mu);
+    free(r);
+}
+
+/* The fused step: LayerNorm (folded weights), then per-token quantization of
+ * its fp32 output with no smoothing (the smoothing is inside gamma and beta). */
+void orc_layernorm_quantize(const uint16_t* X, int64_t M, int64_t K, const float* gamma, const float* beta,
+                            float eps, int8_t* Xq, float* x_scale)
+{
+    float* Y = (float*)malloc((size_t)(M * K) * sizeof(float));
+    orc_layernorm(X, M, K, gamma, beta, eps, Y);
+    orc_quantize_per_token(Y, ORC_F32, M, K, NULL, NULL, Xq, x_scale);
+    free(Y);
+}
+
+/* Offline fold: gamma' = fl32(gamma / s), beta' = fl32(beta / s) per input channel. */
+void orc_fold_layernorm(const float* gamma, const float* beta, const float* s, int64_t K, float* gamma_out,
+                        float* beta_out)
+{
+    for (int64_t j = 0; j < K; ++j) {
+        gamma_out[j] = gamma[j] / s[j];
+        if (beta) beta_out[j] = beta[j] / s[j];
+    }
 }

@@ -462,3 +462,147 @@ def test_quantize_divides_by_scale(orc):
     Xq, xs = orc.quantize_per_token(X)
     assert Xq[:, 0].tolist() == [127] * len(rows)
     assert Xq[:, 1].tolist() == [int(q) for _, _, q in rows]
+
+
+# --------------------------------------------------------------------------
+# LayerNorm with the smoothing folded in, fused with per-token quantization
+# ("SmoothQuant量化实战", sections 2.3, 4.2, 4.5).  Statistics are exact
+# integer sums of binary16 values (the reading for this step).
+# --------------------------------------------------------------------------
+
+def _ln_rows(seed, M, K, scale=1.0):
+    r = np.random.default_rng(seed)
+    X = (r.standard_normal((M, K)) * scale + r.standard_normal((M, 1)) * scale).astype(np.float16)
+    return X
+
+
+def test_layernorm_stats_vs_exact_rationals(orc):
+    """mu and the population variance against exact rational arithmetic with the
+    two-pass definition sum((x - mean)^2) / K (not the oracle's K*S2 - S1^2)."""
+    X = _ln_rows(11, 24, 48, scale=3.0)
+    X[0] = np.float16(65504.0) * np.sign(X[0]).astype(np.float16)     # extreme magnitudes
+    X[1, ::2] = np.float16(6e-8)                                        # subnormals
+    X[2] = np.float16(-0.0)
+    _, _, mu64, var64 = orc.layernorm_stats(X, 1e-5)
+    for m in range(X.shape[0]):
+        xs = [Fraction(float(v)) for v in X[m].astype(np.float64)]
+        mu = sum(xs) / len(xs)
+        var = sum((x - mu) ** 2 for x in xs) / len(xs)
+        assert mu64[m] == float(mu) or abs(mu64[m] - float(mu)) <= math.ulp(float(mu)), m
+        assert abs(var64[m] - float(var)) <= 2 * math.ulp(float(var)) + 0.0, m
+    # small integer-valued rows: the sums stay below 2^53, so the definition is the
+    # correctly rounded exact value
+    Xs = np.array([[1, 2, 3, 4, 5, 6, 7, 9], [0.5, -0.25, 8, 8, 8, 8, -3, 1]], np.float16)
+    _, _, mu64, var64 = orc.layernorm_stats(Xs, 0.0)
+    for m in range(2):
+        xs = [Fraction(float(v)) for v in Xs[m].astype(np.float64)]
+        mu = sum(xs) / 8
+        assert mu64[m] == float(mu)
+        assert var64[m] == float(sum((x - mu) ** 2 for x in xs) / 8)
+
+
+def test_layernorm_vs_torch_fp64(orc):
+    """The normalised, scaled and shifted output against torch's layer_norm in fp64:
+    biased variance, eps inside the square root, y = z * gamma + beta."""
+    torch = pytest.importorskip("torch")
+    M, K = 64, 1040
+    X = _ln_rows(12, M, K, scale=2.0)
+    r = np.random.default_rng(13)
+    g = r.uniform(0.2, 3.0, K).astype(np.float32)
+    b = r.standard_normal(K).astype(np.float32)
+    eps = 1e-5
+    y = orc.layernorm(X, g, b, eps)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(X.astype(np.float64)), (K,),
+                                         weight=torch.from_numpy(g.astype(np.float64)),
+                                         bias=torch.from_numpy(b.astype(np.float64)), eps=eps).numpy()
+    err = np.abs(y.astype(np.float64) - ref)
+    assert err.max() <= 1e-5 * np.abs(ref).max(), err.max()
+    # without beta: no shift at all
+    y0 = orc.layernorm(X, g, None, eps)
+    assert np.array_equal(y0 + b, y)  # fl32(z*g) + b is exactly the with-beta result
+
+
+def test_layernorm_special_rows(orc):
+    K = 64
+    X = np.zeros((4, K), np.float16)
+    X[0] = np.float16(3.5)                       # constant row: var = 0
+    X[1, ::2], X[1, 1::2] = np.float16(-2.0), np.float16(2.0)   # mean 0, var 4
+    X[2] = np.float16(0.0)                       # zero row
+    X[3, :4] = np.array([1, 2, 3, 4], np.float16)
+    eps = 1e-5
+    e64 = float(np.float32(eps))                 # the entry point takes eps as binary32
+    mu32, r32, mu64, var64 = orc.layernorm_stats(X, eps)
+    assert mu64[0] == 3.5 and var64[0] == 0.0 and r32[0] == np.float32(1.0 / math.sqrt(e64))
+    assert mu64[1] == 0.0 and var64[1] == 4.0 and r32[1] == np.float32(1.0 / math.sqrt(4.0 + e64))
+    assert mu64[2] == 0.0 and var64[2] == 0.0
+    b = np.linspace(-1, 1, K).astype(np.float32)
+    y = orc.layernorm(X, np.full(K, 1.5, np.float32), b, eps)
+    assert np.array_equal(y[0], b) and np.array_equal(y[2], b)      # z == 0 exactly
+    # hand-worked: [1,2,3,4] over K = 4 has mean 2.5 and variance 1.25
+    X4 = np.array([[1, 2, 3, 4]], np.float16)
+    mu32, r32, mu64, var64 = orc.layernorm_stats(X4, eps)
+    assert mu64[0] == 2.5 and var64[0] == 1.25
+    q, xs = orc.layernorm_quantize(X4, np.ones(4, np.float32), None, eps)
+    z = np.float32(1.5) * np.float32(1.0 / math.sqrt(1.25 + e64))
+    assert xs[0] == np.float32(z / np.float32(127.0))
+    assert q.tolist() == [[-127, -42, 42, 127]]       # 0.5/1.5 * 127 = 42.33
+    # zero row without beta: scale 0, codes 0
+    q, xs = orc.layernorm_quantize(X[2:3], np.ones(K, np.float32), None, eps)
+    assert xs[0] == 0.0 and not q.any()
+
+
+def test_fold_layernorm_direction_and_axis(orc):
+    """LayerNorm with gamma/s, beta/s equals LayerNorm followed by X / s: bit-exact for
+    power-of-two s (every division exact), close for general s."""
+    M, K = 16, 256
+    X = _ln_rows(14, M, K)
+    r = np.random.default_rng(15)
+    g = r.uniform(0.5, 2.0, K).astype(np.float32)
+    b = r.standard_normal(K).astype(np.float32)
+    s2 = np.exp2(r.integers(-6, 7, K)).astype(np.float32)
+    g2, b2 = orc.fold_layernorm(g, b, s2)
+    assert np.array_equal(g2, g / s2) and np.array_equal(b2, b / s2)
+    y = orc.layernorm(X, g, b, 1e-5)
+    assert np.array_equal(orc.layernorm(X, g2, b2, 1e-5), y / s2[None, :])
+    s = r.uniform(0.05, 20.0, K).astype(np.float32)
+    gs, bs = orc.fold_layernorm(g, b, s)
+    ys = orc.layernorm(X, gs, bs, 1e-5).astype(np.float64)
+    ref = y.astype(np.float64) / s[None, :]
+    assert np.abs(ys - ref).max() <= 4 * np.finfo(np.float32).eps * np.abs(ref).max()
+    gn, bn = orc.fold_layernorm(g, None, s)
+    assert bn is None and np.array_equal(gn, gs)
+
+
+def test_layernorm_quantize_invariants(orc):
+    """Every non-zero row reaches |q| = 127, and |y - q*xs| <= xs/2 elementwise."""
+    M, K = 48, 4112
+    X = _ln_rows(16, M, K, scale=4.0)
+    r = np.random.default_rng(17)
+    g = r.uniform(0.1, 5.0, K).astype(np.float32)
+    b = (r.standard_normal(K) * 0.1).astype(np.float32)
+    q, xs = orc.layernorm_quantize(X, g, b, 1e-5)
+    y = orc.layernorm(X, g, b, 1e-5).astype(np.float64)
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    assert np.all(xs == (np.abs(y).max(axis=1) / 127.0).astype(np.float32)) or \
+        np.all(xs == (np.abs(y).max(axis=1).astype(np.float32) / np.float32(127.0)))
+    err = np.abs(y - q.astype(np.float64) * xs[:, None].astype(np.float64))
+    assert np.all(err <= xs[:, None].astype(np.float64) * (0.5 + 1e-6))
+
+
+def test_layernorm_workload_shape_vs_fp64(orc):
+    """The C2 activation shape (2048 x 4096 fp16, outlier channels), fold with a
+    real smoothing vector, against fp64 within the fp32 error of the steps."""
+    torch = pytest.importorskip("torch")
+    wl = workloads.prefill_7b(which=("qkv",))
+    X = wl.X[:256]
+    K = X.shape[1]
+    r = np.random.default_rng(18)
+    g = r.uniform(0.5, 1.5, K).astype(np.float32)
+    b = (r.standard_normal(K) * 0.05).astype(np.float32)
+    s = r.uniform(0.2, 8.0, K).astype(np.float32)
+    gs, bs = orc.fold_layernorm(g, b, s)
+    y = orc.layernorm(X, gs, bs, 1e-5).astype(np.float64)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(X.astype(np.float64)), (K,),
+                                         weight=torch.from_numpy(g.astype(np.float64)),
+                                         bias=torch.from_numpy(b.astype(np.float64)), eps=1e-5).numpy() / s
+    assert np.abs(y - ref).max() <= 1e-5 * np.abs(ref).max()
