@@ -64,7 +64,7 @@ typedef enum {
     SQ_ERR_SHAPE = 2,     /* M, N or K out of range, or K % 16 != 0 */
     SQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
     SQ_ERR_DTYPE = 4,     /* unsupported dtype or granularity code */
-    SQ_ERR_VALUE = 5,     /* alpha outside [0,1], threshold negative or NaN */
+    SQ_ERR_VALUE = 5,     /* alpha outside [0,1], threshold negative or NaN, eps not finite and > 0 */
     SQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than sq_workspace_size() */
     SQ_ERR_HIP = 7        /* a HIP launch or device query failed */
 } sq_status;
@@ -170,6 +170,40 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq,
                               int64_t M, int64_t N, int64_t K, float threshold, void* Y,
                               void* ws, size_t ws_bytes, int32_t* n_outliers,
                               int32_t* outlier_idx, int32_t* acc_out, hipStream_t stream);
+
+/* Offline fold of the smoothing into the preceding LayerNorm's weights.
+ * [SmoothQuant page, section 2.3: the per-channel division of the activations
+ *  can be merged into the previous layer; section 4.2: absorb the scaling into
+ *  the preceding operation's output, e.g. the LayerNorm; section 4.5: with the
+ *  LayerNorm before the Linear the scaling costs nothing extra.]
+ *   gamma, s   device float [K];  beta device float [K] or NULL.
+ *   gamma_out  device float [K], out: fl32(gamma[j] / s[j]).
+ *   beta_out   device float [K], out: fl32(beta[j] / s[j]); NULL exactly when beta is NULL.
+ * LayerNorm(x; gamma_out, beta_out) is then LayerNorm(x; gamma, beta) / s per channel.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE (K as above), SQ_ERR_ALIGN, SQ_ERR_HIP. */
+sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, const float* s,
+                                      int64_t K, float* gamma_out, float* beta_out,
+                                      hipStream_t stream);
+
+/* LayerNorm (folded weights) fused with per-token quantization (every forward):
+ * the smoothed activation of step 1 comes straight out of the LayerNorm and is
+ * quantized as in sq_quantize_per_token with s = NULL.
+ * [SmoothQuant page, sections 2.3, 4.2 and 4.5, as for the fold above.]
+ *   X        device, fp16 [M x K] (xdt must be SQ_F16).
+ *   gamma    device float [K], beta device float [K] or NULL (from the fold).
+ *   eps      finite, > 0.
+ *   Row statistics are exact: each x is n * 2^-24 for an integer n, and
+ *     mu   = fl64(fl64(S1) / (K 2^24)),  S1 = sum n (exact);
+ *     var  = fl64(fl64(K S2 - S1^2) / (K^2 2^48)),  S2 = sum n^2 (exact);
+ *     rstd = fl64(1 / fl64(sqrt(fl64(var + eps))));
+ *   then per element, in binary32: z = (x - fl32(mu)) * fl32(rstd),
+ *   y = z * gamma[j] (+ beta[j]).
+ *   Xq       device int8 [M x K], out: clamp(rne(fl32(y / xs)), -128, 127).
+ *   x_scale  device float [M], out: xs = fl32(max_j |y_j| / 127) (0 and all-zero codes when y == 0).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_HIP. */
+sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K,
+                                          const float* gamma, const float* beta, float eps,
+                                          int8_t* Xq, float* x_scale, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,8 @@ def _load():
         "sq_quantize_weight": (I, [P, I, I64, I64, P, I, P, P, P, SZ, P]),
         "w8a8_gemm_dequant": (I, [P, P, P, P, I, P, I64, I64, I64, P, I, P, P]),
         "int8_outlier_matmul": (I, [P, P, P, P, P, I64, I64, I64, F, P, P, SZ, P, P, P, P]),
+        "sq_fold_smoothing_layernorm": (I, [P, P, P, I64, P, P, P]),
+        "sq_layernorm_quantize_per_token": (I, [P, I, I64, I64, P, P, F, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -53,7 +55,8 @@ def _load():
 _lib = _load()
 
 EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quantize_per_token",
-           "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul")
+           "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
+           "sq_layernorm_quantize_per_token")
 
 
 def _p(t):
@@ -135,3 +138,17 @@ def int8_outlier_matmul(X, W16, Wq, w_scale, bias, threshold, Y, ws, n_outliers=
     _check("int8_outlier_matmul", _lib.int8_outlier_matmul(
         _p(X), _p(W16), _p(Wq), _p(w_scale), _p(bias), M, N, K, float(threshold), _p(Y), _p(ws),
         nbytes, _p(n_outliers), _p(outlier_idx), _p(acc_out), _stream()))
+
+
+def sq_fold_smoothing_layernorm(gamma, beta, s, gamma_out, beta_out=None):
+    _dense(gamma, beta, s, gamma_out, beta_out)
+    K = gamma.numel()
+    _check("sq_fold_smoothing_layernorm", _lib.sq_fold_smoothing_layernorm(
+        _p(gamma), _p(beta), _p(s), K, _p(gamma_out), _p(beta_out), _stream()))
+
+
+def sq_layernorm_quantize_per_token(X, gamma, beta, eps, Xq, x_scale):
+    _dense(X, gamma, beta, Xq, x_scale)
+    M, K = X.shape
+    _check("sq_layernorm_quantize_per_token", _lib.sq_layernorm_quantize_per_token(
+        _p(X), _dt(X), M, K, _p(gamma), _p(beta), float(eps), _p(Xq), _p(x_scale), _stream()))

@@ -55,7 +55,7 @@ const char* sq_status_string(sq_status st) {
         case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: M, N >= 1 and 16 <= K <= 131056 with K % 16 == 0 are required";
         case SQ_ERR_ALIGN: return "SQ_ERR_ALIGN: pointers must be 16-byte aligned";
         case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: unsupported dtype or granularity";
-        case SQ_ERR_VALUE: return "SQ_ERR_VALUE: alpha must be in [0,1]; threshold finite and >= 0";
+        case SQ_ERR_VALUE: return "SQ_ERR_VALUE: alpha must be in [0,1]; threshold finite and >= 0; eps finite and > 0";
         case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
         case SQ_ERR_HIP: return "SQ_ERR_HIP: a HIP launch failed";
     }
@@ -161,6 +161,27 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, 
     SQ_TRY(launch_gather_cols(static_cast<const _Float16*>(W16), N, K, idx, count, wo, stream));
     SideArgs side{xo, wo, count, K};
     return hip_status(launch_gemm(xq, xs, Wq, w_scale, 1, bias, M, N, K, Y, SQ_F16, acc_out, &side, stream));
+}
+
+sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,
+                                      float* gamma_out, float* beta_out, hipStream_t stream) {
+    if (!gamma || !s || !gamma_out || (!beta) != (!beta_out)) return SQ_ERR_NULL;
+    if (bad_shape(1, 1, K)) return SQ_ERR_SHAPE;
+    if (misaligned(gamma) || misaligned(s) || misaligned(gamma_out) || (beta && (misaligned(beta) || misaligned(beta_out))))
+        return SQ_ERR_ALIGN;
+    return hip_status(launch_fold_layernorm(gamma, beta, s, K, gamma_out, beta_out, stream));
+}
+
+sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* gamma,
+                                          const float* beta, float eps, int8_t* Xq, float* x_scale,
+                                          hipStream_t stream) {
+    if (!X || !gamma || !Xq || !x_scale) return SQ_ERR_NULL;
+    if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
+    if (xdt != SQ_F16) return SQ_ERR_DTYPE;
+    if (!(eps > 0.0f && eps <= 3.4028235e38f)) return SQ_ERR_VALUE;
+    if (misaligned(X) || misaligned(gamma) || (beta && misaligned(beta)) || misaligned(Xq) || misaligned(x_scale))
+        return SQ_ERR_ALIGN;
+    return hip_status(launch_ln_quant(static_cast<const _Float16*>(X), M, K, gamma, beta, eps, Xq, x_scale, stream));
 }
 
 }  // extern "C"

@@ -110,4 +110,12 @@ hipError_t launch_outlier_compact(const uint32_t* cmax_bits, int64_t K, float th
 hipError_t launch_gather_cols(const _Float16* W16, int64_t N, int64_t K, const int32_t* idx,
                               const int32_t* count, _Float16* Wo, hipStream_t st);
 
+// LayerNorm (weights with the smoothing folded in) + per-token quantization, fp16 rows.
+hipError_t launch_ln_quant(const _Float16* X, int64_t M, int64_t K, const float* gamma, const float* beta,
+                           float eps, int8_t* Xq, float* scale, hipStream_t st);
+
+// gamma_out = gamma / s, beta_out = beta / s (beta may be null).
+hipError_t launch_fold_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,
+                                 float* gamma_out, float* beta_out, hipStream_t st);
+
 }  // namespace sq

@@ -33,6 +33,8 @@ def lib():
     lib.sq_quantize_weight.argtypes = [V, I, I64, I64, V, I, V, V, V, SZ, V]
     lib.w8a8_gemm_dequant.argtypes = [V, V, V, V, I, V, I64, I64, I64, V, I, V, V]
     lib.int8_outlier_matmul.argtypes = [V, V, V, V, V, I64, I64, I64, F, V, V, SZ, V, V, V, V]
+    lib.sq_fold_smoothing_layernorm.argtypes = [V, V, V, I64, V, V, V]
+    lib.sq_layernorm_quantize_per_token.argtypes = [V, I, I64, I64, V, V, F, V, V, V]
     return lib
 
 
@@ -136,3 +138,33 @@ def test_outlier_validation(lib):
     assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, P, need - 1, None, None, None, None) == WORKSPACE
     assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, P, need, P + 2, None, None, None) == ALIGN
     assert f(P, P, P, P, None, 32, 32, 64, 6.0, P, P, need, None, MIS, None, None) == ALIGN
+
+
+def test_fold_layernorm_validation(lib):
+    f = lib.sq_fold_smoothing_layernorm
+    assert f(None, None, P, 64, P, None, None) == NULL
+    assert f(P, None, None, 64, P, None, None) == NULL
+    assert f(P, None, P, 64, None, None, None) == NULL
+    assert f(P, P, P, 64, P, None, None) == NULL          # beta without beta_out
+    assert f(P, None, P, 64, P, P, None) == NULL          # beta_out without beta
+    assert f(P, None, P, 72, P, None, None) == SHAPE
+    assert f(P, None, P, 0, P, None, None) == SHAPE
+    assert f(MIS, None, P, 64, P, None, None) == ALIGN
+    assert f(P, P, P, 64, P, MIS, None) == ALIGN
+
+
+def test_layernorm_quantize_validation(lib):
+    f = lib.sq_layernorm_quantize_per_token
+    assert f(None, 1, 4, 64, P, None, 1e-5, P, P, None) == NULL
+    assert f(P, 1, 4, 64, None, None, 1e-5, P, P, None) == NULL
+    assert f(P, 1, 4, 64, P, None, 1e-5, None, P, None) == NULL
+    assert f(P, 1, 4, 64, P, None, 1e-5, P, None, None) == NULL
+    assert f(P, 1, 0, 64, P, None, 1e-5, P, P, None) == SHAPE
+    assert f(P, 1, 4, 40, P, None, 1e-5, P, P, None) == SHAPE
+    assert f(P, 0, 4, 64, P, None, 1e-5, P, P, None) == DTYPE      # fp16 rows only
+    assert f(P, 1, 4, 64, P, None, 0.0, P, P, None) == VALUE
+    assert f(P, 1, 4, 64, P, None, -1e-5, P, P, None) == VALUE
+    assert f(P, 1, 4, 64, P, None, math.nan, P, P, None) == VALUE
+    assert f(P, 1, 4, 64, P, None, math.inf, P, P, None) == VALUE
+    assert f(P, 1, 4, 64, P, MIS, 1e-5, P, P, None) == ALIGN
+    assert f(P, 1, 4, 64, P, None, 1e-5, MIS, P, None) == ALIGN

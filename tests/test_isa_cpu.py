@@ -1,11 +1,18 @@
 """Checks on the gfx950 ISA the library's sources compile to (hipcc runs on the
 CPU; nothing is launched).  They guard assumptions the kernels make about code
 generation that no numerical test would catch reliably."""
+import importlib.util
+import os
 import re
 
 import pytest
 
-from int8_quantization_amd import build as B
+# the build script itself, not the package (whose import loads the built library)
+_spec = importlib.util.spec_from_file_location(
+    "_sq_hip_build", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                  "int8_quantization_amd", "build.py"))
+B = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(B)
 
 
 def kernels(asm):

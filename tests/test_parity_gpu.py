@@ -383,3 +383,117 @@ def test_full_llm_int8(sq, orc):
     y = orc.dequant_sampled(acc_r, xs_r, ws_r, 0, None, r, cc)
     side = orc.side_product_sampled(X, W16, ref_idx, r, cc)
     assert_close(Y[r, cc], orc.combine_to_half(y, side), 1e-2)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm with the smoothing folded in + per-token quantization
+# ("SmoothQuant量化实战", sections 2.3, 4.2, 4.5)
+# ---------------------------------------------------------------------------
+def gpu_fold(sq, gamma, beta, s):
+    K = gamma.size
+    go = Guarded((K,), torch.float32)
+    bo = None if beta is None else Guarded((K,), torch.float32)
+    sq.sq_fold_smoothing_layernorm(dev(gamma), None if beta is None else dev(beta), dev(s), go.t,
+                                   None if bo is None else bo.t)
+    torch.cuda.synchronize()
+    return go.np(), None if bo is None else bo.np()
+
+
+def gpu_ln_quant(sq, X, gamma, beta, eps):
+    M, K = X.shape
+    Xq = Guarded((M, K), torch.int8)
+    xs = Guarded((M,), torch.float32)
+    sq.sq_layernorm_quantize_per_token(dev(X), dev(gamma), None if beta is None else dev(beta), eps, Xq.t, xs.t)
+    torch.cuda.synchronize()
+    return Xq.np(), xs.np()
+
+
+def _ln_case(seed, M, K):
+    r = np.random.default_rng(seed)
+    X = (r.standard_normal((M, K)) * r.uniform(0.1, 30.0, (M, 1)) + r.standard_normal((M, 1)) * 5.0)
+    X[:, r.choice(K, max(1, K // 200), replace=False)] *= 40.0          # outlier channels
+    X = np.clip(X, -65504, 65504).astype(np.float16)
+    g = r.uniform(0.2, 3.0, K).astype(np.float32)
+    b = (r.standard_normal(K) * 0.2).astype(np.float32)
+    s = r.uniform(0.05, 40.0, K).astype(np.float32)
+    return X, g, b, s
+
+
+LN_CASES = [
+    # M, K   (K <= 8192: one 16-byte chunk per thread; <= 16384: two; longer: three passes per row)
+    (1, 16), (3, 64), (7, 1040), (33, 4096), (300, 4112), (64, 8192), (17, 12304), (16, 16384),
+    (5, 20480), (2, 131056), (1000, 256),
+]
+
+
+@pytest.mark.parametrize("M,K", LN_CASES)
+@pytest.mark.parametrize("with_beta", [True, False])
+def test_layernorm_quantize(sq, orc, M, K, with_beta):
+    X, g, b, s = _ln_case(M * 7 + K, M, K)
+    b = b if with_beta else None
+    go, bo = gpu_fold(sq, g, b, s)
+    go_r, bo_r = orc.fold_layernorm(g, b, s)
+    assert_bits_equal(go, go_r, "gamma'")
+    if with_beta:
+        assert_bits_equal(bo, bo_r, "beta'")
+    Xq, xs = gpu_ln_quant(sq, X, go_r, bo_r, 1e-5)
+    Xq_r, xs_r = orc.layernorm_quantize(X, go_r, bo_r, 1e-5)
+    assert_bits_equal(xs, xs_r, "x_scale")
+    assert_bits_equal(Xq, Xq_r, "Xq")
+
+
+def test_layernorm_quantize_special_rows(sq, orc):
+    """Constant, zero and symmetric rows; binary16 extremes (65504, subnormals) whose
+    sums need the full 128-bit range; a row with a single non-zero value."""
+    K = 16384
+    X = np.zeros((9, K), np.float16)
+    X[0] = np.float16(3.25)                                   # var = 0
+    X[1] = np.float16(0.0)                                    # all zero
+    X[2, ::2], X[2, 1::2] = np.float16(-7.0), np.float16(7.0)
+    X[3] = np.float16(65504.0)
+    X[3, ::3] = np.float16(-65504.0)                          # S2 ~ 2^94: the 128-bit path
+    X[4] = np.float16(6e-8)                                   # smallest subnormal
+    X[4, 1::2] = np.float16(-1.2e-7)
+    X[5, 17] = np.float16(1.0)                                # one spike
+    r = np.random.default_rng(5)
+    X[6] = (r.standard_normal(K) * 60000 / 4).clip(-65504, 65504).astype(np.float16)
+    X[7] = np.float16(-0.0)
+    X[8] = (r.standard_normal(K) * 1e-4).astype(np.float16)   # mostly subnormal-range values
+    g = r.uniform(0.5, 2.0, K).astype(np.float32)
+    for b in (None, (r.standard_normal(K) * 0.3).astype(np.float32)):
+        for eps in (1e-5, 1e-12, 0.5):
+            Xq, xs = gpu_ln_quant(sq, X, g, b, eps)
+            Xq_r, xs_r = orc.layernorm_quantize(X, g, b, eps)
+            assert_bits_equal(xs, xs_r, f"x_scale eps={eps}")
+            assert_bits_equal(Xq, Xq_r, f"Xq eps={eps}")
+    # the zero row without beta: scale 0, all codes 0
+    Xq, xs = gpu_ln_quant(sq, X[1:2], g, None, 1e-5)
+    assert xs[0] == 0.0 and not Xq.any()
+
+
+def test_layernorm_quantize_prefill_7b(sq, orc):
+    """The 7B prefill activation (2048 x 4096 fp16, outlier channels) with the
+    workload's own smoothing vector folded into a LayerNorm, full size."""
+    wl = workloads.prefill_7b(which=("qkv",))
+    X, W = wl.X, wl.weights["qkv"]
+    K = X.shape[1]
+    _, s = orc.smooth_scales(wl.calib, W, wl.alpha)
+    r = np.random.default_rng(21)
+    g = r.uniform(0.5, 1.5, K).astype(np.float32)
+    b = (r.standard_normal(K) * 0.05).astype(np.float32)
+    go, bo = gpu_fold(sq, g, b, s)
+    go_r, bo_r = orc.fold_layernorm(g, b, s)
+    assert_bits_equal(go, go_r, "gamma'")
+    assert_bits_equal(bo, bo_r, "beta'")
+    Xq, xs = gpu_ln_quant(sq, X, go_r, bo_r, 1e-5)
+    Xq_r, xs_r = orc.layernorm_quantize(X, go_r, bo_r, 1e-5)
+    assert_bits_equal(xs, xs_r, "x_scale")
+    assert_bits_equal(Xq, Xq_r, "Xq")
+
+
+def test_layernorm_quantize_deterministic(sq):
+    X, g, b, _ = _ln_case(3, 640, 4096)
+    outs = [gpu_ln_quant(sq, X, g, b, 1e-5) for _ in range(3)]
+    for q, x in outs[1:]:
+        assert_bits_equal(q, outs[0][0], "Xq repeat")
+        assert_bits_equal(x, outs[0][1], "x_scale repeat")
