@@ -194,6 +194,30 @@ def bench_llm_int8(torch, sq, d, wl, steps, warmup):
                 n_outliers=int(cnt.item()))
 
 
+def bench_layernorm_quant(torch, sq, d, wl, steps, warmup):
+    """LayerNorm with the smoothing folded into its weights, fused with per-token
+    quantization, on the prefill activation (HBM-bound: 2 B read + 1 B written per
+    element); the unfused smoothing + quantization step it replaces is timed beside it."""
+    M, K = wl.X.shape
+    X = d(wl.X)
+    r = np.random.default_rng(3)
+    g = d(r.uniform(0.5, 1.5, K).astype(np.float32))
+    b = d((r.standard_normal(K) * 0.05).astype(np.float32))
+    s = d(r.uniform(0.1, 10.0, K).astype(np.float32))
+    g2, b2 = torch.empty_like(g), torch.empty_like(b)
+    sq.sq_fold_smoothing_layernorm(g, b, s, g2, b2)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    fused_ms, _ = time_steps(torch, lambda t: sq.sq_layernorm_quantize_per_token(X, g2, b2, 1e-5, Xq, xs),
+                             steps, warmup, kernel_events=False)
+    unfused_ms, _ = time_steps(torch, lambda t: sq.sq_quantize_per_token(X, s, Xq, xs), steps, warmup,
+                               kernel_events=False)
+    nbytes = 2 * M * K + M * K + 4 * M + 8 * K
+    return dict(M=M, K=K, us=fused_ms * 1e3, GBps=nbytes / (fused_ms * 1e-3) / 1e9,
+                hbm_frac=nbytes / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                smooth_quant_us=unfused_ms * 1e3)
+
+
 def cpu_baseline(wl, target_s):
     """The oracle on the same per-token work (quantize + int8 GEMM + dequant +
     fp16 store, every projection) for a bounded number of token rows."""
@@ -229,7 +253,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", default=None, help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b")
+    ap.add_argument("--only", default=None,
+                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -294,6 +319,10 @@ def main():
         if args.only in (None, "llm_int8"):
             log("llm_int8: generating inputs")
             secondary["llm_int8"] = bench_llm_int8(torch, sq, d, workloads.llm_int8_4096(), sec_steps, sec_warm)
+        if args.only in (None, "layernorm_quant"):
+            log("layernorm_quant: prefill activation")
+            secondary["layernorm_quant_7b"] = bench_layernorm_quant(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
+                                                                    sec_steps * 4, sec_warm)
         if args.only in (None, "slice_530b"):
             log("slice_530b: generating inputs")
             wl5 = workloads.slice_530b()

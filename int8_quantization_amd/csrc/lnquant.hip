@@ -36,33 +36,57 @@ __device__ __forceinline__ void lds_sync() {
     asm volatile("" ::: "memory");
 }
 
-// Integer partial sums of one thread: S1 = sum n; with |n| = a * 2^20 + b
-// (a, b < 2^20), S2 = sum n^2 = A * 2^40 + 2B * 2^20 + C, A = sum a^2,
-// B = sum a*b, C = sum b^2; every partial fits 64 bits for K <= 2^17.
+// Partial sums of one thread.  S1 = sum n: every n is an integer below 2^40 and a
+// thread adds at most 128 of them, so the fp64 sum of x * 2^24 (one FMA per value)
+// stays an integer below 2^53 and is exact; it goes to int64 before the cross-lane
+// reduction.  S2 = sum n^2 as a 128-bit (hi, lo) pair: with significand f (11
+// bits, implicit bit included) and exponent e, n = f << (e - 1) and
+// n^2 = f^2 << (2e - 2), f^2 < 2^22 (a 24-bit multiply): one shift and a carry add.
 struct Sums {
     int64_t s1;
-    uint64_t a, b, c;
+    uint64_t lo, hi;
 };
 
-__device__ __forceinline__ void add_half(Sums& t, uint16_t h) {
+struct Acc {
+    double s1;
+    uint64_t lo, hi;
+};
+
+__device__ __forceinline__ void add_half(Acc& t, uint16_t h, float x) {
+    t.s1 = __builtin_fma((double)x, 0x1p24, t.s1);
     const uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
-    const uint64_t u = e ? (uint64_t)(1024u + m) << (e - 1) : (uint64_t)m;   // |n|
-    t.s1 += (h & 0x8000u) ? -(int64_t)u : (int64_t)u;
-    const uint32_t hi = (uint32_t)(u >> 20), lo = (uint32_t)u & 0xfffffu;
-    t.a += (uint64_t)hi * hi;
-    t.b += (uint64_t)hi * lo;
-    t.c += (uint64_t)lo * lo;
+    const uint32_t f = e ? 1024u + m : m;
+    const uint32_t s2 = e ? 2 * e - 2 : 0;                     // n^2 = f^2 << s2, s2 <= 58
+    const uint64_t f2 = (uint64_t)(f * f);                     // < 2^22 (a 24-bit multiply)
+    const uint64_t add_lo = f2 << s2;
+    const uint64_t add_hi = s2 ? f2 >> (64 - s2) : 0;
+    const uint64_t lo = t.lo + add_lo;
+    t.hi += add_hi + (lo < add_lo ? 1u : 0u);
+    t.lo = lo;
+}
+
+__device__ __forceinline__ Sums to_sums(const Acc& a) {
+    return Sums{(int64_t)a.s1, a.lo, a.hi};                   // a.s1 is an exact integer
 }
 
 __device__ __forceinline__ Sums wave_sums(Sums t) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-        t.s1 += __shfl_xor(t.s1, off, 64);
-        t.a += __shfl_xor(t.a, off, 64);
-        t.b += __shfl_xor(t.b, off, 64);
-        t.c += __shfl_xor(t.c, off, 64);
+        const int64_t s1 = __shfl_xor(t.s1, off, 64);
+        const uint64_t lo = __shfl_xor(t.lo, off, 64), hi = __shfl_xor(t.hi, off, 64);
+        t.s1 += s1;
+        const uint64_t nl = t.lo + lo;
+        t.hi += hi + (nl < lo ? 1u : 0u);
+        t.lo = nl;
     }
     return t;
+}
+
+__device__ __forceinline__ void add_sums(Sums& t, const Sums& o) {
+    t.s1 += o.s1;
+    const uint64_t nl = t.lo + o.lo;
+    t.hi += o.hi + (nl < o.lo ? 1u : 0u);
+    t.lo = nl;
 }
 
 // Round-to-nearest-even conversions of exact integers: the two halves of a
@@ -83,7 +107,7 @@ __device__ __forceinline__ double u128_to_f64(unsigned __int128 v) {
 
 // Row statistics from the exact sums (same operation sequence on every thread).
 __device__ __forceinline__ void row_stats(const Sums& t, int64_t K, float eps, float& mu32, float& r32) {
-    const unsigned __int128 s2 = ((unsigned __int128)t.a << 40) + ((unsigned __int128)t.b << 21) + t.c;
+    const unsigned __int128 s2 = ((unsigned __int128)t.hi << 64) | t.lo;
     const uint64_t as1 = t.s1 < 0 ? (uint64_t)(-t.s1) : (uint64_t)t.s1;
     const unsigned __int128 v = (unsigned __int128)(uint64_t)K * s2 - (unsigned __int128)as1 * as1;
     const double d1 = t.s1 < 0 ? -u64_to_f64(as1) : u64_to_f64(as1);
@@ -101,6 +125,114 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 struct U16x8 {
     uint16_t v[8];
 };
+
+// binary16 bit pattern e (0..7) of a 16-byte chunk held as four dwords
+__device__ __forceinline__ uint16_t hbits(const v4i& c, int e) {
+    return (uint16_t)((uint32_t)c[e >> 1] >> (16 * (e & 1)));
+}
+
+// One wave per row (rows up to 8192 values): lane l holds the 16-byte chunks
+// l, l + 64, ... (CPL of them), so the two row reductions are wave shuffles and
+// the waves of a CU run independently (no block barrier after the prologue).
+// gamma' and beta' sit in LDS; the normalised values are computed twice (for the
+// row maximum, then for the codes) instead of being kept in registers.  With
+// PF, each wave loads its next row while it works on the current one.
+template <int CPL, bool BETA, bool PF>
+__global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                     const float* __restrict__ gamma,
+                                                     const float* __restrict__ beta, float eps,
+                                                     int8_t* __restrict__ Xq, float* __restrict__ scale) {
+    extern __shared__ v4f sgb[];             // gamma' [K], then beta' [K]
+    const v4f* sg = sgb;
+    const v4f* sb = sgb + K / 4;
+    for (int64_t j = threadIdx.x; j < K / 4; j += blockDim.x) {
+        sgb[j] = reinterpret_cast<const v4f*>(gamma)[j];
+        if constexpr (BETA) sgb[K / 4 + j] = reinterpret_cast<const v4f*>(beta)[j];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wpb = blockDim.x >> 6;
+    const int64_t nwv = (int64_t)gridDim.x * wpb;
+    const int nchunk = (int)(K / 8);
+    int64_t m = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6);   // uniform per wave
+    v4i cur[CPL], nxt[PF ? CPL : 1];
+    auto load = [&](int64_t row, v4i* r) {
+        const v4i* src = reinterpret_cast<const v4i*>(X + row * K);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            r[i] = (row < M && c < nchunk) ? src[c] : v4i{0, 0, 0, 0};
+        }
+    };
+    load(m, cur);
+    // y for the 8 values of chunk c (clamped into the row for the LDS reads; chunks past
+    // the row end are computed on zeros and never used)
+    auto yval = [&](const v4i& h, int c, float mu, float rs, float* y) {
+        const int cc = c < nchunk ? c : 0;
+        const v4f g0 = sg[2 * cc], g1 = sg[2 * cc + 1];
+        v4f b0{}, b1{};
+        if constexpr (BETA) {
+            b0 = sb[2 * cc];
+            b1 = sb[2 * cc + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = ((half_bits_to_float(hbits(h, e)) - mu) * rs) * (e < 4 ? g0[e] : g1[e - 4]);
+            if constexpr (BETA) v = v + (e < 4 ? b0[e] : b1[e - 4]);
+            y[e] = v;
+        }
+    };
+    for (; m < M; m += nwv) {
+        if constexpr (PF) load(m + nwv, nxt);
+        Acc ta{0.0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) add_half(ta, hbits(cur[i], e), half_bits_to_float(hbits(cur[i], e)));   // zeros add nothing
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const Sums t = wave_sums(to_sums(ta));
+        float mu, rs;
+        row_stats(t, K, eps, mu, rs);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            float y[8];
+            yval(cur[i], c, mu, rs, y);
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(y[e]));
+            amax = c < nchunk ? __builtin_fmaxf(amax, a) : amax;
+            __builtin_amdgcn_sched_barrier(0);   // one chunk's values live at a time
+        }
+        amax = wave_max(amax);
+        const float xs = amax / 127.0f;
+        if (lane == 0) scale[m] = xs;
+        const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            float y[8];
+            yval(cur[i], c, mu, rs, y);
+            int q[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of((float)((double)y[e] * rx));
+            const uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                                ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+            const uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
+                                ((uint32_t)(q[6] & 0xff) << 16) | ((uint32_t)(q[7] & 0xff) << 24);
+            if (c < nchunk) *reinterpret_cast<uint2*>(Xq + m * K + c * 8) = make_uint2(lo, hi);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) cur[i] = nxt[i];
+        } else {
+            load(m + nwv, cur);
+        }
+    }
+}
 
 // Register-resident rows: CH 16-byte chunks per thread per row.
 template <int CH, bool BETA>
@@ -150,22 +282,16 @@ __global__ __launch_bounds__(1024) void ln_quant_rows(const uint16_t* __restrict
 #pragma unroll
         for (int i = 0; i < CH; ++i) h[i] = __builtin_bit_cast(U16x8, buf[0][i]);
         // exact integer sums
-        Sums t{0, 0, 0, 0};
+        Acc ta{0.0, 0, 0};
 #pragma unroll
         for (int i = 0; i < CH; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add_half(t, h[i].v[e]);   // zeros for invalid chunks
-        t = wave_sums(t);
+            for (int e = 0; e < 8; ++e) add_half(ta, h[i].v[e], half_bits_to_float(h[i].v[e]));   // zeros for invalid chunks
+        Sums t = wave_sums(to_sums(ta));
         if (lane == 0) sred[p][wave] = t;
         lds_sync();
         Sums r = sred[p][w0];
-        for (int w = 1; w < nw; ++w) {
-            const Sums& o = sred[p][w0 + w];
-            r.s1 += o.s1;
-            r.a += o.a;
-            r.b += o.b;
-            r.c += o.c;
-        }
+        for (int w = 1; w < nw; ++w) add_sums(r, sred[p][w0 + w]);
         float mu, rs;
         row_stats(r, K, eps, mu, rs);
         // normalise, scale, shift; row maximum
@@ -195,7 +321,7 @@ __global__ __launch_bounds__(1024) void ln_quant_rows(const uint16_t* __restrict
                 if (!valid[i]) continue;
                 int q[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of(div_rcp64(y[i][e], rx, xs));
+                for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of((float)((double)y[i][e] * rx));
                 const uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
                                     ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
                 const uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
@@ -220,23 +346,22 @@ __global__ __launch_bounds__(1024) void ln_quant_long(const uint16_t* __restrict
     const int64_t nchunk = K / 8;
     for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
         const v4i* src = reinterpret_cast<const v4i*>(X + m * K);
-        Sums t{0, 0, 0, 0};
-        for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
-            const U16x8 h = __builtin_bit_cast(U16x8, src[c]);
+        Sums t{0, 0, 0};
+        for (int64_t c0 = threadIdx.x; c0 < nchunk; c0 += 16 * (int64_t)blockDim.x) {
+            Acc ta{0.0, 0, 0};                 // at most 128 values per fp64 partial sum
+            for (int64_t c = c0; c < nchunk && c < c0 + 16 * (int64_t)blockDim.x; c += blockDim.x) {
+                const U16x8 h = __builtin_bit_cast(U16x8, src[c]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add_half(t, h.v[e]);
+                for (int e = 0; e < 8; ++e) add_half(ta, h.v[e], half_bits_to_float(h.v[e]));
+            }
+            add_sums(t, to_sums(ta));
         }
         t = wave_sums(t);
         __syncthreads();                      // the previous row is done with sred/fred
         if (lane == 0) sred[wave] = t;
         __syncthreads();
         Sums r = sred[0];
-        for (int w = 1; w < nw; ++w) {
-            r.s1 += sred[w].s1;
-            r.a += sred[w].a;
-            r.b += sred[w].b;
-            r.c += sred[w].c;
-        }
+        for (int w = 1; w < nw; ++w) add_sums(r, sred[w]);
         float mu, rs;
         row_stats(r, K, eps, mu, rs);
         auto yval = [&](uint16_t hb, int64_t j) {
@@ -262,7 +387,7 @@ __global__ __launch_bounds__(1024) void ln_quant_long(const uint16_t* __restrict
             const U16x8 h = __builtin_bit_cast(U16x8, src[c]);
             int q[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of(div_rcp64(yval(h.v[e], c * 8 + e), rx, xs));
+            for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of((float)((double)yval(h.v[e], c * 8 + e) * rx));
             const uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
                                 ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
             const uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
@@ -294,10 +419,29 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const float* gam
     return hipGetLastError();
 }
 
+template <int CPL, bool BETA, bool PF>
+hipError_t launch_wave(const uint16_t* X, int64_t M, int64_t K, const float* gamma, const float* beta, float eps,
+                       int8_t* Xq, float* scale, hipStream_t st) {
+    constexpr int kWaves = 4;                                          // rows in flight per block
+    const int64_t blocks = (M + kWaves - 1) / kWaves;
+    const int64_t cap = (int64_t)dev_info().cus * 8;
+    const size_t lds = (size_t)K * sizeof(float) * (BETA ? 2 : 1);
+    hipLaunchKernelGGL((ln_quant_wave<CPL, BETA, PF>), dim3((unsigned)(blocks < cap ? blocks : cap)),
+                       dim3(64 * kWaves), lds, st, X, M, K, gamma, beta, eps, Xq, scale);
+    return hipGetLastError();
+}
+
 template <bool BETA>
 hipError_t launch_ln(const uint16_t* X, int64_t M, int64_t K, const float* gamma, const float* beta, float eps,
                      int8_t* Xq, float* scale, hipStream_t st) {
-    if (K <= 8192) return launch_rows<1, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    // few rows: spread each row over a group of threads (up to 1024) instead of one wave
+    if (K <= 8192 && M < 4 * (int64_t)dev_info().cus)
+        return launch_rows<1, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 512) return launch_wave<1, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 1024) return launch_wave<2, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 2048) return launch_wave<4, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 4096) return launch_wave<8, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 8192) return launch_wave<16, BETA, false>(X, M, K, gamma, beta, eps, Xq, scale, st);
     if (K <= 16384) return launch_rows<2, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
     const int64_t cap = (int64_t)dev_info().cus * 2;
     hipLaunchKernelGGL((ln_quant_long<BETA>), dim3((unsigned)(M < cap ? M : cap)), dim3(1024), 0, st, X, M, K,
