@@ -167,8 +167,9 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
     load(m, cur);
     // y for the 8 values of chunk c (clamped into the row for the LDS reads; chunks past
     // the row end are computed on zeros and never used)
+    uint32_t lbase = 0;                       // LDS offset, re-read per row (see below)
     auto yval = [&](const v4i& h, int c, float mu, float rs, float* y) {
-        const int cc = c < nchunk ? c : 0;
+        const int cc = (c < nchunk ? c : 0) + (int)lbase;
         const v4f g0 = sg[2 * cc], g1 = sg[2 * cc + 1];
         v4f b0{}, b1{};
         if constexpr (BETA) {
@@ -183,6 +184,9 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
         }
     };
     for (; m < M; m += nwv) {
+        // an opaque zero: keeps the compiler from hoisting every gamma'/beta' read out of
+        // the row loop into registers (which would cost the occupancy that hides latency)
+        asm volatile("" : "+s"(lbase));
         if constexpr (PF) load(m + nwv, nxt);
         Acc ta{0.0, 0, 0};
 #pragma unroll
@@ -194,11 +198,13 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
         const Sums t = wave_sums(to_sums(ta));
         float mu, rs;
         row_stats(t, K, eps, mu, rs);
+        constexpr bool KEEP = CPL <= 8;           // keep y in registers for the code pass
+        float yk[KEEP ? CPL : 1][8];
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            float y[8];
+            float* y = yk[KEEP ? i : 0];
             yval(cur[i], c, mu, rs, y);
             float a = 0.0f;
 #pragma unroll
@@ -213,8 +219,8 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            float y[8];
-            yval(cur[i], c, mu, rs, y);
+            float* y = yk[KEEP ? i : 0];
+            if (!KEEP) yval(cur[i], c, mu, rs, y);
             int q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of((float)((double)y[e] * rx));
