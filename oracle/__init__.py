@@ -50,6 +50,10 @@ def _load():
         "orc_layernorm": (None, [P, I64, I64, P, P, F, P]),
         "orc_layernorm_quantize": (None, [P, I64, I64, P, P, F, P, P]),
         "orc_fold_layernorm": (None, [P, P, P, I64, P, P]),
+        "orc_percentile_rank": (I64, [I64, D]),
+        "orc_abs_percentile": (F, [P, I, I64, I64, P, D]),
+        "orc_static_scale": (F, [P, I, I64, I64, P, D]),
+        "orc_quantize_static": (None, [P, I, I64, I64, P, F, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -307,3 +311,35 @@ def layernorm_quantize(X16, gamma, beta, eps):
     xs = np.empty(M, np.float32)
     _load().orc_layernorm_quantize(_ptr(h), M, K, _ptr(g), _ptr(b), float(eps), _ptr(Xq), _ptr(xs))
     return Xq, xs
+
+
+# ---------------------------------------------------------------------------
+# Static per-tensor activation scale (basics notes, 静态量化; the percentile
+# calibrator of the deployment page): nearest-rank percentile of |x'| over the
+# calibration batch, scale = fl32(T / 127), then quantization with that scale.
+# ---------------------------------------------------------------------------
+def percentile_rank(n, p):
+    return int(_load().orc_percentile_rank(int(n), float(p)))
+
+
+def abs_percentile(X, s, p):
+    Xc, dt = _fp(X)
+    M, K = Xc.shape
+    sv = None if s is None else _as(s, np.float32)
+    return np.float32(_load().orc_abs_percentile(_ptr(Xc), dt, M, K, _ptr(sv), float(p)))
+
+
+def static_scale(X, s, p):
+    Xc, dt = _fp(X)
+    M, K = Xc.shape
+    sv = None if s is None else _as(s, np.float32)
+    return np.float32(_load().orc_static_scale(_ptr(Xc), dt, M, K, _ptr(sv), float(p)))
+
+
+def quantize_static(X, s, xs):
+    Xc, dt = _fp(X)
+    M, K = Xc.shape
+    sv = None if s is None else _as(s, np.float32)
+    Xq = np.empty((M, K), np.int8)
+    _load().orc_quantize_static(_ptr(Xc), dt, M, K, _ptr(sv), float(np.float32(xs)), _ptr(Xq))
+    return Xq

@@ -457,3 +457,62 @@ void orc_fold_layernorm(const float* gamma, const float* beta, const float* s, i
         if (beta) beta_out[j] = beta[j] / s[j];
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Static per-tensor activation scale from calibration data, and        */
+/* quantization with it (basics notes, 静态量化: activation ranges are  */
+/* precomputed on a calibration set; the deployment page's calibrator  */
+/* takes a percentile (99.99) of the activation distribution).          */
+/*                                                                      */
+/* Reading: the statistic is the nearest-rank percentile of |x'| over   */
+/* every calibration element, x' = fl32(x / s_j) (or x without s): the  */
+/* value at 1-based rank r = ceil(p * n / 100) (fp64 expression,        */
+/* clamped to [1, n]) in ascending order, so p = 100 is the maximum.    */
+/* The scale is fl32(T / 127); quantizing divides by it and clamps, so  */
+/* values beyond T saturate at 127 / -128.                              */
+/* ------------------------------------------------------------------ */
+static int cmp_float(const void* a, const void* b)
+{
+    float x = *(const float*)a, y = *(const float*)b;
+    return (x > y) - (x < y);
+}
+
+int64_t orc_percentile_rank(int64_t n, double p)
+{
+    int64_t r = (int64_t)ceil(p * (double)n / 100.0);
+    if (r < 1) r = 1;
+    if (r > n) r = n;
+    return r;
+}
+
+float orc_abs_percentile(const void* X, int dt, int64_t M, int64_t K, const float* s, double p)
+{
+    int64_t n = M * K;
+    float* v = (float*)malloc((size_t)n * sizeof(float));
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; ++j) {
+            float x = load_elem(X, dt, m * K + j);
+            if (s) x = x / s[j];
+            v[m * K + j] = fabsf(x);
+        }
+    qsort(v, (size_t)n, sizeof(float), cmp_float);
+    float t = v[orc_percentile_rank(n, p) - 1];
+    free(v);
+    return t;
+}
+
+float orc_static_scale(const void* X, int dt, int64_t M, int64_t K, const float* s, double p)
+{
+    return orc_abs_percentile(X, dt, M, K, s, p) / 127.0f;
+}
+
+void orc_quantize_static(const void* X, int dt, int64_t M, int64_t K, const float* s, float xs, int8_t* Xq)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; ++j) {
+            float x = load_elem(X, dt, m * K + j);
+            if (s) x = x / s[j];
+            Xq[m * K + j] = xs == 0.0f ? 0 : quant_code(x / xs);
+        }
+}

@@ -606,3 +606,63 @@ def test_layernorm_workload_shape_vs_fp64(orc):
                                          weight=torch.from_numpy(g.astype(np.float64)),
                                          bias=torch.from_numpy(b.astype(np.float64)), eps=1e-5).numpy() / s
     assert np.abs(y - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+# --------------------------------------------------------------------------
+# Static per-tensor activation scale (basics notes, 静态量化; the percentile
+# calibrator of the deployment page).  Nearest-rank percentile of |x'|.
+# --------------------------------------------------------------------------
+
+def test_percentile_is_numpy_inverted_cdf(orc):
+    """The nearest-rank percentile is numpy's 'inverted_cdf' method; p = 100 is the max."""
+    r = np.random.default_rng(31)
+    X = (r.standard_normal((96, 160)) * 3).astype(np.float16)
+    X[:, 5] = np.float16(7.0)                                  # many ties
+    s = r.uniform(0.2, 5.0, 160).astype(np.float32)
+    for sv in (None, s):
+        a = np.abs(X.astype(np.float32) if sv is None else X.astype(np.float32) / sv[None, :]).ravel()
+        for p in (0.5, 10.0, 50.0, 90.0, 99.0, 99.9, 99.99, 100.0):
+            ref = np.percentile(a, p, method="inverted_cdf")
+            assert orc.abs_percentile(X, sv, p) == np.float32(ref), (p, sv is None)
+        assert orc.abs_percentile(X, sv, 100.0) == a.max()
+    assert orc.percentile_rank(10, 100.0) == 10 and orc.percentile_rank(10, 0.001) == 1
+    assert orc.percentile_rank(10000, 99.99) == 9999
+
+
+def test_static_scale_closed_form(orc):
+    X = np.arange(1, 101, dtype=np.float32).reshape(10, 10)
+    assert orc.abs_percentile(X, None, 50.0) == 50.0
+    assert orc.abs_percentile(X, None, 99.0) == 99.0
+    assert orc.static_scale(X, None, 100.0) == np.float32(np.float32(100.0) / np.float32(127.0))
+    assert orc.static_scale(np.zeros((3, 16), np.float32), None, 99.9) == 0.0
+
+
+def test_static_quantize_with_row_scale_is_per_token(orc):
+    """Quantizing a row with its own dynamic scale as the static one reproduces the
+    (pinned) per-token quantizer exactly, with and without smoothing."""
+    r = np.random.default_rng(32)
+    X = (r.standard_normal((12, 272)) * 5).astype(np.float16)
+    s = r.uniform(0.1, 9.0, 272).astype(np.float32)
+    for sv in (None, s):
+        q_dyn, xs_dyn = orc.quantize_per_token(X, sv)
+        for m in range(X.shape[0]):
+            q = orc.quantize_static(X[m:m + 1], sv, xs_dyn[m])
+            assert np.array_equal(q[0], q_dyn[m])
+
+
+def test_static_quantize_saturates_and_bounds(orc):
+    """Beyond the calibrated threshold codes saturate at 127 / -128; inside it the
+    round trip is within half a step."""
+    r = np.random.default_rng(33)
+    X = (r.standard_normal((64, 512)) * 2).astype(np.float32)
+    xs = orc.static_scale(X, None, 99.0)
+    T = xs * np.float32(127.0)
+    q = orc.quantize_static(X, None, xs)
+    big = X > T * 1.01
+    assert big.any() and np.all(q[big] == 127)
+    neg = X < -T * 1.02
+    assert neg.any() and np.all(q[neg] <= -127)
+    assert np.all(q[X <= -T * 128.6 / 127.0] == -128)
+    inside = np.abs(X) <= T
+    err = np.abs(X[inside].astype(np.float64) - q[inside].astype(np.float64) * float(xs))
+    assert err.max() <= float(xs) * (0.5 + 1e-6)
