@@ -64,14 +64,15 @@ typedef enum {
     SQ_ERR_SHAPE = 2,     /* M, N or K out of range, or K % 16 != 0 */
     SQ_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
     SQ_ERR_DTYPE = 4,     /* unsupported dtype or granularity code */
-    SQ_ERR_VALUE = 5,     /* alpha outside [0,1], threshold negative or NaN, eps not finite and > 0 */
+    SQ_ERR_VALUE = 5,     /* alpha outside [0,1], threshold negative or NaN, eps not finite and > 0,
+                             percentile outside (0, 100] */
     SQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than sq_workspace_size() */
     SQ_ERR_HIP = 7        /* a HIP launch or device query failed */
 } sq_status;
 
 typedef enum { SQ_F32 = 0, SQ_F16 = 1 } sq_dtype;
 typedef enum { SQ_PER_CHANNEL = 0, SQ_PER_TENSOR = 1 } sq_wgran;
-typedef enum { SQ_OP_QUANT_WEIGHT = 0, SQ_OP_OUTLIER = 1 } sq_op;
+typedef enum { SQ_OP_QUANT_WEIGHT = 0, SQ_OP_OUTLIER = 1, SQ_OP_CALIB_STATIC = 2 } sq_op;
 
 /* Static, human-readable name of a status code. */
 const char* sq_status_string(sq_status st);
@@ -80,6 +81,7 @@ const char* sq_status_string(sq_status st);
  *   SQ_OP_QUANT_WEIGHT: for sq_quantize_weight (M ignored).
  *   SQ_OP_OUTLIER:      for int8_outlier_matmul; sized for the worst case of
  *                       all K columns being outliers: (M + N) * K * 2 + 16 * K + 1024.
+ *   SQ_OP_CALIB_STATIC: for sq_calibrate_static_scale (N ignored): 8448 bytes.
  * Returns 0 for an unknown op or sizes out of range. */
 size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K);
 
@@ -204,6 +206,35 @@ sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, con
 sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K,
                                           const float* gamma, const float* beta, float eps,
                                           int8_t* Xq, float* x_scale, hipStream_t stream);
+
+/* Static per-tensor activation scale from a calibration batch (offline).
+ * [basics notes, 静态量化: activation ranges are precomputed on a calibration
+ *  set; the deployment page's calibration flow uses a percentile calibrator
+ *  (percentile 99.99) over the collected activations.]
+ *   X_cal      device, [M_cal x K] in xdt (M_cal * K < 2^32).
+ *   s          device float [K] (smoothing, x' = fl32(x / s_j)) or NULL (x' = x).
+ *   percentile in (0, 100]: T = the value at 1-based rank r = ceil(percentile * n / 100)
+ *              (fp64 expression, clamped to [1, n]) among the n = M_cal * K values |x'|
+ *              in ascending order (nearest rank; 100 gives the maximum).
+ *   x_scale    device float [1], out: fl32(T / 127).
+ *   ws         device workspace >= sq_workspace_size(SQ_OP_CALIB_STATIC, M_cal, 0, K).
+ * The rank is found by an exact radix select on the device (no host synchronization).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
+sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_cal, int64_t K,
+                                    const float* s, double percentile, float* x_scale,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Activation quantization with a static (calibrated) per-tensor scale (every forward).
+ * [basics notes, 静态量化; with the scale fixed there is no per-token maximum to take.]
+ *   X        device, [M x K] in xdt;  s device float [K] or NULL, as in sq_quantize_per_token.
+ *   x_scale  device float [1]: the calibrated scale xs (e.g. from sq_calibrate_static_scale).
+ *   Xq       device int8 [M x K], out: clamp(rne(fl32(x'_j / xs)), -128, 127) (0 when xs == 0);
+ *            values beyond the calibrated range saturate.
+ *   x_scale_rows  device float [M] or NULL: when given, every entry is set to xs, so the
+ *            codes feed w8a8_gemm_dequant unchanged.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
+                             const float* x_scale, int8_t* Xq, float* x_scale_rows, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
 
 SQ_F32, SQ_F16 = 0, 1
 SQ_PER_CHANNEL, SQ_PER_TENSOR = 0, 1
-SQ_OP_QUANT_WEIGHT, SQ_OP_OUTLIER = 0, 1
+SQ_OP_QUANT_WEIGHT, SQ_OP_OUTLIER, SQ_OP_CALIB_STATIC = 0, 1, 2
 
 
 class SqError(RuntimeError):
@@ -44,6 +44,8 @@ def _load():
         "int8_outlier_matmul": (I, [P, P, P, P, P, I64, I64, I64, F, P, P, SZ, P, P, P, P]),
         "sq_fold_smoothing_layernorm": (I, [P, P, P, I64, P, P, P]),
         "sq_layernorm_quantize_per_token": (I, [P, I, I64, I64, P, P, F, P, P, P]),
+        "sq_calibrate_static_scale": (I, [P, I, I64, I64, P, C.c_double, P, P, SZ, P]),
+        "sq_quantize_static": (I, [P, I, I64, I64, P, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -56,7 +58,7 @@ _lib = _load()
 
 EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quantize_per_token",
            "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
-           "sq_layernorm_quantize_per_token")
+           "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static")
 
 
 def _p(t):
@@ -152,3 +154,18 @@ def sq_layernorm_quantize_per_token(X, gamma, beta, eps, Xq, x_scale):
     M, K = X.shape
     _check("sq_layernorm_quantize_per_token", _lib.sq_layernorm_quantize_per_token(
         _p(X), _dt(X), M, K, _p(gamma), _p(beta), float(eps), _p(Xq), _p(x_scale), _stream()))
+
+
+def sq_calibrate_static_scale(X_cal, s, percentile, x_scale, ws):
+    _dense(X_cal, s, x_scale, ws)
+    M, K = X_cal.shape
+    nbytes = ws.numel() * ws.element_size()
+    _check("sq_calibrate_static_scale", _lib.sq_calibrate_static_scale(
+        _p(X_cal), _dt(X_cal), M, K, _p(s), float(percentile), _p(x_scale), _p(ws), nbytes, _stream()))
+
+
+def sq_quantize_static(X, s, x_scale, Xq, x_scale_rows=None):
+    _dense(X, s, x_scale, Xq, x_scale_rows)
+    M, K = X.shape
+    _check("sq_quantize_static", _lib.sq_quantize_static(
+        _p(X), _dt(X), M, K, _p(s), _p(x_scale), _p(Xq), _p(x_scale_rows), _stream()))

@@ -1,5 +1,7 @@
 // C ABI of libsq: argument validation on the host, then kernel launches on the
 // caller's stream.  No allocation, no host synchronization, no device-to-host copy.
+#include <math.h>
+
 #include "sq_internal.h"
 
 using namespace sq;
@@ -55,7 +57,9 @@ const char* sq_status_string(sq_status st) {
         case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: M, N >= 1 and 16 <= K <= 131056 with K % 16 == 0 are required";
         case SQ_ERR_ALIGN: return "SQ_ERR_ALIGN: pointers must be 16-byte aligned";
         case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: unsupported dtype or granularity";
-        case SQ_ERR_VALUE: return "SQ_ERR_VALUE: alpha must be in [0,1]; threshold finite and >= 0; eps finite and > 0";
+        case SQ_ERR_VALUE:
+            return "SQ_ERR_VALUE: alpha must be in [0,1]; threshold finite and >= 0; eps finite and > 0; "
+                   "percentile in (0, 100]";
         case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
         case SQ_ERR_HIP: return "SQ_ERR_HIP: a HIP launch failed";
     }
@@ -70,6 +74,10 @@ size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
     if (op == SQ_OP_OUTLIER) {
         if (bad_shape(M, N, K)) return 0;
         return outlier_layout(M, N, K).total;
+    }
+    if (op == SQ_OP_CALIB_STATIC) {
+        if (bad_shape(M, 1, K)) return 0;
+        return kStaticWorkspaceBytes;
     }
     return 0;
 }
@@ -182,6 +190,33 @@ sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M
     if (misaligned(X) || misaligned(gamma) || (beta && misaligned(beta)) || misaligned(Xq) || misaligned(x_scale))
         return SQ_ERR_ALIGN;
     return hip_status(launch_ln_quant(static_cast<const _Float16*>(X), M, K, gamma, beta, eps, Xq, x_scale, stream));
+}
+
+sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_cal, int64_t K, const float* s,
+                                    double percentile, float* x_scale, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    if (!X_cal || !x_scale) return SQ_ERR_NULL;
+    if (bad_shape(M_cal, 1, K) || (uint64_t)M_cal * (uint64_t)K >= (1ull << 32)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt)) return SQ_ERR_DTYPE;
+    if (!(percentile > 0.0 && percentile <= 100.0)) return SQ_ERR_VALUE;
+    if (!ws || ws_bytes < kStaticWorkspaceBytes) return SQ_ERR_WORKSPACE;
+    if (misaligned(X_cal) || misaligned(x_scale) || misaligned(ws) || (s && misaligned(s))) return SQ_ERR_ALIGN;
+    const int64_t n = M_cal * K;
+    int64_t r = (int64_t)ceil(percentile * (double)n / 100.0);   // nearest rank, 1-based
+    if (r < 1) r = 1;
+    if (r > n) r = n;
+    return hip_status(launch_static_calibrate(X_cal, xdt, M_cal, K, s, (uint32_t)r, x_scale, ws, stream));
+}
+
+sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, const float* x_scale,
+                             int8_t* Xq, float* x_scale_rows, hipStream_t stream) {
+    if (!X || !x_scale || !Xq) return SQ_ERR_NULL;
+    if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt)) return SQ_ERR_DTYPE;
+    if (misaligned(X) || misaligned(x_scale) || misaligned(Xq) || (s && misaligned(s)) ||
+        (x_scale_rows && misaligned(x_scale_rows)))
+        return SQ_ERR_ALIGN;
+    return hip_status(launch_static_quant(X, xdt, M, K, s, x_scale, Xq, x_scale_rows, stream));
 }
 
 }  // extern "C"

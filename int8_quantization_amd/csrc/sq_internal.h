@@ -114,6 +114,16 @@ hipError_t launch_gather_cols(const _Float16* W16, int64_t N, int64_t K, const i
 hipError_t launch_ln_quant(const _Float16* X, int64_t M, int64_t K, const float* gamma, const float* beta,
                            float eps, int8_t* Xq, float* scale, hipStream_t st);
 
+// Static per-tensor activation scale: exact nearest-rank percentile of |x'| (radix
+// select in the workspace: a 2048-bin histogram, then the selection state).
+constexpr size_t kStaticHistBytes = 2048 * 4;
+constexpr size_t kStaticWorkspaceBytes = 8448;
+hipError_t launch_static_calibrate(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, uint32_t rank,
+                                   float* x_scale, void* ws, hipStream_t st);
+// Quantization with a calibrated scale xs[0]; xs_rows (may be null) receives xs per row.
+hipError_t launch_static_quant(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, const float* xs,
+                               int8_t* Xq, float* xs_rows, hipStream_t st);
+
 // gamma_out = gamma / s, beta_out = beta / s (beta may be null).
 hipError_t launch_fold_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,
                                  float* gamma_out, float* beta_out, hipStream_t st);

@@ -35,6 +35,8 @@ def lib():
     lib.int8_outlier_matmul.argtypes = [V, V, V, V, V, I64, I64, I64, F, V, V, SZ, V, V, V, V]
     lib.sq_fold_smoothing_layernorm.argtypes = [V, V, V, I64, V, V, V]
     lib.sq_layernorm_quantize_per_token.argtypes = [V, I, I64, I64, V, V, F, V, V, V]
+    lib.sq_calibrate_static_scale.argtypes = [V, I, I64, I64, V, C.c_double, V, V, SZ, V]
+    lib.sq_quantize_static.argtypes = [V, I, I64, I64, V, V, V, V, V]
     return lib
 
 
@@ -168,3 +170,28 @@ def test_layernorm_quantize_validation(lib):
     assert f(P, 1, 4, 64, P, None, math.inf, P, P, None) == VALUE
     assert f(P, 1, 4, 64, P, MIS, 1e-5, P, P, None) == ALIGN
     assert f(P, 1, 4, 64, P, None, 1e-5, MIS, P, None) == ALIGN
+
+
+def test_static_scale_validation(lib):
+    f = lib.sq_calibrate_static_scale
+    need = lib.sq_workspace_size(2, 512, 0, 64)
+    assert need == 8448 and lib.sq_workspace_size(2, 512, 0, 60) == 0
+    assert f(None, 1, 512, 64, None, 99.9, P, P, need, None) == NULL
+    assert f(P, 1, 512, 64, None, 99.9, None, P, need, None) == NULL
+    assert f(P, 1, 512, 48 + 8, None, 99.9, P, P, need, None) == SHAPE
+    assert f(P, 1, 1 << 27, 64, None, 99.9, P, P, need, None) == SHAPE      # M*K >= 2^32
+    assert f(P, 4, 512, 64, None, 99.9, P, P, need, None) == DTYPE
+    for bad in (0.0, -1.0, 100.5, math.nan):
+        assert f(P, 1, 512, 64, None, bad, P, P, need, None) == VALUE
+    assert f(P, 1, 512, 64, None, 99.9, P, None, need, None) == WORKSPACE
+    assert f(P, 1, 512, 64, None, 99.9, P, P, need - 1, None) == WORKSPACE
+    assert f(P, 1, 512, 64, MIS, 99.9, P, P, need, None) == ALIGN
+    assert f(P, 1, 512, 64, None, 99.9, P, MIS, need, None) == ALIGN
+    g = lib.sq_quantize_static
+    assert g(None, 1, 4, 64, None, P, P, None, None) == NULL
+    assert g(P, 1, 4, 64, None, None, P, None, None) == NULL
+    assert g(P, 1, 4, 64, None, P, None, None, None) == NULL
+    assert g(P, 1, 0, 64, None, P, P, None, None) == SHAPE
+    assert g(P, 1, 4, 50, None, P, P, None, None) == SHAPE
+    assert g(P, 3, 4, 64, None, P, P, None, None) == DTYPE
+    assert g(P, 1, 4, 64, None, P, P, MIS, None) == ALIGN

@@ -497,3 +497,98 @@ def test_layernorm_quantize_deterministic(sq):
     for q, x in outs[1:]:
         assert_bits_equal(q, outs[0][0], "Xq repeat")
         assert_bits_equal(x, outs[0][1], "x_scale repeat")
+
+
+# ---------------------------------------------------------------------------
+# Static per-tensor activation scale (basics notes, 静态量化; percentile
+# calibration) and quantization with it
+# ---------------------------------------------------------------------------
+def gpu_calibrate_static(sq, X, s, p):
+    M, K = X.shape
+    xs = Guarded((1,), torch.float32, fill=-1.0)
+    ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_CALIB_STATIC, M, 0, K), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)   # the workspace starts as garbage on purpose
+    sq.sq_calibrate_static_scale(dev(X), None if s is None else dev(s), p, xs.t, ws)
+    torch.cuda.synchronize()
+    return xs.np()[0]
+
+
+def gpu_quantize_static(sq, X, s, xs):
+    M, K = X.shape
+    Xq = Guarded((M, K), torch.int8)
+    rows = Guarded((M,), torch.float32, fill=-3.0)
+    sq.sq_quantize_static(dev(X), None if s is None else dev(s), dev(np.array([xs], np.float32)), Xq.t, rows.t)
+    torch.cuda.synchronize()
+    return Xq.np(), rows.np()
+
+
+STATIC_CASES = [
+    # M, K, dtype, smooth
+    (1, 16, np.float32, False), (7, 48, np.float16, True), (512, 8192, np.float16, True),
+    (300, 4112, np.float16, False), (64, 1040, np.float32, True), (3, 131056, np.float16, True),
+    (4100, 272, np.float16, True),
+]
+
+
+@pytest.mark.parametrize("M,K,dt,smooth", STATIC_CASES)
+@pytest.mark.parametrize("p", [100.0, 99.99, 50.0])
+def test_static_calibrate(sq, orc, M, K, dt, smooth, p):
+    r = np.random.default_rng(M + K)
+    X = (r.standard_normal((M, K)) * r.uniform(0.5, 4.0, (M, 1))).astype(dt)
+    X[:, r.choice(K, max(1, K // 300), replace=False)] *= 30.0        # outlier channels
+    X[0, : min(K, 40)] = dt(2.5)                                       # ties
+    s = r.uniform(0.1, 10.0, K).astype(np.float32) if smooth else None
+    xs = gpu_calibrate_static(sq, X, s, p)
+    assert_bits_equal(np.array([xs]), np.array([orc.static_scale(X, s, p)]), f"static scale p={p}")
+
+
+def test_static_calibrate_special(sq, orc):
+    K = 64
+    Z = np.zeros((8, K), np.float16)
+    assert gpu_calibrate_static(sq, Z, None, 99.9) == 0.0
+    X = np.abs(np.random.default_rng(4).standard_normal((5, K))).astype(np.float32) + 1.0
+    for p in (1e-6, 0.5, 100.0):     # rank 1 (the minimum), low rank, the maximum
+        assert_bits_equal(np.array([gpu_calibrate_static(sq, X, None, p)]), np.array([orc.static_scale(X, None, p)]),
+                          f"p={p}")
+    Xs = X.copy()
+    Xs[2, 7] = np.float32(1.1754944e-38 * 0.25)                       # a subnormal |x'|
+    Xs[3, 3] = np.float32(0.0)
+    assert_bits_equal(np.array([gpu_calibrate_static(sq, Xs, None, 1e-6)]),
+                      np.array([orc.static_scale(Xs, None, 1e-6)]), "subnormal minimum")
+
+
+@pytest.mark.parametrize("M,K,dt,smooth", STATIC_CASES)
+def test_static_quantize(sq, orc, M, K, dt, smooth):
+    r = np.random.default_rng(2 * M + K)
+    X = (r.standard_normal((M, K)) * 3.0).astype(dt)
+    s = r.uniform(0.1, 10.0, K).astype(np.float32) if smooth else None
+    xs = orc.static_scale(X[: max(1, M // 2)], s, 99.0)             # calibrated on part of the data: saturation
+    Xq, rows = gpu_quantize_static(sq, X, s, xs)
+    assert_bits_equal(Xq, orc.quantize_static(X, s, xs), "static codes")
+    assert np.all(rows == xs)
+    assert (np.abs(Xq.astype(np.int32)) >= 127).any()
+    Xq0, _ = gpu_quantize_static(sq, X, s, np.float32(0.0))
+    assert not Xq0.any()
+
+
+def test_static_decode_layer(sq, orc):
+    """The decode workload with a static activation scale calibrated on its 512-token
+    batch: static quantization, then the decode GEMM, against the oracle."""
+    wl = workloads.decode_70b()
+    W = wl.weights["w"]
+    _, s = orc.smooth_scales(wl.calib, W, wl.alpha)
+    xs_cal = gpu_calibrate_static(sq, wl.calib, s, 99.99)
+    assert_bits_equal(np.array([xs_cal]), np.array([orc.static_scale(wl.calib, s, 99.99)]), "calibrated scale")
+    Wq, ws = orc.quantize_weight(W, s, 0)
+    for m in wl.decode_rows:
+        X = wl.X[:m]
+        Xq, rows = gpu_quantize_static(sq, X, s, xs_cal)
+        Xq_r = orc.quantize_static(X, s, xs_cal)
+        assert_bits_equal(Xq, Xq_r, "codes")
+        acc, Y = gpu_gemm(sq, Xq, rows, Wq, ws, 0, None, np.float16)
+        N = W.shape[0]
+        rr, cc = sample_positions(m, N, 4000)
+        acc_r = orc.gemm_i8_sampled(Xq_r, Wq, rr, cc)
+        assert_bits_equal(acc[rr, cc], acc_r, "acc (sampled)")
+        y = orc.dequant_sampled(acc_r, np.full(m, xs_cal, np.float32), ws, 0, None, rr, cc)
+        assert_bits_equal(Y[rr, cc], orc.float_to_half(y), "Y (sampled)")
