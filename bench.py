@@ -218,6 +218,54 @@ def bench_layernorm_quant(torch, sq, d, wl, steps, warmup):
                 smooth_quant_us=unfused_ms * 1e3)
 
 
+def bench_static(torch, sq, d, wl_pre, wl_dec, steps, warmup, copies=3):
+    """Static (calibrated, per-tensor) activation scale: quantization of the prefill
+    activation and the decode step (quantize + GEMV) with it, each beside its
+    per-token (dynamic) counterpart."""
+    out = {}
+    M, K = wl_pre.X.shape
+    X = d(wl_pre.X)
+    s = d(np.random.default_rng(5).uniform(0.1, 10.0, K).astype(np.float32))
+    xs1 = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_CALIB_STATIC, M, 0, K), dtype=torch.uint8, device="cuda")
+    sq.sq_calibrate_static_scale(X, s, 99.99, xs1, ws)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    rows = torch.empty(M, dtype=torch.float32, device="cuda")
+    ms, _ = time_steps(torch, lambda t: sq.sq_quantize_static(X, s, xs1, Xq, rows), steps, warmup, kernel_events=False)
+    ms_dyn, _ = time_steps(torch, lambda t: sq.sq_quantize_per_token(X, s, Xq, rows), steps, warmup,
+                           kernel_events=False)
+    nbytes = 2 * M * K + M * K + 4 * M
+    out["quantize_prefill"] = dict(M=M, K=K, us=ms * 1e3, GBps=nbytes / (ms * 1e-3) / 1e9,
+                                   hbm_frac=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, per_token_us=ms_dyn * 1e3)
+    # decode: calibrated on the 512-token batch, three rotated weight copies
+    W = wl_dec.weights["w"]
+    N, K = W.shape
+    sd, Wq0, wsc = prepare_weight(torch, sq, d, wl_dec.calib, W, wl_dec.alpha, wl_dec.gran)
+    cal = d(wl_dec.calib)
+    ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_CALIB_STATIC, cal.shape[0], 0, K), dtype=torch.uint8,
+                     device="cuda")
+    sq.sq_calibrate_static_scale(cal, sd, 99.99, xs1, ws)
+    Wqs = [Wq0] + [Wq0.clone() for _ in range(copies - 1)]
+    for Md in wl_dec.decode_rows:
+        Xd = d(wl_dec.X[:Md])
+        Xqd = torch.empty(Md, K, dtype=torch.int8, device="cuda")
+        rowsd = torch.empty(Md, dtype=torch.float32, device="cuda")
+        Y = torch.empty(Md, N, dtype=torch.float16, device="cuda")
+        it = [0]
+
+        def step(timer):
+            Wq = Wqs[it[0] % copies]
+            it[0] += 1
+            sq.sq_quantize_static(Xd, sd, xs1, Xqd, rowsd)
+            sq.w8a8_gemm_dequant(Xqd, rowsd, Wq, wsc, 0, None, Y)
+
+        ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
+        nb = N * K + 4 * N + 2 * Md * K + 2 * Md * N
+        out[f"decode_M{Md}"] = dict(ms_per_step=ms, GBps=nb / (ms * 1e-3) / 1e9,
+                                    hbm_frac=nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    return out
+
+
 def cpu_baseline(wl, target_s):
     """The oracle on the same per-token work (quantize + int8 GEMM + dequant +
     fp16 store, every projection) for a bounded number of token rows."""
@@ -254,7 +302,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default=None,
-                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant")
+                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant|static_quant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -323,6 +371,10 @@ def main():
             log("layernorm_quant: prefill activation")
             secondary["layernorm_quant_7b"] = bench_layernorm_quant(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
                                                                     sec_steps * 4, sec_warm)
+        if args.only in (None, "static_quant"):
+            log("static_quant: prefill activation and decode")
+            secondary["static_scale"] = bench_static(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
+                                                     workloads.decode_70b(), sec_steps * 2, sec_warm)
         if args.only in (None, "slice_530b"):
             log("slice_530b: generating inputs")
             wl5 = workloads.slice_530b()

@@ -14,6 +14,8 @@
 // Forward: q = clamp(rne(fl32(x' / scale)), -128, 127) with the one calibrated
 // scale, so there is no per-row reduction: a thread owns a 16-byte column chunk
 // (its fp64 reciprocals of s computed once) and walks down the rows.
+#include <type_traits>
+
 #include "sq_internal.h"
 
 namespace sq {
@@ -39,23 +41,32 @@ struct SelState {
     uint32_t rank;     // 1-based rank of T among the values sharing that prefix
 };
 
-// Per-thread column constants: the exact smoothing divide x / s_j.
+// Per-thread column constants: the exact smoothing divide x / s_j, as the fp64
+// reciprocal product.  A quotient can fall below the fp32 normal range (where the
+// IEEE division itself is taken) only for fp32 inputs or some s_j >= 2^100: a
+// nonzero binary16 x is at least 2^-24.  `guard` marks such threads.
 template <typename T, bool SMOOTH>
 struct Cols {
     static constexpr int N = Chunk16<T>::N;
     double rs[SMOOTH ? N : 1];
     float sv[SMOOTH ? N : 1];
+    bool guard = false;
     __device__ void init(const float* s, int64_t c) {
-        if constexpr (SMOOTH)
+        if constexpr (SMOOTH) {
 #pragma unroll
             for (int e = 0; e < N; ++e) {
                 sv[e] = s[c * N + e];
                 rs[e] = 1.0 / (double)sv[e];
+                guard = guard || !(sv[e] < 0x1p100f);
             }
+            if constexpr (sizeof(T) == 4) guard = true;
+        }
     }
+    template <bool G>
     __device__ float apply(float x, int e) const {
-        if constexpr (SMOOTH) return div_rcp64(x, rs[e], sv[e]);
-        return x;
+        if constexpr (!SMOOTH) return x;
+        else if constexpr (G) return div_rcp64(x, rs[e], sv[e]);
+        else return (float)((double)x * rs[e]);
     }
 };
 
@@ -76,23 +87,41 @@ __global__ __launch_bounds__(kThreads) void static_quant_kernel(const T* __restr
     if (c >= nchunk) return;
     Cols<T, SMOOTH> cols;
     cols.init(s, c);
-    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
-        const V v = reinterpret_cast<const V*>(X + m * K)[c];
-        int q[N];
+    // rows in batches of RB: the batch's loads are all in flight before its codes are formed
+    constexpr int RB = 4;
+    const int64_t step = gridDim.y;
+    auto rows = [&](auto guarded) {
+        for (int64_t m0 = blockIdx.y; m0 < M; m0 += RB * step) {
+            V v[RB];
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-            const float x = cols.apply((float)v[e], e);
-            // a quotient below the fp32 normal range codes to 0 either way
-            q[e] = xs == 0.0f ? 0 : code_of((float)((double)x * rx));
+            for (int r = 0; r < RB; ++r) {
+                const int64_t m = m0 + r * step;
+                v[r] = m < M ? reinterpret_cast<const V*>(X + m * K)[c] : V{};
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int64_t m = m0 + r * step;
+                int q[N];
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const float x = cols.template apply<decltype(guarded)::value>((float)v[r][e], e);
+                    // a quotient below the fp32 normal range codes to 0 either way
+                    q[e] = xs == 0.0f ? 0 : code_of((float)((double)x * rx));
+                }
+                uint32_t w[N / 4];
+#pragma unroll
+                for (int k = 0; k < N / 4; ++k)
+                    w[k] = (uint32_t)(q[4 * k] & 0xff) | ((uint32_t)(q[4 * k + 1] & 0xff) << 8) |
+                           ((uint32_t)(q[4 * k + 2] & 0xff) << 16) | ((uint32_t)(q[4 * k + 3] & 0xff) << 24);
+                if (m < M) {
+                    if constexpr (N == 8) *reinterpret_cast<uint2*>(Xq + m * K + c * N) = make_uint2(w[0], w[1]);
+                    else *reinterpret_cast<uint32_t*>(Xq + m * K + c * N) = w[0];
+                }
+            }
         }
-        uint32_t w[N / 4];
-#pragma unroll
-        for (int k = 0; k < N / 4; ++k)
-            w[k] = (uint32_t)(q[4 * k] & 0xff) | ((uint32_t)(q[4 * k + 1] & 0xff) << 8) |
-                   ((uint32_t)(q[4 * k + 2] & 0xff) << 16) | ((uint32_t)(q[4 * k + 3] & 0xff) << 24);
-        if constexpr (N == 8) *reinterpret_cast<uint2*>(Xq + m * K + c * N) = make_uint2(w[0], w[1]);
-        else *reinterpret_cast<uint32_t*>(Xq + m * K + c * N) = w[0];
-    }
+    };
+    if (cols.guard) rows(std::true_type{});
+    else rows(std::false_type{});
 }
 
 // Pass PASS of the radix select: histogram of one bit field of |x'| over the values
@@ -125,7 +154,8 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const T* __restrict__ X,
             const V v = reinterpret_cast<const V*>(X + m * K)[c];
 #pragma unroll
             for (int e = 0; e < N; ++e) {
-                const uint32_t bits = __builtin_bit_cast(uint32_t, __builtin_fabsf(cols.apply((float)v[e], e)));
+                const uint32_t bits =
+                    __builtin_bit_cast(uint32_t, __builtin_fabsf(cols.template apply<true>((float)v[e], e)));
                 if ((bits >> HI) == want) atomicAdd(&lh[(bits >> LO) & (NB - 1)], 1u);
             }
         }
@@ -186,10 +216,14 @@ __global__ void select_finish_kernel(const SelState* __restrict__ state, float* 
     if (threadIdx.x == 0) x_scale[0] = __builtin_bit_cast(float, state->prefix) / 127.0f;
 }
 
+// Up to kRowsPerThread rows per thread, but at least ~64K threads when there are
+// enough rows (few rows: one row per block row).
 dim3 grid_of(int64_t M, int64_t K, int vec) {
     const int64_t nchunk = K / vec;
     const int64_t gx = (nchunk + kThreads - 1) / kThreads;
     int64_t gy = (M + kRowsPerThread - 1) / kRowsPerThread;
+    const int64_t want = (65536 / kThreads + gx - 1) / gx;
+    if (gy < want) gy = want < M ? want : M;
     if (gy > 65535) gy = 65535;
     return dim3((unsigned)gx, (unsigned)gy);
 }
