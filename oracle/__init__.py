@@ -54,6 +54,9 @@ def _load():
         "orc_abs_percentile": (F, [P, I, I64, I64, P, D]),
         "orc_static_scale": (F, [P, I, I64, I64, P, D]),
         "orc_quantize_static": (None, [P, I, I64, I64, P, F, P]),
+        "orc_kv_calibrate_per_head": (None, [P, I, I64, I64, I64, F, P]),
+        "orc_kv_quantize_per_head": (None, [P, I, I64, I64, I64, P, P]),
+        "orc_dequantize": (None, [P, I64, I64, P, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -343,3 +346,34 @@ def quantize_static(X, s, xs):
     Xq = np.empty((M, K), np.int8)
     _load().orc_quantize_static(_ptr(Xc), dt, M, K, _ptr(sv), float(np.float32(xs)), _ptr(Xq))
     return Xq
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache with per-head scales ("SmoothQuant量化实战", section 5.2).
+# KV layout [T, H, D] (tokens, heads, head dim).
+# ---------------------------------------------------------------------------
+def kv_calibrate_per_head(KV, margin=1.0):
+    KVc, dt = _fp(KV)
+    T, H, D = KVc.shape
+    sc = np.empty(H, np.float32)
+    _load().orc_kv_calibrate_per_head(_ptr(KVc), dt, T, H, D, float(margin), _ptr(sc))
+    return sc
+
+
+def kv_quantize_per_head(KV, scale):
+    KVc, dt = _fp(KV)
+    T, H, D = KVc.shape
+    sc = _as(scale, np.float32)
+    q = np.empty((T, H, D), np.int8)
+    _load().orc_kv_quantize_per_head(_ptr(KVc), dt, T, H, D, _ptr(sc), _ptr(q))
+    return q
+
+
+def dequantize(q, scale, row_stride, group):
+    """y[m, j] = fl32(q[m, j] * scale[m * row_stride + j // group]) (fp32)."""
+    qc = np.ascontiguousarray(q, np.int8)
+    M, K = qc.shape
+    sc = _as(scale, np.float32)
+    y = np.empty((M, K), np.float32)
+    _load().orc_dequantize(_ptr(qc), M, K, _ptr(sc), int(row_stride), int(group), _ptr(y))
+    return y

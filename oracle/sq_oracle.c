@@ -516,3 +516,52 @@ void orc_quantize_static(const void* X, int dt, int64_t M, int64_t K, const floa
             Xq[m * K + j] = xs == 0.0f ? 0 : quant_code(x / xs);
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* INT8 KV cache with per-head scales (SmoothQuant page, section 5.2:  */
+/* the KV cache is quantized to INT8 with one scale per head, since the */
+/* heads' distributions differ; as the cache grows, a scale from the    */
+/* calibration stage with a safety factor avoids recomputing it).       */
+/*                                                                      */
+/* Layout [T x H x D] row-major (tokens, heads, head dim).              */
+/*   scale_h = fl32( fl32(margin * max_{t,d} |x[t,h,d]|) / 127 )         */
+/*   q = clamp(rne(fl32(x / scale_h)), -128, 127)   (0 when scale_h = 0) */
+/* Dequantization, general: y[m,j] = fl32(q[m,j] * scale[m*rs + j/g])     */
+/* (rs = 0, g = D: per head over [T x H*D]; rs = 1, g = K: per row).     */
+/* ------------------------------------------------------------------ */
+void orc_kv_calibrate_per_head(const void* KV, int dt, int64_t T, int64_t H, int64_t D, float margin,
+                               float* scale)
+{
+    for (int64_t h = 0; h < H; ++h) {
+        float m = 0.0f;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t d = 0; d < D; ++d) {
+                float v = fabsf(load_elem(KV, dt, (t * H + h) * D + d));
+                if (v > m) m = v;
+            }
+        scale[h] = (margin * m) / 127.0f;
+    }
+}
+
+void orc_kv_quantize_per_head(const void* KV, int dt, int64_t T, int64_t H, int64_t D, const float* scale,
+                              int8_t* q)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < D; ++d) {
+                int64_t i = (t * H + h) * D + d;
+                float x = load_elem(KV, dt, i);
+                q[i] = scale[h] == 0.0f ? 0 : quant_code(x / scale[h]);
+            }
+}
+
+/* y = fl32(q * scale[m*row_stride + j/group]), fp32 out (the caller rounds to fp16) */
+void orc_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t row_stride,
+                    int64_t group, float* y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; ++j)
+            y[m * K + j] = (float)q[m * K + j] * scale[m * row_stride + j / group];
+}

@@ -666,3 +666,52 @@ def test_static_quantize_saturates_and_bounds(orc):
     inside = np.abs(X) <= T
     err = np.abs(X[inside].astype(np.float64) - q[inside].astype(np.float64) * float(xs))
     assert err.max() <= float(xs) * (0.5 + 1e-6)
+
+
+# --------------------------------------------------------------------------
+# INT8 KV cache with per-head scales ("SmoothQuant量化实战", section 5.2)
+# --------------------------------------------------------------------------
+
+def _kv(seed, T, H, D, dt=np.float16):
+    r = np.random.default_rng(seed)
+    KV = r.standard_normal((T, H, D)) * r.uniform(0.2, 8.0, (1, H, 1))    # heads differ in range
+    return KV.astype(dt)
+
+
+def test_kv_calibration_is_numpy_head_max(orc):
+    KV = _kv(41, 64, 8, 128)
+    for margin in (1.0, 1.25):
+        ref = (np.float32(margin) * np.abs(KV.astype(np.float32)).max(axis=(0, 2))) / np.float32(127.0)
+        assert np.array_equal(orc.kv_calibrate_per_head(KV, margin), ref.astype(np.float32))
+    assert not orc.kv_calibrate_per_head(np.zeros((4, 2, 16), np.float16)).any()
+
+
+def test_kv_per_head_is_static_quantization_per_head(orc):
+    """Each head is quantized exactly like a static per-tensor quantization of its
+    own [T x D] slice with its own scale (the pinned N3 quantizer)."""
+    T, H, D = 40, 4, 64
+    KV = _kv(42, T, H, D)
+    sc = orc.kv_calibrate_per_head(KV[: T // 2], 1.0)                     # later tokens can saturate
+    q = orc.kv_quantize_per_head(KV, sc)
+    for h in range(H):
+        assert np.array_equal(q[:, h, :], orc.quantize_static(KV[:, h, :], None, sc[h]))
+    assert np.abs(q.astype(np.int32)).max() >= 127
+
+
+def test_dequantize_closed_form_and_round_trip(orc):
+    T, H, D = 32, 4, 64
+    KV = _kv(43, T, H, D, np.float32)
+    sc = orc.kv_calibrate_per_head(KV, 1.0)
+    q = orc.kv_quantize_per_head(KV, sc)
+    y = orc.dequantize(q.reshape(T, H * D), sc, 0, D).reshape(T, H, D)
+    assert np.array_equal(y, q.astype(np.float32) * sc[None, :, None])    # one fp32 product
+    err = np.abs(KV.astype(np.float64) - y.astype(np.float64))
+    assert np.all(err <= sc[None, :, None].astype(np.float64) * (0.5 + 1e-6))
+    # power-of-two scales: exact
+    s2 = np.exp2(np.arange(-3, 1)).astype(np.float32)
+    y2 = orc.dequantize(q.reshape(T, H * D), s2, 0, D).reshape(T, H, D)
+    assert np.array_equal(y2, q.astype(np.float32) * s2[None, :, None])
+    # per-token-per-head (dynamic) scales: rows of D with the per-token quantizer, row-indexed dequant
+    qd, xs = orc.quantize_per_token(KV.reshape(T * H, D), None)
+    yd = orc.dequantize(qd, xs, 1, D)
+    assert np.all(np.abs(KV.reshape(T * H, D) - yd) <= xs[:, None] * (0.5 + 1e-6))
