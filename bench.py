@@ -266,6 +266,51 @@ def bench_static(torch, sq, d, wl_pre, wl_dec, steps, warmup, copies=3):
     return out
 
 
+def bench_kv_cache(torch, sq, d, steps, warmup, copies=3, batch=16):
+    """INT8 KV cache of one layer (8 KV heads x 128) for a batch of 16 sequences of
+    4096 tokens: per-head calibration on a 512-token batch, quantization of K and V
+    with the fixed scales, and the fp16 read-back.  Three rotated buffer sets keep
+    the working set beyond the on-die caches."""
+    import workloads
+    K_cal, V_cal, Kx, Vx = workloads.kv_cache()
+    T1, H, D = Kx.shape
+    T = T1 * batch
+    KV = [torch.cat([d(Kx)] * batch), torch.cat([d(Vx)] * batch)]
+    sets = [[t.clone() for t in KV] for _ in range(copies)]
+    sc = [torch.empty(H, dtype=torch.float32, device="cuda") for _ in range(2)]
+    cal = [d(K_cal), d(V_cal)]
+    for i in range(2):
+        sq.sq_kv_calibrate_per_head(cal[i], 1.2, sc[i])
+    ms_cal, _ = time_steps(torch, lambda t: sq.sq_kv_calibrate_per_head(cal[0], 1.2, sc[0]), steps, warmup,
+                           kernel_events=False)
+    q = [[torch.empty(T, H, D, dtype=torch.int8, device="cuda") for _ in range(2)] for _ in range(copies)]
+    it = [0]
+
+    def quant(timer):
+        j = it[0] % copies
+        it[0] += 1
+        for i in range(2):
+            sq.sq_kv_quantize_per_head(sets[j][i], sc[i], q[j][i])
+
+    ms_q, _ = time_steps(torch, quant, steps, warmup, kernel_events=False)
+    Y = [[torch.empty(T, H * D, dtype=torch.float16, device="cuda") for _ in range(2)] for _ in range(copies)]
+
+    def deq(timer):
+        j = it[0] % copies
+        it[0] += 1
+        for i in range(2):
+            sq.sq_dequantize(q[j][i], sc[i], 0, D, Y[j][i])
+
+    ms_d, _ = time_steps(torch, deq, steps, warmup, kernel_events=False)
+    n = 2 * T * H * D
+    qb, db = 3 * n + 8 * H, 3 * n + 8 * H
+    return dict(tokens=T, heads=H, head_dim=D, calibrate_us=ms_cal * 1e3,
+                quantize_kv=dict(us=ms_q * 1e3, GBps=qb / (ms_q * 1e-3) / 1e9,
+                                 hbm_frac=qb / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBS),
+                dequantize_kv=dict(us=ms_d * 1e3, GBps=db / (ms_d * 1e-3) / 1e9,
+                                   hbm_frac=db / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS))
+
+
 def cpu_baseline(wl, target_s):
     """The oracle on the same per-token work (quantize + int8 GEMM + dequant +
     fp16 store, every projection) for a bounded number of token rows."""
@@ -302,7 +347,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default=None,
-                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant|static_quant")
+                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant|static_quant|kv_cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -375,6 +420,10 @@ def main():
             log("static_quant: prefill activation and decode")
             secondary["static_scale"] = bench_static(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
                                                      workloads.decode_70b(), sec_steps * 2, sec_warm)
+        if args.only in (None, "kv_cache"):
+            log("kv_cache: 16 x 4096 tokens, 8 heads x 128")
+            secondary["kv_cache"] = bench_kv_cache(torch, sq, d, sec_steps * 2, sec_warm)
+            torch.cuda.empty_cache()
         if args.only in (None, "slice_530b"):
             log("slice_530b: generating inputs")
             wl5 = workloads.slice_530b()

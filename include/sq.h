@@ -236,6 +236,46 @@ sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_c
 sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
                              const float* x_scale, int8_t* Xq, float* x_scale_rows, hipStream_t stream);
 
+/* INT8 KV cache, per-head calibration (offline or at cache creation).
+ * [SmoothQuant page, section 5.2: the KV cache is stored as int8 with one scale per
+ *  attention head, the heads' ranges being different; a scale fixed from calibration
+ *  and widened by a safety factor avoids recomputing it while the cache grows.]
+ *   KV      device, [T x H x D] in dt (tokens x heads x head_dim), row-major.
+ *   T >= 1, H >= 1, 16 <= D, D % 16 == 0, H * D <= 131056.
+ *   margin  finite, > 0: the safety factor.
+ *   scale   device float [H], out: scale_h = fl32(fl32(margin * max_{t,d} |x[t,h,d]|) / 127)
+ *           (0 for a head that is all zero).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_HIP. */
+sq_status sq_kv_calibrate_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D,
+                                   float margin, float* scale, hipStream_t stream);
+
+/* INT8 KV cache, quantization with fixed per-head scales (every appended block).
+ * [SmoothQuant page, section 5.2.]
+ *   KV      device, [T x H x D] in dt; sizes as for sq_kv_calibrate_per_head.
+ *   scale   device float [H] (e.g. from sq_kv_calibrate_per_head).
+ *   q       device int8 [T x H x D], out: clamp(rne(fl32(x[t,h,d] / scale_h)), -128, 127)
+ *           (0 when scale_h == 0); values beyond the calibrated range saturate.
+ *   To append T new tokens to a cache of capacity C, pass q + t0 * H * D.
+ *   Per-token (per row and head) scales instead: sq_quantize_per_token on the
+ *   [T*H x D] view, whose row scales are the per-token-per-head scales.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status sq_kv_quantize_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D,
+                                  const float* scale, int8_t* q, hipStream_t stream);
+
+/* Dequantization of int8 codes with grouped scales (reading an INT8 KV cache back).
+ * ["量化基础与INT8", section 量化流程示例: x ~ q * scale.]
+ *   q        device int8 [M x K] (16 <= K <= 131056, K % 16 == 0).
+ *   scale    device float, 4-byte aligned; element (m, j) uses
+ *            scale[m * scale_row_stride + j / group]:
+ *              per head of a [T x H*D] cache:  scale_row_stride 0, group D;
+ *              one scale per row:              scale_row_stride 1, group K;
+ *              per token and head:             scale_row_stride K / group, group D.
+ *   group    >= 16, group % 16 == 0, K % group == 0;  0 <= scale_row_stride <= 131056.
+ *   Y        device [M x K] in ydt, out: fl32(q * scale) (rounded to nearest even for fp16).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status sq_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t scale_row_stride,
+                        int64_t group, void* Y, sq_dtype ydt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

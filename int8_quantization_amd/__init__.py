@@ -46,6 +46,9 @@ def _load():
         "sq_layernorm_quantize_per_token": (I, [P, I, I64, I64, P, P, F, P, P, P]),
         "sq_calibrate_static_scale": (I, [P, I, I64, I64, P, C.c_double, P, P, SZ, P]),
         "sq_quantize_static": (I, [P, I, I64, I64, P, P, P, P, P]),
+        "sq_kv_calibrate_per_head": (I, [P, I, I64, I64, I64, F, P, P]),
+        "sq_kv_quantize_per_head": (I, [P, I, I64, I64, I64, P, P, P]),
+        "sq_dequantize": (I, [P, I64, I64, P, I64, I64, P, I, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -58,7 +61,8 @@ _lib = _load()
 
 EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quantize_per_token",
            "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
-           "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static")
+           "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static",
+           "sq_kv_calibrate_per_head", "sq_kv_quantize_per_head", "sq_dequantize")
 
 
 def _p(t):
@@ -169,3 +173,28 @@ def sq_quantize_static(X, s, x_scale, Xq, x_scale_rows=None):
     M, K = X.shape
     _check("sq_quantize_static", _lib.sq_quantize_static(
         _p(X), _dt(X), M, K, _p(s), _p(x_scale), _p(Xq), _p(x_scale_rows), _stream()))
+
+
+def sq_kv_calibrate_per_head(KV, margin, scale):
+    """KV [T, H, D] fp16/fp32; scale [H] fp32 out."""
+    _dense(KV, scale)
+    T, H, D = KV.shape
+    _check("sq_kv_calibrate_per_head", _lib.sq_kv_calibrate_per_head(
+        _p(KV), _dt(KV), T, H, D, float(margin), _p(scale), _stream()))
+
+
+def sq_kv_quantize_per_head(KV, scale, q):
+    """KV [T, H, D] fp16/fp32; scale [H] fp32; q [T, H, D] int8 out."""
+    _dense(KV, scale, q)
+    T, H, D = KV.shape
+    _check("sq_kv_quantize_per_head", _lib.sq_kv_quantize_per_head(
+        _p(KV), _dt(KV), T, H, D, _p(scale), _p(q), _stream()))
+
+
+def sq_dequantize(q, scale, scale_row_stride, group, Y):
+    """q [M, K] int8 (or any shape whose last dimension is K); Y the same shape, fp16/fp32 out."""
+    _dense(q, Y)
+    K = q.shape[-1]
+    M = q.numel() // K
+    _check("sq_dequantize", _lib.sq_dequantize(
+        _p(q), M, K, _p(scale), int(scale_row_stride), int(group), _p(Y), _dt(Y), _stream()))

@@ -216,7 +216,37 @@ sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, 
     if (misaligned(X) || misaligned(x_scale) || misaligned(Xq) || (s && misaligned(s)) ||
         (x_scale_rows && misaligned(x_scale_rows)))
         return SQ_ERR_ALIGN;
-    return hip_status(launch_static_quant(X, xdt, M, K, s, x_scale, Xq, x_scale_rows, stream));
+    return hip_status(launch_static_quant(X, xdt, M, K, s, x_scale, K, Xq, x_scale_rows, stream));
+}
+
+sq_status sq_kv_calibrate_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, float margin,
+                                   float* scale, hipStream_t stream) {
+    if (!KV || !scale) return SQ_ERR_NULL;
+    if (H < 1 || D < 16 || (D % 16) != 0 || H > kMaxK / D || bad_shape(T, 1, H * D)) return SQ_ERR_SHAPE;
+    if (bad_dtype(dt)) return SQ_ERR_DTYPE;
+    if (!(margin > 0.0f && margin <= 3.4028235e38f)) return SQ_ERR_VALUE;
+    if (misaligned(KV) || misaligned(scale)) return SQ_ERR_ALIGN;
+    return hip_status(launch_kv_calibrate(KV, dt, T, H, D, margin, scale, stream));
+}
+
+sq_status sq_kv_quantize_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, const float* scale,
+                                  int8_t* q, hipStream_t stream) {
+    if (!KV || !scale || !q) return SQ_ERR_NULL;
+    if (H < 1 || D < 16 || (D % 16) != 0 || H > kMaxK / D || bad_shape(T, 1, H * D)) return SQ_ERR_SHAPE;
+    if (bad_dtype(dt)) return SQ_ERR_DTYPE;
+    if (misaligned(KV) || misaligned(scale) || misaligned(q)) return SQ_ERR_ALIGN;
+    return hip_status(launch_static_quant(KV, dt, T, H * D, nullptr, scale, D, q, nullptr, stream));
+}
+
+sq_status sq_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t scale_row_stride,
+                        int64_t group, void* Y, sq_dtype ydt, hipStream_t stream) {
+    if (!q || !scale || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, 1, K) || group < 16 || (group % 16) != 0 || (K % group) != 0 || scale_row_stride < 0 ||
+        scale_row_stride > kMaxK)
+        return SQ_ERR_SHAPE;
+    if (bad_dtype(ydt)) return SQ_ERR_DTYPE;
+    if (misaligned(q) || misaligned(Y) || ((uintptr_t)scale & 3u)) return SQ_ERR_ALIGN;
+    return hip_status(launch_dequantize(q, M, K, scale, scale_row_stride, group, Y, ydt, stream));
 }
 
 }  // extern "C"

@@ -63,6 +63,29 @@ const DevInfo& dev_info();
 // Fill n 32-bit words with a value (kernel, so it is safe inside stream capture).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 
+// Grid of an elementwise pass over M rows of nchunk 16-byte chunks with 256-thread
+// blocks: a block covers P = min(256, pow2 >= nchunk) chunks (grid x) of each of
+// 256 / P consecutive rows, so short rows still fill every lane; grid y walks the
+// row groups, about rows_per_thread rows per thread, but with at least min_blocks
+// blocks when there are rows for them.  Thread t of block (x, y) takes chunk
+// x * P + (t % P) of rows (y * 256/P + t / P) + k * gridDim.y * 256/P.
+struct RowPack {
+    int lgp;      // log2 P
+    dim3 grid;
+};
+inline RowPack row_pack(int64_t M, int64_t nchunk, int64_t rows_per_thread, int64_t min_blocks) {
+    int lgp = 0;
+    while (lgp < 8 && ((int64_t)1 << lgp) < nchunk) ++lgp;
+    const int64_t P = (int64_t)1 << lgp, R = 256 / P;
+    const int64_t gx = (nchunk + P - 1) / P;
+    const int64_t groups = (M + R - 1) / R;
+    int64_t gy = (groups + rows_per_thread - 1) / rows_per_thread;
+    const int64_t want = (min_blocks + gx - 1) / gx;
+    if (gy < want) gy = want < groups ? want : groups;
+    if (gy > 65535) gy = 65535;
+    return RowPack{lgp, dim3((unsigned)gx, (unsigned)gy)};
+}
+
 // Per-row smoothing + absmax quantization (activations per token, weights per channel).
 // mode 0: no smoothing; 1: x / s_j; 2: x * s_j.  pos/Xo (LLM.int8() only): pos[j] >= 0
 // marks an outlier column, whose value is copied to Xo[m*K + pos[j]] and whose code is 0.
@@ -120,9 +143,17 @@ constexpr size_t kStaticHistBytes = 2048 * 4;
 constexpr size_t kStaticWorkspaceBytes = 8448;
 hipError_t launch_static_calibrate(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, uint32_t rank,
                                    float* x_scale, void* ws, hipStream_t st);
-// Quantization with a calibrated scale xs[0]; xs_rows (may be null) receives xs per row.
+// Quantization with calibrated scales: column j uses xs[j / group]; xs_rows (may be null)
+// receives xs[0] per row.
 hipError_t launch_static_quant(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, const float* xs,
-                               int8_t* Xq, float* xs_rows, hipStream_t st);
+                               int64_t group, int8_t* Xq, float* xs_rows, hipStream_t st);
+
+// KV cache [T x H x D]: per-head calibration scale_h = fl32(fl32(margin * max|x|) / 127).
+hipError_t launch_kv_calibrate(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, float margin,
+                               float* scale, hipStream_t st);
+// y[m, j] = fl32(q[m, j] * scale[m * row_stride + j / group]), stored as ydt.
+hipError_t launch_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t row_stride,
+                             int64_t group, void* Y, sq_dtype ydt, hipStream_t st);
 
 // gamma_out = gamma / s, beta_out = beta / s (beta may be null).
 hipError_t launch_fold_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,

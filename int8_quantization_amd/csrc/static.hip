@@ -13,7 +13,8 @@
 //
 // Forward: q = clamp(rne(fl32(x' / scale)), -128, 127) with the one calibrated
 // scale, so there is no per-row reduction: a thread owns a 16-byte column chunk
-// (its fp64 reciprocals of s computed once) and walks down the rows.
+// (its fp64 reciprocals of s computed once) and walks down the rows; short rows
+// are packed several to a block.
 #include <type_traits>
 
 #include "sq_internal.h"
@@ -70,28 +71,32 @@ struct Cols {
     }
 };
 
+// Column j uses the scale xs_in[j / group] (group = K: one scale; group = D: one per
+// attention head of a [T x H*D] KV block); a 16-byte chunk never straddles a group.
 template <typename T, bool SMOOTH>
 __global__ __launch_bounds__(kThreads) void static_quant_kernel(const T* __restrict__ X, int64_t M, int64_t K,
                                                                 const float* __restrict__ s,
-                                                                const float* __restrict__ xs_in,
+                                                                const float* __restrict__ xs_in, int64_t group,
                                                                 int8_t* __restrict__ Xq,
-                                                                float* __restrict__ xs_rows) {
+                                                                float* __restrict__ xs_rows, int lgp) {
     using V = typename Chunk16<T>::V;
     constexpr int N = Chunk16<T>::N;
     const int64_t nchunk = K / N;
-    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const float xs = *xs_in;
-    const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+    const int64_t c = ((int64_t)blockIdx.x << lgp) + (threadIdx.x & ((1u << lgp) - 1));
     if (xs_rows != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-        for (int64_t m = blockIdx.y; m < M; m += gridDim.y) xs_rows[m] = xs;
+        for (int64_t m = blockIdx.y; m < M; m += gridDim.y) xs_rows[m] = xs_in[0];
     if (c >= nchunk) return;
+    const float xs = xs_in[(c * N) / group];
+    const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
     Cols<T, SMOOTH> cols;
     cols.init(s, c);
     // rows in batches of RB: the batch's loads are all in flight before its codes are formed
     constexpr int RB = 4;
-    const int64_t step = gridDim.y;
+    const int64_t R = kThreads >> lgp;
+    const int64_t step = gridDim.y * R;
+    const int64_t first = blockIdx.y * R + (threadIdx.x >> lgp);
     auto rows = [&](auto guarded) {
-        for (int64_t m0 = blockIdx.y; m0 < M; m0 += RB * step) {
+        for (int64_t m0 = first; m0 < M; m0 += RB * step) {
             V v[RB];
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
@@ -246,10 +251,11 @@ hipError_t calibrate_t(const T* X, int64_t M, int64_t K, const float* s, uint32_
 }
 
 template <typename T, bool SMOOTH>
-hipError_t quant_t(const T* X, int64_t M, int64_t K, const float* s, const float* xs, int8_t* Xq, float* xs_rows,
-                   hipStream_t st) {
-    hipLaunchKernelGGL((static_quant_kernel<T, SMOOTH>), grid_of(M, K, Chunk16<T>::N), dim3(kThreads), 0, st, X, M, K,
-                       s, xs, Xq, xs_rows);
+hipError_t quant_t(const T* X, int64_t M, int64_t K, const float* s, const float* xs, int64_t group, int8_t* Xq,
+                   float* xs_rows, hipStream_t st) {
+    const RowPack g = row_pack(M, K / Chunk16<T>::N, kRowsPerThread, 65536 / kThreads);
+    hipLaunchKernelGGL((static_quant_kernel<T, SMOOTH>), g.grid, dim3(kThreads), 0, st, X, M, K, s, xs, group, Xq,
+                       xs_rows, g.lgp);
     return hipGetLastError();
 }
 
@@ -266,13 +272,13 @@ hipError_t launch_static_calibrate(const void* X, sq_dtype dt, int64_t M, int64_
 }
 
 hipError_t launch_static_quant(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, const float* xs,
-                               int8_t* Xq, float* xs_rows, hipStream_t st) {
+                               int64_t group, int8_t* Xq, float* xs_rows, hipStream_t st) {
     if (dt == SQ_F16) {
-        if (s) return quant_t<_Float16, true>((const _Float16*)X, M, K, s, xs, Xq, xs_rows, st);
-        return quant_t<_Float16, false>((const _Float16*)X, M, K, s, xs, Xq, xs_rows, st);
+        if (s) return quant_t<_Float16, true>((const _Float16*)X, M, K, s, xs, group, Xq, xs_rows, st);
+        return quant_t<_Float16, false>((const _Float16*)X, M, K, s, xs, group, Xq, xs_rows, st);
     }
-    if (s) return quant_t<float, true>((const float*)X, M, K, s, xs, Xq, xs_rows, st);
-    return quant_t<float, false>((const float*)X, M, K, s, xs, Xq, xs_rows, st);
+    if (s) return quant_t<float, true>((const float*)X, M, K, s, xs, group, Xq, xs_rows, st);
+    return quant_t<float, false>((const float*)X, M, K, s, xs, group, Xq, xs_rows, st);
 }
 
 }  // namespace sq

@@ -37,6 +37,9 @@ def lib():
     lib.sq_layernorm_quantize_per_token.argtypes = [V, I, I64, I64, V, V, F, V, V, V]
     lib.sq_calibrate_static_scale.argtypes = [V, I, I64, I64, V, C.c_double, V, V, SZ, V]
     lib.sq_quantize_static.argtypes = [V, I, I64, I64, V, V, V, V, V]
+    lib.sq_kv_calibrate_per_head.argtypes = [V, I, I64, I64, I64, F, V, V]
+    lib.sq_kv_quantize_per_head.argtypes = [V, I, I64, I64, I64, V, V, V]
+    lib.sq_dequantize.argtypes = [V, I64, I64, V, I64, I64, V, I, V]
     return lib
 
 
@@ -195,3 +198,34 @@ def test_static_scale_validation(lib):
     assert g(P, 1, 4, 50, None, P, P, None, None) == SHAPE
     assert g(P, 3, 4, 64, None, P, P, None, None) == DTYPE
     assert g(P, 1, 4, 64, None, P, P, MIS, None) == ALIGN
+
+
+def test_kv_cache_validation(lib):
+    f = lib.sq_kv_calibrate_per_head
+    assert f(None, 1, 16, 8, 128, 1.0, P, None) == NULL
+    assert f(P, 1, 16, 8, 128, 1.0, None, None) == NULL
+    for T, H, D in ((0, 8, 128), (16, 0, 128), (16, 8, 8), (16, 8, 120), (16, 1024, 128), (1 << 31, 8, 128)):
+        assert f(P, 1, T, H, D, 1.0, P, None) == SHAPE, (T, H, D)
+    assert f(P, 5, 16, 8, 128, 1.0, P, None) == DTYPE
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert f(P, 1, 16, 8, 128, bad, P, None) == VALUE
+    assert f(MIS, 1, 16, 8, 128, 1.0, P, None) == ALIGN
+    assert f(P, 1, 16, 8, 128, 1.0, MIS, None) == ALIGN
+    g = lib.sq_kv_quantize_per_head
+    assert g(P, 1, 16, 8, 128, None, P, None) == NULL
+    assert g(P, 1, 16, 8, 128, P, None, None) == NULL
+    assert g(P, 1, 16, 8, 40, P, P, None) == SHAPE
+    assert g(P, 1, 16, 8193, 16, P, P, None) == SHAPE
+    assert g(P, 2, 16, 8, 128, P, P, None) == DTYPE
+    assert g(P, 1, 16, 8, 128, P, MIS, None) == ALIGN
+    d = lib.sq_dequantize
+    assert d(None, 4, 64, P, 0, 16, P, 1, None) == NULL
+    assert d(P, 4, 64, None, 0, 16, P, 1, None) == NULL
+    assert d(P, 4, 64, P, 0, 16, None, 1, None) == NULL
+    for M, K, rs, grp in ((0, 64, 0, 16), (4, 60, 0, 60), (4, 64, 0, 8), (4, 64, 0, 24), (4, 96, 0, 64),
+                          (4, 64, -1, 16), (4, 64, 0, 0)):
+        assert d(P, M, K, P, rs, grp, P, 1, None) == SHAPE, (M, K, rs, grp)
+    assert d(P, 4, 64, P, 0, 16, P, 7, None) == DTYPE
+    assert d(MIS, 4, 64, P, 0, 16, P, 1, None) == ALIGN
+    assert d(P, 4, 64, P, 0, 16, MIS, 1, None) == ALIGN
+    assert d(P, 4, 64, P + 2, 0, 16, P, 1, None) == ALIGN     # scale needs 4-byte alignment only

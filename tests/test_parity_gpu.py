@@ -592,3 +592,133 @@ def test_static_decode_layer(sq, orc):
         assert_bits_equal(acc[rr, cc], acc_r, "acc (sampled)")
         y = orc.dequant_sampled(acc_r, np.full(m, xs_cal, np.float32), ws, 0, None, rr, cc)
         assert_bits_equal(Y[rr, cc], orc.float_to_half(y), "Y (sampled)")
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache with per-head scales (SmoothQuant page, section 5.2) and
+# grouped dequantization
+# ---------------------------------------------------------------------------
+def gpu_kv_calibrate(sq, KV, margin):
+    H = KV.shape[1]
+    sc = Guarded((H,), torch.float32, fill=-1.0)
+    sq.sq_kv_calibrate_per_head(dev(KV), margin, sc.t)
+    torch.cuda.synchronize()
+    return sc.np()
+
+
+def gpu_kv_quantize(sq, KV, scale):
+    q = Guarded(KV.shape, torch.int8)
+    sq.sq_kv_quantize_per_head(dev(KV), dev(np.asarray(scale, np.float32)), q.t)
+    torch.cuda.synchronize()
+    return q.np()
+
+
+def gpu_dequantize(sq, q, scale, rs, group, out_dt):
+    Y = Guarded(q.shape, torch.float16 if out_dt == np.float16 else torch.float32, fill=7.0)
+    sq.sq_dequantize(dev(q), dev(np.asarray(scale, np.float32)), rs, group, Y.t)
+    torch.cuda.synchronize()
+    return Y.np()
+
+
+def _kv_case(seed, T, H, D, dt):
+    r = np.random.default_rng(seed)
+    KV = (r.standard_normal((T, H, D)) * np.exp(r.uniform(-2.0, 2.0, (1, H, 1)))).astype(dt)
+    return KV
+
+
+KV_CASES = [
+    # T, H, D, dtype, margin
+    (1, 1, 16, np.float32, 1.0), (7, 3, 48, np.float16, 1.0), (4096, 8, 128, np.float16, 1.0),
+    (1000, 32, 128, np.float16, 1.2), (33, 2, 64, np.float32, 1.5), (5, 1023, 128, np.float16, 1.0),
+    (300, 40, 112, np.float16, 1.25), (2049, 4, 256, np.float32, 1.1),
+]
+
+
+@pytest.mark.parametrize("T,H,D,dt,margin", KV_CASES)
+def test_kv_calibrate_per_head(sq, orc, T, H, D, dt, margin):
+    KV = _kv_case(T + H + D, T, H, D, dt)
+    KV[T - 1, H - 1, D - 1] = -2 * (np.abs(KV[:, H - 1]).max() + 1)                       # max at the last element
+    if H > 2:
+        KV[:, 1] = 0                                                                     # an all-zero head
+    sc = gpu_kv_calibrate(sq, KV, margin)
+    ref = orc.kv_calibrate_per_head(KV, margin)
+    assert_bits_equal(sc, ref, "per-head scales")
+    if H > 2:
+        assert sc[1] == 0.0
+
+
+@pytest.mark.parametrize("T,H,D,dt,margin", KV_CASES)
+def test_kv_quantize_per_head(sq, orc, T, H, D, dt, margin):
+    KV = _kv_case(2 * T + H + D, T, H, D, dt)
+    sc = orc.kv_calibrate_per_head(KV[: max(1, T // 2)], margin)          # calibrated on a prefix
+    if H > 2:
+        sc[1] = 0.0                                                        # zero scale: zero codes
+    q = gpu_kv_quantize(sq, KV, sc)
+    q_ref = orc.kv_quantize_per_head(KV, sc)
+    assert_bits_equal(q, q_ref, "KV codes")
+    if H > 2:
+        assert not q[:, 1].any()
+
+
+@pytest.mark.parametrize("out_dt", [np.float16, np.float32])
+@pytest.mark.parametrize("M,K,mode", [(1, 16, "head"), (17, 48, "row"), (300, 1024, "head"), (300, 1024, "token_head"),
+                                      (4097, 1040, "row"), (33, 131056, "row"), (64, 4096, "token_head")])
+def test_dequantize(sq, orc, M, K, mode, out_dt):
+    r = np.random.default_rng(M + K)
+    q = r.integers(-128, 128, (M, K), dtype=np.int16).astype(np.int8)
+    q[0, :16] = [-128, 127, 0, 1, -1, 2, -2, 64, -64, 100, -100, 3, 5, 7, 9, 11]
+    if mode == "head":
+        group, rs = 16 if K == 16 else 64, 0
+        n = K // group
+    elif mode == "row":
+        group, rs = K, 1
+        n = M
+    else:
+        group, rs = 16 if K == 48 else 128, K // (16 if K == 48 else 128)
+        n = M * rs
+    scale = (r.uniform(0.0, 1.0, n) ** 4 * 700.0).astype(np.float32)    # down to tiny; fp16 may overflow
+    scale[0] = np.float32(2.0 ** -130)                                   # subnormal scale
+    if n > 2:
+        scale[2] = 0.0
+    Y = gpu_dequantize(sq, q, scale, rs, group, out_dt)
+    y = orc.dequantize(q, scale, rs, group)
+    ref = orc.float_to_half(y) if out_dt == np.float16 else y
+    assert_bits_equal(Y, ref, "dequantized")
+
+
+def test_kv_cache_append_and_read(sq, orc):
+    """A cache of capacity C filled by three appends (the last one ragged) with
+    calibrated per-head scales and a safety factor, then read back whole."""
+    K_cal, _, Kx, _ = workloads.kv_cache(seed=3, T=700)
+    H, D = Kx.shape[1], Kx.shape[2]
+    sc = gpu_kv_calibrate(sq, K_cal, 1.25)
+    assert_bits_equal(sc, orc.kv_calibrate_per_head(K_cal, 1.25), "scales")
+    C = 1024
+    cache = Guarded((C, H, D), torch.int8)
+    cache.t.fill_(0x11)
+    sc_d = dev(sc)
+    for t0, t1 in ((0, 512), (512, 513), (513, 700)):
+        sq.sq_kv_quantize_per_head(dev(Kx[t0:t1]), sc_d, cache.t[t0:t1])
+    torch.cuda.synchronize()
+    q = cache.np()
+    q_ref = orc.kv_quantize_per_head(Kx, sc)
+    assert_bits_equal(q[:700], q_ref, "cache codes")
+    assert np.all(q[700:] == 0x11), "write past the appended tokens"
+    Y = gpu_dequantize(sq, q[:700].reshape(700, H * D), sc, 0, D, np.float16)
+    assert_bits_equal(Y, orc.float_to_half(orc.dequantize(q_ref.reshape(700, H * D), sc, 0, D)), "read back")
+
+
+def test_kv_cache_layer(sq, orc):
+    """The 4096-token, 8-head, 128-dim K and V of one layer: per-head scales from a
+    512-token calibration batch (safety factor 1.2), codes, and the read-back."""
+    K_cal, V_cal, Kx, Vx = workloads.kv_cache()
+    T, H, D = Kx.shape
+    for cal, x in ((K_cal, Kx), (V_cal, Vx)):
+        sc = gpu_kv_calibrate(sq, cal, 1.2)
+        sc_ref = orc.kv_calibrate_per_head(cal, 1.2)
+        assert_bits_equal(sc, sc_ref, "scales")
+        q = gpu_kv_quantize(sq, x, sc)
+        q_ref = orc.kv_quantize_per_head(x, sc_ref)
+        assert_bits_equal(q, q_ref, "codes")
+        Y = gpu_dequantize(sq, q.reshape(T, H * D), sc, 0, D, np.float16)
+        assert_bits_equal(Y, orc.float_to_half(orc.dequantize(q_ref.reshape(T, H * D), sc_ref, 0, D)), "read back")

@@ -144,6 +144,29 @@ def random_layer(seed: int, M: int, K: int, N: int, dtype=np.float16, n_outliers
     return X.astype(dtype), W.astype(dtype), idx
 
 
+def kv_cache(seed: int = 0, T: int = 4096, H: int = 8, D: int = 128, T_cal: int = 512):
+    """One layer's K and V cache, [T x H x D] fp16, with a calibration prefix.
+
+    Heads differ in range (the reason for per-head scales): head h is drawn as
+    N(0, 1) times a per-head factor, log-uniform in [0.25, 8]; a few (head, dim)
+    lanes per head are 10x larger.  Draw order: per-head factors (K, then V),
+    outlier lanes (K, then V), K_cal, V_cal [T_cal x H x D], then K, V [T x H x D].
+    Returns (K_cal, V_cal, K, V) as float16 arrays.
+    """
+    rng = np.random.default_rng(seed)
+    fac = [np.exp(rng.uniform(np.log(0.25), np.log(8.0), H)).astype(np.float32) for _ in range(2)]
+    lanes = [np.stack([_pick(rng, D, 2) for _ in range(H)]) for _ in range(2)]
+
+    def draw(n, which):
+        x = rng.standard_normal((n, H, D), dtype=np.float32) * fac[which][None, :, None]
+        for h in range(H):
+            x[:, h, lanes[which][h]] *= np.float32(10.0)
+        return x.astype(np.float16)
+
+    K_cal, V_cal = draw(T_cal, 0), draw(T_cal, 1)
+    return K_cal, V_cal, draw(T, 0), draw(T, 1)
+
+
 WORKLOADS = {
     "single_w8a8": single_w8a8,
     "prefill_7b": prefill_7b,
