@@ -57,6 +57,13 @@ def _load():
         "orc_kv_calibrate_per_head": (None, [P, I, I64, I64, I64, F, P]),
         "orc_kv_quantize_per_head": (None, [P, I, I64, I64, I64, P, P]),
         "orc_dequantize": (None, [P, I64, I64, P, I64, I64, P]),
+        "orc_fp8_encode_array": (None, [P, P, I64]),
+        "orc_fp8_decode_array": (None, [P, P, I64]),
+        "orc_fp8_quantize_rows": (None, [P, I, I64, I64, P, I, P, P]),
+        "orc_fp8_quantize_tensor": (None, [P, I, I64, I64, P, P, P]),
+        "orc_gemm_fp8": (None, [P, P, I64, I64, I64, P, P]),
+        "orc_gemm_fp8_sampled": (None, [P, P, I64, P, P, I64, P, P]),
+        "orc_fp8_dequant": (None, [P, P, P, I, P, P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -377,3 +384,94 @@ def dequantize(q, scale, row_stride, group):
     y = np.empty((M, K), np.float32)
     _load().orc_dequantize(_ptr(qc), M, K, _ptr(sc), int(row_stride), int(group), _ptr(y))
     return y
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3, OCP e4m3fn) W8A8 variant (SmoothQuant page, section 6.1)
+# ---------------------------------------------------------------------------
+def fp8_encode(v):
+    """float32 -> e4m3fn code bytes (uint8), nearest-even, saturating at 448."""
+    v = _as(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_fp8_encode_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def fp8_decode(c):
+    c = _as(c, np.uint8)
+    out = np.empty(c.shape, np.float32)
+    _load().orc_fp8_decode_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def fp8_quantize_per_token(X, s=None):
+    """Per-row FP8 codes of X' = X / s (or X): (codes uint8 [M,K], scale fp32 [M])."""
+    X, dt = _fp(X)
+    M, K = X.shape
+    q = np.empty((M, K), np.uint8)
+    sc = np.empty(M, np.float32)
+    sv = None if s is None else _as(s, np.float32)
+    _load().orc_fp8_quantize_rows(_ptr(X), dt, M, K, _ptr(sv), 0 if s is None else 1, _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def fp8_quantize_weight(W, s, gran):
+    """FP8 codes of W' = W diag(s) (or W): per output row (gran 0) or per tensor (gran 1)."""
+    W, dt = _fp(W)
+    N, K = W.shape
+    q = np.empty((N, K), np.uint8)
+    sv = None if s is None else _as(s, np.float32)
+    if gran == 0:
+        sc = np.empty(N, np.float32)
+        _load().orc_fp8_quantize_rows(_ptr(W), dt, N, K, _ptr(sv), 0 if s is None else 2, _ptr(q), _ptr(sc))
+    else:
+        sc = np.empty(1, np.float32)
+        _load().orc_fp8_quantize_tensor(_ptr(W), dt, N, K, _ptr(sv), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def gemm_fp8(A, B, with_abs=False):
+    """Exact sum_k dec(A[m,k]) dec(B[n,k]) in fp64 (and sum_k |...| when with_abs)."""
+    A = _as(A, np.uint8)
+    B = _as(B, np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    acc = np.empty((M, N), np.float64)
+    ab = np.empty((M, N), np.float64) if with_abs else None
+    _load().orc_gemm_fp8(_ptr(A), _ptr(B), M, N, K, _ptr(acc), _ptr(ab))
+    return (acc, ab) if with_abs else acc
+
+
+def gemm_fp8_sampled(A, B, rows, cols):
+    """(exact acc, sum |products|) at the given positions."""
+    A = _as(A, np.uint8)
+    B = _as(B, np.uint8)
+    K = A.shape[1]
+    rows = _as(rows, np.int64)
+    cols = _as(cols, np.int64)
+    acc = np.empty(rows.size, np.float64)
+    ab = np.empty(rows.size, np.float64)
+    _load().orc_gemm_fp8_sampled(_ptr(A), _ptr(B), K, _ptr(rows), _ptr(cols), rows.size, _ptr(acc), _ptr(ab))
+    return acc, ab
+
+
+def fp8_dequant_sampled(acc, x_scale, w_scale, wgran, bias, rows, cols):
+    """y = ((float)acc * xs[m]) * ws[n or 0] (+ bias[n]) at the given positions (fp32)."""
+    acc = _as(acc, np.float64)
+    rows = _as(rows, np.int64)
+    cols = _as(cols, np.int64)
+    y = np.empty(rows.size, np.float32)
+    _load().orc_fp8_dequant(_ptr(acc), _ptr(_as(x_scale, np.float32)), _ptr(_as(w_scale, np.float32)), int(wgran),
+                            _ptr(None if bias is None else _as(bias, np.float32)), _ptr(rows), _ptr(cols), rows.size,
+                            _ptr(y))
+    return y
+
+
+def fp8_linear(X, s, Wq, ws, wgran, bias, out_dtype):
+    """FP8 W8A8 forward for small shapes: per-token FP8 codes, exact GEMM, dequant."""
+    Xq, xs = fp8_quantize_per_token(X, s)
+    M, N = X.shape[0], Wq.shape[0]
+    acc = gemm_fp8(Xq, Wq)
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    y = fp8_dequant_sampled(acc.ravel(), xs, ws, wgran, bias, rr.ravel(), cc.ravel()).reshape(M, N)
+    return float_to_half(y) if out_dtype == np.float16 else y

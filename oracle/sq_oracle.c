@@ -565,3 +565,173 @@ void orc_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, i
         for (int64_t j = 0; j < K; ++j)
             y[m * K + j] = (float)q[m * K + j] * scale[m * row_stride + j / group];
 }
+
+/* ------------------------------------------------------------------ */
+/* FP8 W8A8 variant (SmoothQuant page, section 6.1: W8A8 in FP8 on      */
+/* hardware with FP8 matrix units).  The same flow with the 8-bit code  */
+/* switched from int8 to FP8 E4M3 (OCP "e4m3fn": 1 sign bit, 4 exponent */
+/* bits with bias 7, 3 mantissa bits, no infinities; largest finite     */
+/* value 448, smallest subnormal 2^-9):                                 */
+/*   scale = fl32(max|x'| / 448); code = e4m3(clamp(fl32(x' / scale),   */
+/*   -448, 448)), rounded to nearest, ties to even; scale 0 -> code 0.  */
+/* ------------------------------------------------------------------ */
+
+/* binary32 -> e4m3fn, round to nearest even; |v| above 448 saturates to 448
+ * (the quantizer's clamp).  Finite inputs only. */
+uint8_t orc_fp8_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80u : 0x00u;
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7eu);              /* 448 = 1.110b * 2^8 */
+    if (a < 0x1p-6) {
+        /* subnormal range: multiples of 2^-9; code = the multiple (8 = 2^-6 is the
+         * first normal, whose code is also 8) */
+        double q = nearbyint(a * 512.0);                         /* exact scaling; ties to even */
+        return (uint8_t)(sign | (uint8_t)q);
+    }
+    int e;
+    double f = frexp(a, &e);                                     /* a = f * 2^e, f in [0.5, 1) */
+    int E = e - 1;                                               /* a = (2f) * 2^E, 2f in [1, 2) */
+    double r = nearbyint((2.0 * f - 1.0) * 8.0);                 /* 3-bit mantissa, ties to even */
+    if (r == 8.0) {
+        r = 0.0;
+        E += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | (int)r));
+}
+
+float orc_fp8_decode(uint8_t c)
+{
+    int s = c >> 7, E = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (E == 15 && m == 7) v = NAN;
+    else if (E == 0) v = (float)m * 0x1p-9f;
+    else v = ldexpf(1.0f + (float)m / 8.0f, E - 7);
+    return s ? -v : v;
+}
+
+void orc_fp8_encode_array(const float* in, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_encode(in[i]);
+}
+
+void orc_fp8_decode_array(const uint8_t* in, float* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_decode(in[i]);
+}
+
+static uint8_t fp8_code_of(float x, float sc)
+{
+    if (sc == 0.0f) return 0;
+    float v = x / sc;
+    if (v > 448.0f) v = 448.0f;
+    if (v < -448.0f) v = -448.0f;
+    return orc_fp8_encode(v);
+}
+
+/* Per-row FP8 quantization of X [M x K]: mode 0 x' = x, mode 1 x' = fl32(x / s_j)
+ * (activations, smoothing), mode 2 x' = fl32(x * s_j) (weight rows, smoothed). */
+void orc_fp8_quantize_rows(const void* X, int dt, int64_t M, int64_t K, const float* s, int mode,
+                           uint8_t* q, float* scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            float x = load_elem(X, dt, m * K + j);
+            if (mode == 1) x = x / s[j];
+            if (mode == 2) x = x * s[j];
+            float v = fabsf(x);
+            if (v > a) a = v;
+        }
+        float sc = a / 448.0f;
+        scale[m] = sc;
+        for (int64_t j = 0; j < K; ++j) {
+            float x = load_elem(X, dt, m * K + j);
+            if (mode == 1) x = x / s[j];
+            if (mode == 2) x = x * s[j];
+            q[m * K + j] = fp8_code_of(x, sc);
+        }
+    }
+}
+
+/* Per-tensor FP8 weight quantization: one scale fl32(max|W'| / 448). */
+void orc_fp8_quantize_tensor(const void* W, int dt, int64_t N, int64_t K, const float* s, uint8_t* q,
+                             float* scale)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float w = load_elem(W, dt, i);
+        if (s) w = w * s[i % K];
+        float v = fabsf(w);
+        if (v > a) a = v;
+    }
+    float sc = a / 448.0f;
+    scale[0] = sc;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N * K; ++i) {
+        float w = load_elem(W, dt, i);
+        if (s) w = w * s[i % K];
+        q[i] = fp8_code_of(w, sc);
+    }
+}
+
+/* Every finite e4m3 value is an integer multiple of 2^-9 with |n| <= 448 * 2^9 < 2^18,
+ * so a product is n_a n_b 2^-18 with |n_a n_b| < 2^36, and a sum of K <= 131071 such
+ * products is an integer below 2^53: accumulated in int64 it is exact, and so is its
+ * conversion to fp64. */
+static int64_t fp8_units(uint8_t c)
+{
+    int E = (c >> 3) & 15, m = c & 7;
+    int64_t n = E == 0 ? m : (int64_t)(8 + m) << (E - 1);      /* value * 2^9 */
+    return (c & 0x80u) ? -n : n;
+}
+
+/* Exact FP8 "NT" GEMM: acc[m,n] = sum_k A[m,k] B[n,k] (fp64, exact); abs_sum (may be
+ * NULL) receives sum_k |A[m,k] B[n,k]|, for error bounds of inexact accumulations. */
+void orc_gemm_fp8(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, double* acc,
+                  double* abs_sum)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t t = 0, u = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t p = fp8_units(A[m * K + k]) * fp8_units(B[n * K + k]);
+                t += p;
+                u += p < 0 ? -p : p;
+            }
+            acc[m * N + n] = ldexp((double)t, -18);
+            if (abs_sum) abs_sum[m * N + n] = ldexp((double)u, -18);
+        }
+}
+
+void orc_gemm_fp8_sampled(const uint8_t* A, const uint8_t* B, int64_t K, const int64_t* rows,
+                          const int64_t* cols, int64_t nsamp, double* acc, double* abs_sum)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nsamp; ++i) {
+        int64_t t = 0, u = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t p = fp8_units(A[rows[i] * K + k]) * fp8_units(B[cols[i] * K + k]);
+            t += p;
+            u += p < 0 ? -p : p;
+        }
+        acc[i] = ldexp((double)t, -18);
+        if (abs_sum) abs_sum[i] = ldexp((double)u, -18);
+    }
+}
+
+/* FP8 dequantization: y = ((float)acc * x_scale[m]) * w_scale[n or 0] (+ bias[n]), with
+ * the exact accumulator rounded once to fp32 (a matrix unit accumulates in fp32). */
+void orc_fp8_dequant(const double* acc, const float* x_scale, const float* w_scale, int wgran,
+                     const float* bias, const int64_t* rows, const int64_t* cols, int64_t nsamp, float* y)
+{
+    for (int64_t i = 0; i < nsamp; ++i) {
+        float v = (float)acc[i];
+        v = v * x_scale[rows[i]];
+        v = v * w_scale[wgran == 0 ? cols[i] : 0];
+        if (bias) v = v + bias[cols[i]];
+        y[i] = v;
+    }
+}

@@ -715,3 +715,128 @@ def test_dequantize_closed_form_and_round_trip(orc):
     qd, xs = orc.quantize_per_token(KV.reshape(T * H, D), None)
     yd = orc.dequantize(qd, xs, 1, D)
     assert np.all(np.abs(KV.reshape(T * H, D) - yd) <= xs[:, None] * (0.5 + 1e-6))
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 W8A8 variant (SmoothQuant page, section 6.1)
+# --------------------------------------------------------------------------
+def _torch_e4m3(v):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_decode_closed_form_and_torch(orc):
+    """All 256 codes: (-1)^s 2^(E-7) (1 + m/8), subnormals m 2^-9, NaN at S.1111.111;
+    and torch's float8_e4m3fn widening agrees."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    d = orc.fp8_decode(codes)
+    for c in range(256):
+        s, E, m = c >> 7, (c >> 3) & 15, c & 7
+        if E == 15 and m == 7:
+            assert np.isnan(d[c])
+            continue
+        v = Fraction(m, 512) if E == 0 else Fraction(8 + m, 8) * Fraction(2) ** (E - 7)
+        assert Fraction(float(d[c])) == (-v if s else v), c
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    ok = np.isnan(t) & np.isnan(d) | (t == d)
+    assert ok.all()
+    assert d[0x7E] == 448.0 and d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6
+
+
+def test_fp8_encode_rne_against_torch(orc):
+    """Nearest-even rounding: random values, every midpoint between adjacent codes,
+    and the floats just beside each midpoint, against torch's conversion."""
+    vals = orc.fp8_decode(np.arange(0, 0x7F, dtype=np.uint8)).astype(np.float64)   # 0 .. 448, ascending
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)                          # exact in fp32
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000))])
+    r = np.random.default_rng(61)
+    rnd = (r.uniform(-1, 1, 200000) * np.exp2(r.uniform(-14, 8.8, 200000))).astype(np.float32)
+    x = np.concatenate([near, -near, rnd, np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 2.0 ** -12])])
+    x = np.clip(x, -448, 448)
+    assert np.array_equal(orc.fp8_encode(x), _torch_e4m3(x))
+    # ties go to the even mantissa: 1 + 1/16 -> 1.0, 1 + 3/16 -> 1.25, 1.5 * 2^-9 -> 2^-8
+    assert list(orc.fp8_decode(orc.fp8_encode(np.float32([1.0625, 1.1875, 1.5 * 2 ** -9])))) == [1.0, 1.25, 2 ** -8]
+    assert orc.fp8_encode(np.float32([1e6]))[0] == 0x7E                           # saturates (the clamp)
+
+
+def test_fp8_per_token_invariants(orc):
+    """Per row: the absmax element codes to +-448, |x' - dec(q) xs| within half a code
+    step (relative 2^-4 for normals), zero rows give scale 0 and code 0, and the codes
+    equal an independent recipe (numpy fp32 division + torch's e4m3 conversion)."""
+    r = np.random.default_rng(62)
+    X = (r.standard_normal((9, 96)) * r.uniform(0.01, 50, (9, 1))).astype(np.float16)
+    X[3] = 0
+    s = r.uniform(0.2, 5.0, 96).astype(np.float32)
+    q, xs = orc.fp8_quantize_per_token(X, s)
+    Xs = X.astype(np.float32) / s
+    a = np.abs(Xs).max(axis=1)
+    assert np.array_equal(xs, (a / np.float32(448)).astype(np.float32))
+    assert xs[3] == 0 and not q[3].any()
+    live = xs > 0
+    v = np.clip(Xs[live] / xs[live, None], -448, 448).astype(np.float32)
+    assert np.array_equal(q[live], _torch_e4m3(v))
+    dec = orc.fp8_decode(q[live]).astype(np.float64)
+    assert np.all(np.abs(dec).max(axis=1) == 448.0)
+    step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(v - dec) <= step / 2 * (1 + 1e-12))
+
+
+def test_fp8_weight_granularity_reductions(orc):
+    """Per-channel = per-token on W' = W diag(s) (mode: multiply); per-tensor = one
+    flattened row."""
+    r = np.random.default_rng(63)
+    W = (r.standard_normal((7, 64)) * 0.02).astype(np.float32)
+    s = np.exp2(r.integers(-3, 4, 64)).astype(np.float32)      # power-of-two s: W * s exact
+    q0, s0 = orc.fp8_quantize_weight(W, s, 0)
+    qr, sr = orc.fp8_quantize_per_token(W * s, None)
+    assert np.array_equal(q0, qr) and np.array_equal(s0, sr)
+    q1, s1 = orc.fp8_quantize_weight(W, s, 1)
+    qf, sf = orc.fp8_quantize_per_token((W * s).reshape(1, -1), None)
+    assert np.array_equal(q1.ravel(), qf.ravel()) and s1[0] == sf[0]
+
+
+def test_fp8_gemm_exact(orc):
+    """For K = 64 the fp64 product of the decoded operands is exact (spans < 53 bits),
+    so the integer-unit GEMM must equal it; for large K, Python integers on a few
+    entries.  Transposed operands would fail on the non-square shape."""
+    r = np.random.default_rng(64)
+    A = r.integers(0, 256, (5, 64), dtype=np.uint16).astype(np.uint8)
+    B = r.integers(0, 256, (3, 64), dtype=np.uint16).astype(np.uint8)
+    A[A & 0x7F == 0x7F] = 0x11                                  # no NaN codes
+    B[B & 0x7F == 0x7F] = 0x22
+    acc, ab = orc.gemm_fp8(A, B, with_abs=True)
+    da, db = orc.fp8_decode(A).astype(np.float64), orc.fp8_decode(B).astype(np.float64)
+    assert np.array_equal(acc, da @ db.T)
+    assert np.array_equal(ab, np.abs(da) @ np.abs(db).T)
+    K = 40000
+    A = r.integers(0, 0x7E, (2, K), dtype=np.uint16).astype(np.uint8) | (r.integers(0, 2, (2, K)) << 7).astype(np.uint8)
+    B = r.integers(0, 0x7E, (2, K), dtype=np.uint16).astype(np.uint8)
+    acc = orc.gemm_fp8(A, B)
+    fa = [Fraction(float(v)) for v in orc.fp8_decode(A[1])]
+    fb = [Fraction(float(v)) for v in orc.fp8_decode(B[0])]
+    assert Fraction(float(acc[1, 0])) == sum(x * y for x, y in zip(fa, fb))
+    rows, cols = np.array([1, 0]), np.array([0, 1])
+    sa, _ = orc.gemm_fp8_sampled(A, B, rows, cols)
+    assert np.array_equal(sa, acc[rows, cols])
+
+
+def test_fp8_linear_error_bound(orc):
+    """The FP8 W8A8 layer against fp64 X W^T: each code carries at most 2^-4 relative
+    error (3 mantissa bits, nearest), so |y - XW^T| <= ((1+2^-4)^2 - 1 + 2^-20) sum|x||w|
+    elementwise (normals; subnormal codes add at most 2^-10 xs ws per product)."""
+    X, W, _ = workloads.random_layer(65, 32, 256, 48, np.float32, n_outliers=3)
+    _, s = orc.smooth_scales(X, W, 0.5)
+    Wq, ws = orc.fp8_quantize_weight(W, s, 0)
+    y = orc.fp8_linear(X, s, Wq, ws, 0, None, np.float32).astype(np.float64)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    xq, xs = orc.fp8_quantize_per_token(X, s)
+    bound = ((1 + 2.0 ** -4) ** 2 - 1 + 2.0 ** -20) * (np.abs(X.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
+    bound += 2.0 ** -10 * 256 * 2 * (xs[:, None].astype(np.float64) * ws[None, :].astype(np.float64)) * 448
+    assert np.all(np.abs(y - ref) <= bound)
+    # dequantization with power-of-two scales is exact on an exactly representable acc
+    acc = orc.gemm_fp8(xq, Wq)
+    rr, cc = np.meshgrid(np.arange(32), np.arange(48), indexing="ij")
+    p2x, p2w = np.exp2(np.arange(-2, 30) % 5 - 2).astype(np.float32), np.exp2(np.arange(48) % 3 - 1).astype(np.float32)
+    yd = orc.fp8_dequant_sampled(acc.ravel(), p2x, p2w, 0, None, rr.ravel(), cc.ravel()).reshape(32, 48)
+    assert np.array_equal(yd, (acc.astype(np.float32) * p2x[:, None]) * p2w[None, :])
