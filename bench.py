@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W8A8 linear TOPS incl. quant+dequant (% int8 MFMA peak); decode GB/s (% HBM peak)"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP8_TOPS = 5000.0       # MI355X dense fp8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "int8_quantization_amd", "csrc", "gemm.hip")
@@ -138,6 +139,40 @@ def bench_w8a8(torch, sq, d, wl, steps, warmup):
     ops = sum(2.0 * M * p[2].shape[0] * K for p in projs)
     return dict(ms=ms, gemm_ms=gemm_ms, ops=ops, gemm_ops_per_launch=ops / len(projs),
                 Ns=[p[2].shape[0] for p in projs])
+
+
+def bench_fp8(torch, sq, d, wl, steps, warmup):
+    """The headline prefill step with FP8 E4M3 codes instead of int8: per-token FP8
+    quantization and the FP8 GEMM + dequant epilogue for each projection (same shapes,
+    smoothing and per-channel weight scales)."""
+    M, K = wl.X.shape
+    X = d(wl.X)
+    projs = []
+    for name, W in wl.weights.items():
+        N = W.shape[0]
+        act = torch.zeros(K, dtype=torch.float32, device="cuda")
+        s = torch.empty(K, dtype=torch.float32, device="cuda")
+        W_d = d(W)
+        sq.sq_smooth_scales(d(wl.calib), W_d, wl.alpha, act, s)
+        Wq = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(N, dtype=torch.float32, device="cuda")
+        sq.sq_quantize_weight_fp8(W_d, s, 0, Wq, ws)
+        del W_d
+        projs.append((s, Wq, ws, torch.empty(M, N, dtype=torch.float16, device="cuda")))
+    Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+
+    def step(timer):
+        for s, Wq, ws, Y in projs:
+            sq.sq_quantize_per_token_fp8(X, s, Xq, xs)
+            g = lambda: sq.fp8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
+            timer.around(g) if timer else g()
+
+    ms, gemm_ms = time_steps(torch, step, steps, warmup)
+    ops = sum(2.0 * M * p[1].shape[0] * K for p in projs)
+    gemm_tops = ops / len(projs) / (gemm_ms * 1e-3) / 1e12
+    return dict(ms_per_step=ms, TOPS=ops / (ms * 1e-3) / 1e12, gemm_us_per_launch=gemm_ms * 1e3,
+                gemm_TOPS=gemm_tops, gemm_mfma_frac=gemm_tops / PEAK_FP8_TOPS)
 
 
 def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
@@ -347,7 +382,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default=None,
-                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant|static_quant|kv_cache")
+                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant|static_quant|kv_cache|fp8")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -420,6 +455,10 @@ def main():
             log("static_quant: prefill activation and decode")
             secondary["static_scale"] = bench_static(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
                                                      workloads.decode_70b(), sec_steps * 2, sec_warm)
+        if args.only in (None, "fp8"):
+            log("fp8: 7B prefill projections with FP8 E4M3 codes")
+            secondary["fp8_prefill_7b"] = bench_fp8(torch, sq, d, workloads.prefill_7b(), sec_steps, sec_warm)
+            torch.cuda.empty_cache()
         if args.only in (None, "kv_cache"):
             log("kv_cache: 16 x 4096 tokens, 8 heads x 128")
             secondary["kv_cache"] = bench_kv_cache(torch, sq, d, sec_steps * 2, sec_warm)

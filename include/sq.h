@@ -236,6 +236,39 @@ sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_c
 sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
                              const float* x_scale, int8_t* Xq, float* x_scale_rows, hipStream_t stream);
 
+/* FP8 W8A8 variant: FP8 E4M3 codes (OCP "e4m3fn": bias 7, 3 mantissa bits, largest
+ * finite 448, smallest subnormal 2^-9, no infinities; byte = sign | exponent | mantissa).
+ * [SmoothQuant page, section 6.1: W8A8 in FP8 is the scheme to prefer on hardware
+ *  with FP8 matrix units; the flow is the int8 one with the 8-bit code changed.]
+ * Per-token activation codes:
+ *   X, s, M, K as for sq_quantize_per_token.
+ *   x_scale  device float [M], out: xs = fl32(max_j |x'_j| / 448) (0 for an all-zero row).
+ *   Xq       device uint8 [M x K], out: e4m3(clamp(fl32(x'_j / xs), -448, 448)), nearest even
+ *            (0x00 when xs == 0; -0 codes as 0x80).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status sq_quantize_per_token_fp8(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
+                                    uint8_t* Xq, float* x_scale, hipStream_t stream);
+
+/* FP8 E4M3 weight codes of W' = fl32(W * s_j) (or W), per output channel (w_scale [N]) or
+ * per tensor (w_scale [1], workspace as for sq_quantize_weight): scale = fl32(max|W'| / 448),
+ * codes as in sq_quantize_per_token_fp8.  Arguments as for sq_quantize_weight.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
+sq_status sq_quantize_weight_fp8(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s,
+                                 sq_wgran g, uint8_t* Wq, float* w_scale, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* FP8 E4M3 GEMM with the dequantizing epilogue (any M; gfx950 FP8 matrix instructions):
+ *   acc[m,n] = sum_k dec(Xq[m,k]) dec(Wq[n,k]), accumulated in fp32 (the products are
+ *   exact; the order of the fp32 additions is the hardware's, so acc is within
+ *   gamma_K * sum_k |products| of the exact sum, gamma_K = K 2^-24 / (1 - K 2^-24));
+ *   y = ((acc * x_scale[m]) * w_scale[n or 0]) (+ bias[n]), fp32 steps, stored as ydt.
+ *   Other arguments as for w8a8_gemm_dequant; acc_out (device float [M x N] or NULL)
+ *   receives the fp32 accumulators.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status fp8_gemm_dequant(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                           sq_wgran g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                           sq_dtype ydt, float* acc_out, hipStream_t stream);
+
 /* INT8 KV cache, per-head calibration (offline or at cache creation).
  * [SmoothQuant page, section 5.2: the KV cache is stored as int8 with one scale per
  *  attention head, the heads' ranges being different; a scale fixed from calibration

@@ -46,6 +46,9 @@ def _load():
         "sq_layernorm_quantize_per_token": (I, [P, I, I64, I64, P, P, F, P, P, P]),
         "sq_calibrate_static_scale": (I, [P, I, I64, I64, P, C.c_double, P, P, SZ, P]),
         "sq_quantize_static": (I, [P, I, I64, I64, P, P, P, P, P]),
+        "sq_quantize_per_token_fp8": (I, [P, I, I64, I64, P, P, P, P]),
+        "sq_quantize_weight_fp8": (I, [P, I, I64, I64, P, I, P, P, P, SZ, P]),
+        "fp8_gemm_dequant": (I, [P, P, P, P, I, P, I64, I64, I64, P, I, P, P]),
         "sq_kv_calibrate_per_head": (I, [P, I, I64, I64, I64, F, P, P]),
         "sq_kv_quantize_per_head": (I, [P, I, I64, I64, I64, P, P, P]),
         "sq_dequantize": (I, [P, I64, I64, P, I64, I64, P, I, P]),
@@ -62,7 +65,8 @@ _lib = _load()
 EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quantize_per_token",
            "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
            "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static",
-           "sq_kv_calibrate_per_head", "sq_kv_quantize_per_head", "sq_dequantize")
+           "sq_kv_calibrate_per_head", "sq_kv_quantize_per_head", "sq_dequantize", "sq_quantize_per_token_fp8",
+           "sq_quantize_weight_fp8", "fp8_gemm_dequant")
 
 
 def _p(t):
@@ -198,3 +202,29 @@ def sq_dequantize(q, scale, scale_row_stride, group, Y):
     M = q.numel() // K
     _check("sq_dequantize", _lib.sq_dequantize(
         _p(q), M, K, _p(scale), int(scale_row_stride), int(group), _p(Y), _dt(Y), _stream()))
+
+
+def sq_quantize_per_token_fp8(X, s, Xq, x_scale):
+    """Xq: uint8 [M, K] (FP8 E4M3 code bytes) out; x_scale fp32 [M] out."""
+    _dense(X, s, Xq, x_scale)
+    M, K = X.shape
+    _check("sq_quantize_per_token_fp8", _lib.sq_quantize_per_token_fp8(
+        _p(X), _dt(X), M, K, _p(s), _p(Xq), _p(x_scale), _stream()))
+
+
+def sq_quantize_weight_fp8(W, s, gran, Wq, w_scale, ws=None):
+    _dense(W, s, Wq, w_scale, ws)
+    N, K = W.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("sq_quantize_weight_fp8", _lib.sq_quantize_weight_fp8(
+        _p(W), _dt(W), N, K, _p(s), int(gran), _p(Wq), _p(w_scale), _p(ws), nbytes, _stream()))
+
+
+def fp8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
+    """Xq uint8 [M, K], Wq uint8 [N, K] (FP8 E4M3 codes); Y fp16/fp32 [M, N]; acc_out fp32 [M, N]."""
+    _dense(Xq, x_scale, Wq, w_scale, bias, Y, acc_out)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    _check("fp8_gemm_dequant", _lib.fp8_gemm_dequant(
+        _p(Xq), _p(x_scale), _p(Wq), _p(w_scale), int(gran), _p(bias), M, N, K, _p(Y), _dt(Y),
+        _p(acc_out), _stream()))

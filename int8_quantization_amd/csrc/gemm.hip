@@ -36,6 +36,13 @@
 // output type and written to LDS, then copied out with 16-byte row-contiguous
 // stores.
 //
+// FP8 E4M3 variant (FP8 = true; "SmoothQuant量化实战", section 6.1, W8A8 in FP8
+// on hardware with FP8 matrix units): the same tiles, staging and epilogue with
+// v_mfma_f32_32x32x64_f8f6f4 and fp32 accumulators.  That instruction takes 32
+// bytes per lane; a lane concatenates the two 16-byte chunks it reads for two
+// consecutive int8 k-steps, so both operands keep one k placement and the LDS
+// reads are the int8 kernel's (conflict-free) pattern.
+//
 // LLM.int8() ["LLM.int8()技术解析", section 3.1]: when a side product is
 // requested, the dequantized tile becomes the C input of
 // v_mfma_f32_32x32x16_f16 over the gathered fp16 outlier columns, so the fp16
@@ -103,7 +110,7 @@ __device__ __forceinline__ v4i buffer_desc(const int8_t* p, int nrec) {
                __builtin_amdgcn_readfirstlane(nrec), 0x00020000};
 }
 
-template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
+template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
@@ -112,7 +119,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     int tiles_n) {
     constexpr int BK = 128;                  // bytes of K per stage: one cache line per row
     constexpr int S = 2;                     // LDS stages
-    constexpr int KS = BK / 32;              // MFMA k-steps per stage
+    constexpr int KS = BK / (FP8 ? 64 : 32); // MFMA k-steps per stage
+    using Frag = typename std::conditional<FP8, v8i, v4i>::type;
+    using Acc = typename std::conditional<FP8, v16f, v16i>::type;
+    static_assert(!(FP8 && SIDE), "the LLM.int8() side product is int8 only");
     constexpr int NW = WM * WN;              // waves, in a WM x WN grid over the tile
     constexpr int NT = 64 * NW;              // threads
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -195,35 +205,50 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         }
     };
 
-    v16i acc[TM][TN];
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
+        for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
 
     const int lrow = lane & 31, lk = lane >> 5;
-    v4i af[2][TM], bf[2][TN];
+    Frag af[2][TM], bf[2][TN];
+    // fragment of k-step ks for one LDS row: chunk 2ks + lane/32 (int8); chunks
+    // 4ks + lane/32 and 4ks + 2 + lane/32, concatenated (FP8)
+    auto frag = [&](const int8_t* rowp, int row, int ks) -> Frag {
+        if constexpr (FP8) {
+            const v4i lo = *reinterpret_cast<const v4i*>(rowp + (((4 * ks + lk) ^ swz(row)) << 4));
+            const v4i hi = *reinterpret_cast<const v4i*>(rowp + (((4 * ks + 2 + lk) ^ swz(row)) << 4));
+            return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            return *reinterpret_cast<const v4i*>(rowp + (((2 * ks + lk) ^ swz(row)) << 4));
+        }
+    };
     auto fload = [&](int stage, int ks, int slot) {
-        const int c = ks * 2 + lk;
         const int8_t* As = lds + stage * STAGE;
         const int8_t* Bs = As + BM * BK;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = wm * WTM + i * 32 + lrow;
-            af[slot][i] = *reinterpret_cast<const v4i*>(As + row * BK + ((c ^ swz(row)) << 4));
+            af[slot][i] = frag(As + row * BK, row, ks);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int row = wn * WTN + j * 32 + lrow;
-            bf[slot][j] = *reinterpret_cast<const v4i*>(Bs + row * BK + ((c ^ swz(row)) << 4));
+            bf[slot][j] = frag(Bs + row * BK, row, ks);
         }
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[slot][j], af[slot][i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (FP8)   // format 0 = E4M3 for both operands; no block scales
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[slot][j], af[slot][i], acc[i][j],
+                                                                                0, 0, 0, 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[slot][j], af[slot][i], acc[i][j], 0, 0, 0);
+            }
     };
 
     // Tile order: [partial tail], 0, 1, ..., nfull-1.  Tile j lives in stage j % 2.
@@ -400,7 +425,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                     for (int b = 0; b < 4; ++b) {
                         // read the accumulator register directly, one value at a time
                         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(iv[b]) : "a"(acc[i][j][4 * a + b]));
-                        float v = (float)iv[b];
+                        float v = FP8 ? __builtin_bit_cast(float, iv[b]) : (float)iv[b];
                         v = v * xsv;
                         v = v * w4[b];
                         v = v + b4[b];      // -0.0 without a bias: an exact identity
@@ -491,7 +516,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE>
+template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8>
 hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int32_t* acc_out,
                const SideArgs* side, hipStream_t st) {
@@ -500,7 +525,7 @@ hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float*
     const _Float16* Wo = side ? side->Wo : nullptr;
     const int32_t* cnt = side ? side->count : nullptr;
     const int64_t ldo = side ? side->ldo : 0;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE>), dim3((unsigned)(tm * tn)),
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE, FP8>), dim3((unsigned)(tm * tn)),
                        dim3(64 * WM * WN), 0, st, Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out,
                        Xo, Wo, cnt, ldo, ldy, tm, tn);
     return hipGetLastError();
@@ -509,16 +534,30 @@ hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float*
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                     const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, sq_dtype ydt,
-                    int32_t* acc_out, const SideArgs* side, hipStream_t st) {
+                    int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st) {
+    if (fp8) {
+        if constexpr (BN == 256) {
+            return hipErrorInvalidValue;   // the FP8 fragments do not fit beside 256 x 256 accumulators
+        } else {
+            if (side) return hipErrorInvalidValue;
+            if (ydt == SQ_F16)
+                return run<BM, BN, WM, WN, true, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy,
+                                                              acc_out, side, st);
+            return run<BM, BN, WM, WN, false, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy,
+                                                           acc_out, side, st);
+        }
+    }
     if (ydt == SQ_F16) {
         if (side)
-            return run<BM, BN, WM, WN, true, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side,
-                                                   st);
-        return run<BM, BN, WM, WN, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side, st);
+            return run<BM, BN, WM, WN, true, true, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out,
+                                                          side, st);
+        return run<BM, BN, WM, WN, true, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out,
+                                                       side, st);
     }
     // The LLM.int8() side product comes with fp16 output only (int8_outlier_matmul writes fp16).
     if (side) return hipErrorInvalidValue;
-    return run<BM, BN, WM, WN, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side, st);
+    return run<BM, BN, WM, WN, false, false, false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, acc_out, side,
+                                                    st);
 }
 
 // Output columns [0, N) of a product whose output rows are ldy elements apart.
@@ -530,9 +569,10 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
 // a second launch that picks its own tiles, if that is estimated faster.
 hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, sq_dtype ydt,
-                       int32_t* acc_out, const SideArgs* side, hipStream_t st, bool may_split) {
+                       int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st, bool may_split) {
     const int64_t cus = dev_info().cus;
     struct Cand { int bm, bn, per_cu; double rate; };
+    // (FP8 starts at the second candidate: its fragments do not fit beside 256 x 256 accumulators)
     constexpr Cand cands[] = {{256, 256, 1, 1.0}, {256, 192, 1, 1.0}, {128, 128, 2, 0.75}};
     auto cost_of = [&](const Cand& c, int64_t n) {
         const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
@@ -541,7 +581,7 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
     };
     int best = 0;
     double best_cost = 1e300;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = fp8 ? 1 : 0; c < 3; ++c) {
         const double cost = cost_of(cands[c], N);
         if (cost < best_cost * 0.999) {
             best_cost = cost;
@@ -555,10 +595,10 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
     if (may_split && full >= 1 && tn_main >= 1 && tn_main < tn) {
         const int64_t n_main = tn_main * b.bn;
         double tail_cost = 1e300;
-        for (const Cand& c : cands) tail_cost = std::min(tail_cost, cost_of(c, N - n_main));
+        for (int c = fp8 ? 1 : 0; c < 3; ++c) tail_cost = std::min(tail_cost, cost_of(cands[c], N - n_main));
         if (full * b.per_cu * b.bm * b.bn / b.rate + tail_cost < 0.95 * best_cost) {
-            const hipError_t e =
-                launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, n_main, K, Y, ldy, ydt, acc_out, side, st, false);
+            const hipError_t e = launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, n_main, K, Y, ldy, ydt, acc_out,
+                                             side, fp8, st, false);
             if (e != hipSuccess) return e;
             SideArgs side2{};
             if (side) {
@@ -568,16 +608,16 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
             return launch_cols(Xq, xs, Wq + n_main * K, ws + n_main * ws_stride, ws_stride,
                                bias ? bias + n_main : nullptr, M, N - n_main, K,
                                static_cast<char*>(Y) + n_main * (ydt == SQ_F16 ? 2 : 4), ldy, ydt,
-                               acc_out ? acc_out + n_main : nullptr, side ? &side2 : nullptr, st, false);
+                               acc_out ? acc_out + n_main : nullptr, side ? &side2 : nullptr, fp8, st, false);
         }
     }
     if (best == 0)
         return dispatch<256, 256, SQ_W256_WM, SQ_W256_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt,
-                                                          acc_out, side, st);
+                                                          acc_out, side, fp8, st);
     if (best == 1)
         return dispatch<256, 192, SQ_W192_WM, SQ_W192_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt,
-                                                          acc_out, side, st);
-    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt, acc_out, side, st);
+                                                          acc_out, side, fp8, st);
+    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt, acc_out, side, fp8, st);
 }
 
 }  // namespace
@@ -585,7 +625,14 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
-    return launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, N, ydt, acc_out, side, st, true);
+    return launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, N, ydt, acc_out, side, false, st, true);
+}
+
+hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, int ws_stride,
+                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, float* acc_out,
+                           hipStream_t st) {
+    return launch_cols(reinterpret_cast<const int8_t*>(Xq), xs, reinterpret_cast<const int8_t*>(Wq), ws, ws_stride,
+                       bias, M, N, K, Y, N, ydt, reinterpret_cast<int32_t*>(acc_out), nullptr, true, st, true);
 }
 
 }  // namespace sq

@@ -79,6 +79,34 @@ template <> struct CodeStore<4> {
     }
 };
 
+// FP8 E4M3 (OCP e4m3fn) codes of four values, one per byte, nearest-even
+// (v_cvt_pk_fp8_f32).  Callers clamp to [-448, 448] first, so no value overflows.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+__device__ __forceinline__ float fp8_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
+// Codes of VEC quotients x'/scale: int8 (FMT 0) or FP8 E4M3 (FMT 1); `zero` marks
+// elements whose code is 0 (scale 0, LLM.int8() outlier columns).
+template <int VEC, int FMT>
+__device__ __forceinline__ void store_codes(int8_t* p, const float* v, const bool* zero) {
+    if constexpr (FMT == 0) {
+        int q[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) q[e] = zero[e] ? 0 : code_of(v[e]);
+        CodeStore<VEC>::store(p, q);
+    } else {
+        float c[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) c[e] = zero[e] ? 0.0f : fp8_clamp(v[e]);
+        if constexpr (VEC == 8)
+            *reinterpret_cast<uint2*>(p) = make_uint2(fp8x4(c[0], c[1], c[2], c[3]), fp8x4(c[4], c[5], c[6], c[7]));
+        else
+            *reinterpret_cast<uint32_t*>(p) = fp8x4(c[0], c[1], c[2], c[3]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Fused smoothing + per-row quantization, register-resident rows.
 //
@@ -91,6 +119,7 @@ template <> struct CodeStore<4> {
 //   mode 0: x' = x;   mode 1: x' = fl32(x / s_j);   mode 2: x' = fl32(x * s_j)
 //   xs = fl32(max |x'| / 127) over non-outlier columns
 //   q  = clamp(rne(fl32(x' / xs)), -128, 127), 0 for outlier columns or xs == 0
+// FMT 1 (FP8 E4M3): xs = fl32(max |x'| / 448), q = e4m3(clamp(fl32(x' / xs), -448, 448)).
 // Both divisions are exact fp32 quotients computed as RN32(RN64(a * RN64(1/b)))
 // (see div_rcp64).  A quotient below the fp32 normal range takes the IEEE
 // division for x / s_j (only possible for fp32 inputs or s_j > 2^100); for
@@ -105,7 +134,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <typename T, int VEC, int CH, int MODE, bool OUTL>
+template <typename T, int VEC, int CH, int MODE, bool OUTL, int FMT>
 __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X, int64_t M, int64_t K,
                                                         const float* __restrict__ s, int8_t* __restrict__ Xq,
                                                         float* __restrict__ scale, const int32_t* __restrict__ pos,
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
         lds_barrier();
         float a = red[it & 1][w0];
         for (int w = 1; w < nw; ++w) a = __builtin_fmaxf(a, red[it & 1][w0 + w]);
-        const float xs = a / 127.0f;
+        const float xs = a / (FMT == 0 ? 127.0f : 448.0f);
         if (live) {
             if (tid == 0) scale[m] = xs;
             const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
@@ -212,14 +241,15 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
             for (int i = 0; i < CH; ++i) {
                 if (!valid[i]) continue;
                 const int64_t c = tid + (int64_t)i * tpg;
-                int q[VEC];
+                float v[VEC];
+                bool zero[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    bool zero = xs == 0.0f;
-                    if constexpr (OUTL) zero = zero || ((omask[i] >> e) & 1u);
-                    q[e] = zero ? 0 : code_of((float)((double)xv[i][e] * rx));
+                    zero[e] = xs == 0.0f;
+                    if constexpr (OUTL) zero[e] = zero[e] || ((omask[i] >> e) & 1u);
+                    v[e] = (float)((double)xv[i][e] * rx);
                 }
-                CodeStore<VEC>::store(Xq + m * K + c * VEC, q);
+                store_codes<VEC, FMT>(Xq + m * K + c * VEC, v, zero);
             }
         }
 #pragma unroll
@@ -231,7 +261,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
 
 // Fallback for rows too long to keep in registers: two passes over the row
 // (the second from cache), IEEE divisions.
-template <typename T, int MODE, bool OUTL>
+template <typename T, int MODE, bool OUTL, int FMT>
 __global__ __launch_bounds__(1024) void quant_rows_generic(const T* __restrict__ X, int64_t M, int64_t K,
                                                            const float* __restrict__ s, int8_t* __restrict__ Xq,
                                                            float* __restrict__ scale,
@@ -261,7 +291,7 @@ __global__ __launch_bounds__(1024) void quant_rows_generic(const T* __restrict__
         __syncthreads();
         float a = red[it & 1][0];
         for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[it & 1][w]);
-        const float xs = a / 127.0f;
+        const float xs = a / (FMT == 0 ? 127.0f : 448.0f);
         if (tid == 0) scale[m] = xs;
         for (int64_t j = tid; j < K; j += nthr) {
             float x = (float)row[j];
@@ -269,7 +299,8 @@ __global__ __launch_bounds__(1024) void quant_rows_generic(const T* __restrict__
             if constexpr (MODE == 2) x = x * s[j];
             bool zero = xs == 0.0f;
             if constexpr (OUTL) zero = zero || pos[j] >= 0;
-            Xq[m * K + j] = (int8_t)(zero ? 0 : code_of(x / xs));
+            if constexpr (FMT == 0) Xq[m * K + j] = (int8_t)(zero ? 0 : code_of(x / xs));
+            else Xq[m * K + j] = (int8_t)(fp8x4(zero ? 0.0f : fp8_clamp(x / xs), 0.0f, 0.0f, 0.0f) & 0xffu);
         }
     }
 }
@@ -281,14 +312,14 @@ static int blocks_per_cu(Kern k, int threads) {
     return nb;
 }
 
-template <typename T, int VEC, int CH, int MODE, bool OUTL>
+template <typename T, int VEC, int CH, int MODE, bool OUTL, int FMT>
 static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
                               const int32_t* pos, _Float16* Xo, hipStream_t st) {
     const int64_t nchunk = K / VEC;
     const int tpg = (int)((((nchunk + CH - 1) / CH) + 63) / 64 * 64);   // threads per row group
     const int G = 1024 / tpg;                                          // row groups per block
     const int threads = G * tpg;
-    auto k = quant_rows_fast<T, VEC, CH, MODE, OUTL>;
+    auto k = quant_rows_fast<T, VEC, CH, MODE, OUTL, FMT>;
     static int nb_cache[1025] = {0};
     int nb = nb_cache[threads];
     if (nb == 0) nb_cache[threads] = nb = blocks_per_cu(k, threads);
@@ -301,31 +332,43 @@ static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, 
 
 // Register-resident variants by row length (elements per thread <= 20), else the
 // two-pass fallback.
-template <typename T, int MODE, bool OUTL>
+template <typename T, int MODE, bool OUTL, int FMT>
 static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
                                const int32_t* pos, _Float16* Xo, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
         // one 16-byte chunk per thread (one row per block) when there are few rows: the per-block
         // setup is then split over the most threads
         if (K <= 1024 || (K <= 8192 && M <= dev_info().cus))
-            return launch_fast<T, 8, 1, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 16384) return launch_fast<T, 8, 2, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 20480) return launch_fast<T, 4, 5, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+            return launch_fast<T, 8, 1, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 16384) return launch_fast<T, 8, 2, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 20480) return launch_fast<T, 4, 5, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
     } else {
-        if (K <= 4096) return launch_fast<T, 4, 1, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 8192) return launch_fast<T, 4, 2, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 12288) return launch_fast<T, 4, 3, MODE, OUTL>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 4096) return launch_fast<T, 4, 1, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 8192) return launch_fast<T, 4, 2, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 12288) return launch_fast<T, 4, 3, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
     }
-    auto k = quant_rows_generic<T, MODE, OUTL>;
+    auto k = quant_rows_generic<T, MODE, OUTL, FMT>;
     const int64_t g = (int64_t)dev_info().cus * 2;
     hipLaunchKernelGGL(k, dim3((unsigned)(g < M ? g : M)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, int mode,
-                             int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st) {
+                             int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st, int fmt) {
     const bool outl = pos != nullptr;
-#define SQ_QR(T, MD, OL) return quant_rows_t<T, MD, OL>((const T*)X, M, K, s, Xq, scale, pos, Xo, st)
+    if (fmt == 1) {   // FP8 E4M3 codes (no outlier variant)
+#define SQ_QR8(T, MD) return quant_rows_t<T, MD, false, 1>((const T*)X, M, K, s, Xq, scale, nullptr, nullptr, st)
+        if (dt == SQ_F16) {
+            if (mode == 1) SQ_QR8(_Float16, 1);
+            if (mode == 2) SQ_QR8(_Float16, 2);
+            SQ_QR8(_Float16, 0);
+        }
+        if (mode == 1) SQ_QR8(float, 1);
+        if (mode == 2) SQ_QR8(float, 2);
+        SQ_QR8(float, 0);
+#undef SQ_QR8
+    }
+#define SQ_QR(T, MD, OL) return quant_rows_t<T, MD, OL, 0>((const T*)X, M, K, s, Xq, scale, pos, Xo, st)
     if (dt == SQ_F16) {
         if (outl) SQ_QR(_Float16, 0, true);
         if (mode == 1) SQ_QR(_Float16, 1, false);
@@ -442,31 +485,33 @@ __global__ __launch_bounds__(256) void tensor_max_kernel(const T* __restrict__ W
     }
 }
 
-template <typename T, bool SMOOTH>
+template <typename T, bool SMOOTH, int FMT>
 __global__ __launch_bounds__(256) void tensor_code_kernel(const T* __restrict__ W, int64_t nchunks, int64_t kchunks,
                                                           const float* __restrict__ s,
                                                           const uint32_t* __restrict__ gmax,
                                                           int8_t* __restrict__ Wq, float* __restrict__ w_scale) {
     using V = typename Chunk<T>::V;
     constexpr int VEC = Chunk<T>::N;
-    const float sc = __uint_as_float(*gmax) / 127.0f;
+    const float sc = __uint_as_float(*gmax) / (FMT == 0 ? 127.0f : 448.0f);
     const double rx = sc != 0.0f ? 1.0 / (double)sc : 0.0;
     if (blockIdx.x == 0 && threadIdx.x == 0) *w_scale = sc;
     for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
         V v = reinterpret_cast<const V*>(W)[c];
         int64_t jc = c % kchunks;
-        int q[VEC];
+        float q[VEC];
+        bool zero[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             float x = (float)v[e];
             if constexpr (SMOOTH) x = x * s[jc * VEC + e];
-            q[e] = sc == 0.0f ? 0 : code_of(div_rcp64(x, rx, sc));
+            zero[e] = sc == 0.0f;
+            q[e] = div_rcp64(x, rx, sc);
         }
-        CodeStore<VEC>::store(Wq + c * VEC, q);
+        store_codes<VEC, FMT>(Wq + c * VEC, q, zero);
     }
 }
 
-template <typename T>
+template <typename T, int FMT>
 static hipError_t quant_tensor_t(const T* W, int64_t N, int64_t K, const float* s, int8_t* Wq, float* w_scale,
                                  uint32_t* gmax, hipStream_t st) {
     constexpr int VEC = Chunk<T>::N;
@@ -476,18 +521,22 @@ static hipError_t quant_tensor_t(const T* W, int64_t N, int64_t K, const float* 
     if (blocks > cap) blocks = cap;
     if (s) {
         hipLaunchKernelGGL((tensor_max_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
-        hipLaunchKernelGGL((tensor_code_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
+        hipLaunchKernelGGL((tensor_code_kernel<T, true, FMT>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
     } else {
         hipLaunchKernelGGL((tensor_max_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
-        hipLaunchKernelGGL((tensor_code_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
+        hipLaunchKernelGGL((tensor_code_kernel<T, false, FMT>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quant_tensor(const void* W, sq_dtype dt, int64_t N, int64_t K, const float* s, int8_t* Wq,
-                               float* w_scale, uint32_t* gmax_bits, hipStream_t st) {
-    if (dt == SQ_F16) return quant_tensor_t((const _Float16*)W, N, K, s, Wq, w_scale, gmax_bits, st);
-    return quant_tensor_t((const float*)W, N, K, s, Wq, w_scale, gmax_bits, st);
+                               float* w_scale, uint32_t* gmax_bits, hipStream_t st, int fmt) {
+    if (fmt == 1) {
+        if (dt == SQ_F16) return quant_tensor_t<_Float16, 1>((const _Float16*)W, N, K, s, Wq, w_scale, gmax_bits, st);
+        return quant_tensor_t<float, 1>((const float*)W, N, K, s, Wq, w_scale, gmax_bits, st);
+    }
+    if (dt == SQ_F16) return quant_tensor_t<_Float16, 0>((const _Float16*)W, N, K, s, Wq, w_scale, gmax_bits, st);
+    return quant_tensor_t<float, 0>((const float*)W, N, K, s, Wq, w_scale, gmax_bits, st);
 }
 
 }  // namespace sq

@@ -59,7 +59,7 @@ const char* sq_status_string(sq_status st) {
         case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: unsupported dtype or granularity";
         case SQ_ERR_VALUE:
             return "SQ_ERR_VALUE: alpha must be in [0,1]; threshold finite and >= 0; eps finite and > 0; "
-                   "percentile in (0, 100]";
+                   "percentile in (0, 100]; margin finite and > 0";
         case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
         case SQ_ERR_HIP: return "SQ_ERR_HIP: a HIP launch failed";
     }
@@ -169,6 +169,45 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, 
     SQ_TRY(launch_gather_cols(static_cast<const _Float16*>(W16), N, K, idx, count, wo, stream));
     SideArgs side{xo, wo, count, K};
     return hip_status(launch_gemm(xq, xs, Wq, w_scale, 1, bias, M, N, K, Y, SQ_F16, acc_out, &side, stream));
+}
+
+sq_status sq_quantize_per_token_fp8(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, uint8_t* Xq,
+                                    float* x_scale, hipStream_t stream) {
+    if (!X || !Xq || !x_scale) return SQ_ERR_NULL;
+    if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt)) return SQ_ERR_DTYPE;
+    if (misaligned(X) || misaligned(Xq) || misaligned(x_scale) || (s && misaligned(s))) return SQ_ERR_ALIGN;
+    return hip_status(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, reinterpret_cast<int8_t*>(Xq), x_scale, nullptr,
+                                        nullptr, stream, 1));
+}
+
+sq_status sq_quantize_weight_fp8(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s, sq_wgran g,
+                                 uint8_t* Wq, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!W || !Wq || !w_scale) return SQ_ERR_NULL;
+    if (bad_shape(1, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(wdt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if (misaligned(W) || misaligned(Wq) || misaligned(w_scale) || (s && misaligned(s))) return SQ_ERR_ALIGN;
+    int8_t* q = reinterpret_cast<int8_t*>(Wq);
+    if (g == SQ_PER_CHANNEL)
+        return hip_status(launch_quant_rows(W, wdt, N, K, s, s ? 2 : 0, q, w_scale, nullptr, nullptr, stream, 1));
+    if (!ws || ws_bytes < sq_workspace_size(SQ_OP_QUANT_WEIGHT, 0, N, K)) return SQ_ERR_WORKSPACE;
+    if (misaligned(ws)) return SQ_ERR_ALIGN;
+    uint32_t* gmax = reinterpret_cast<uint32_t*>(ws);
+    SQ_TRY(launch_fill_u32(gmax, 1, 0u, stream));
+    return hip_status(launch_quant_tensor(W, wdt, N, K, s, q, w_scale, gmax, stream, 1));
+}
+
+sq_status fp8_gemm_dequant(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                           sq_wgran g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                           float* acc_out, hipStream_t stream) {
+    if (!Xq || !x_scale || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(ydt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if (misaligned(Xq) || misaligned(x_scale) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) ||
+        (bias && misaligned(bias)) || (acc_out && misaligned(acc_out)))
+        return SQ_ERR_ALIGN;
+    return hip_status(launch_gemm_fp8(Xq, x_scale, Wq, w_scale, g == SQ_PER_CHANNEL ? 1 : 0, bias, M, N, K, Y, ydt,
+                                      acc_out, stream));
 }
 
 sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,

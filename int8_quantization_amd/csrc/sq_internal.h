@@ -7,6 +7,7 @@
 #include "../../include/sq.h"
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -89,9 +90,10 @@ inline RowPack row_pack(int64_t M, int64_t nchunk, int64_t rows_per_thread, int6
 // Per-row smoothing + absmax quantization (activations per token, weights per channel).
 // mode 0: no smoothing; 1: x / s_j; 2: x * s_j.  pos/Xo (LLM.int8() only): pos[j] >= 0
 // marks an outlier column, whose value is copied to Xo[m*K + pos[j]] and whose code is 0.
+// fmt 0: int8 codes, scale max/127; fmt 1: FP8 E4M3 code bytes, scale max/448 (no pos).
 hipError_t launch_quant_rows(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s,
                              int mode, int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo,
-                             hipStream_t st);
+                             hipStream_t st, int fmt = 0);
 
 // Running column absolute maximum: amax_bits[j] = max(amax_bits[j], bits(max_m |X[m,j]|)),
 // where amax_bits holds non-negative floats as their bit patterns (monotone as uint32).
@@ -104,7 +106,7 @@ hipError_t launch_smooth_pow(const float* act_max, float* s_wmax, int64_t K, flo
 
 // Per-tensor weight quantization: global max then codes.
 hipError_t launch_quant_tensor(const void* W, sq_dtype dt, int64_t N, int64_t K, const float* s,
-                               int8_t* Wq, float* w_scale, uint32_t* gmax_bits, hipStream_t st);
+                               int8_t* Wq, float* w_scale, uint32_t* gmax_bits, hipStream_t st, int fmt = 0);
 
 // int8 GEMM + dequant epilogue (M > 16).  side != nullptr adds the LLM.int8() fp16 side
 // product over the first *count columns of Xo [M x ldo] and Wo [N x ldo].
@@ -117,6 +119,11 @@ struct SideArgs {
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
                        sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+// FP8 E4M3 GEMM (fp32 accumulation) + the same dequant epilogue; acc_out receives the
+// fp32 accumulators' bits.
+hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                           int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                           sq_dtype ydt, float* acc_out, hipStream_t st);
 
 // Weight-streaming decode kernel, M <= 16.
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,

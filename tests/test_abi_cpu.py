@@ -37,6 +37,9 @@ def lib():
     lib.sq_layernorm_quantize_per_token.argtypes = [V, I, I64, I64, V, V, F, V, V, V]
     lib.sq_calibrate_static_scale.argtypes = [V, I, I64, I64, V, C.c_double, V, V, SZ, V]
     lib.sq_quantize_static.argtypes = [V, I, I64, I64, V, V, V, V, V]
+    lib.sq_quantize_per_token_fp8.argtypes = [V, I, I64, I64, V, V, V, V]
+    lib.sq_quantize_weight_fp8.argtypes = [V, I, I64, I64, V, I, V, V, V, SZ, V]
+    lib.fp8_gemm_dequant.argtypes = [V, V, V, V, I, V, I64, I64, I64, V, I, V, V]
     lib.sq_kv_calibrate_per_head.argtypes = [V, I, I64, I64, I64, F, V, V]
     lib.sq_kv_quantize_per_head.argtypes = [V, I, I64, I64, I64, V, V, V]
     lib.sq_dequantize.argtypes = [V, I64, I64, V, I64, I64, V, I, V]
@@ -229,3 +232,35 @@ def test_kv_cache_validation(lib):
     assert d(MIS, 4, 64, P, 0, 16, P, 1, None) == ALIGN
     assert d(P, 4, 64, P, 0, 16, MIS, 1, None) == ALIGN
     assert d(P, 4, 64, P + 2, 0, 16, P, 1, None) == ALIGN     # scale needs 4-byte alignment only
+
+
+def test_fp8_validation(lib):
+    q = lib.sq_quantize_per_token_fp8
+    assert q(None, 1, 4, 64, None, P, P, None) == NULL
+    assert q(P, 1, 4, 64, None, None, P, None) == NULL
+    assert q(P, 1, 4, 64, None, P, None, None) == NULL
+    assert q(P, 1, 0, 64, None, P, P, None) == SHAPE
+    assert q(P, 1, 4, 40, None, P, P, None) == SHAPE
+    assert q(P, 1, 4, 131072, None, P, P, None) == SHAPE
+    assert q(P, 3, 4, 64, None, P, P, None) == DTYPE
+    assert q(P, 1, 4, 64, MIS, P, P, None) == ALIGN
+    assert q(P, 1, 4, 64, None, MIS, P, None) == ALIGN
+    w = lib.sq_quantize_weight_fp8
+    need = lib.sq_workspace_size(0, 0, 8, 64)
+    assert w(None, 1, 8, 64, None, 0, P, P, None, 0, None) == NULL
+    assert w(P, 1, 8, 64, None, 0, None, P, None, 0, None) == NULL
+    assert w(P, 1, 0, 64, None, 0, P, P, None, 0, None) == SHAPE
+    assert w(P, 1, 8, 64, None, 2, P, P, None, 0, None) == DTYPE
+    assert w(P, 1, 8, 64, None, 1, P, P, None, 0, None) == WORKSPACE
+    assert w(P, 1, 8, 64, None, 1, P, P, P, need - 1, None) == WORKSPACE
+    assert w(P, 1, 8, 64, None, 1, P, P, MIS, need, None) == ALIGN
+    assert w(P, 1, 8, 64, None, 0, MIS, P, None, 0, None) == ALIGN
+    g = lib.fp8_gemm_dequant
+    assert g(None, P, P, P, 0, None, 32, 32, 64, P, 1, None, None) == NULL
+    assert g(P, P, P, P, 0, None, 32, 32, 64, None, 1, None, None) == NULL
+    assert g(P, P, P, P, 0, None, 32, 0, 64, P, 1, None, None) == SHAPE
+    assert g(P, P, P, P, 0, None, 32, 32, 72, P, 1, None, None) == SHAPE
+    assert g(P, P, P, P, 5, None, 32, 32, 64, P, 1, None, None) == DTYPE
+    assert g(P, P, P, P, 0, None, 32, 32, 64, P, 9, None, None) == DTYPE
+    assert g(P, P, P, P, 0, MIS, 32, 32, 64, P, 1, None, None) == ALIGN
+    assert g(P, P, P, P, 0, None, 32, 32, 64, P, 1, MIS, None) == ALIGN
