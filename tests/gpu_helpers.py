@@ -36,9 +36,15 @@ def dev(a):
 
 
 def assert_close(y, ref, rtol):
-    """|y - ref| <= rtol |ref| + rtol mean|ref| (relative error with a floor)."""
+    """|y - ref| <= rtol |ref| + rtol mean|ref| (relative error with a floor) on the
+    finite entries; non-finite entries (an fp16 overflow) must be identical."""
     y = np.asarray(y, np.float64)
     ref = np.asarray(ref, np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(y), np.isnan(ref)), "NaN pattern differs"
+    assert np.array_equal(y[~fin & ~np.isnan(ref)], ref[~fin & ~np.isnan(ref)]), "infinities differ"
+    assert np.isfinite(y[fin]).all(), "non-finite output where the reference is finite"
+    y, ref = y[fin], ref[fin]
     atol = rtol * float(np.mean(np.abs(ref))) if ref.size else 0.0
     bad = np.abs(y - ref) > rtol * np.abs(ref) + atol
     assert not bad.any(), (f"{bad.sum()} of {bad.size} outside tolerance; worst "
