@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
         amax = wave_max(amax);
         const float xs = amax / 127.0f;
         if (lane == 0) scale[m] = xs;
-        const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+        const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(1024) void ln_quant_rows(const uint16_t* __restrict
         const float xs = a / 127.0f;
         if (live) {
             if (tid == 0) scale[m] = xs;
-            const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+            const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
                 if (!valid[i]) continue;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(1024) void ln_quant_long(const uint16_t* __restrict
         for (int w = 1; w < nw; ++w) a = __builtin_fmaxf(a, fred[w]);
         const float xs = a / 127.0f;
         if (threadIdx.x == 0) scale[m] = xs;
-        const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+        const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
         for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
             const U16x8 h = __builtin_bit_cast(U16x8, src[c]);
             int q[8];

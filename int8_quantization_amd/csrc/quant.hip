@@ -181,7 +181,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
         for (int e = 0; e < VEC; ++e) {
             if constexpr (MODE == 1) {
                 const float sj = s[cc * VEC + e];
-                rs[i][e] = 1.0 / (double)sj;
+                rs[i][e] = rcp64((double)sj);
                 guard = guard || !(sj < 0x1p100f);
             }
             if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
         const float xs = a / (FMT == 0 ? 127.0f : 448.0f);
         if (live) {
             if (tid == 0) scale[m] = xs;
-            const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+            const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
                 if (!valid[i]) continue;
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void tensor_code_kernel(const T* __restrict__ 
     using V = typename Chunk<T>::V;
     constexpr int VEC = Chunk<T>::N;
     const float sc = __uint_as_float(*gmax) / (FMT == 0 ? 127.0f : 448.0f);
-    const double rx = sc != 0.0f ? 1.0 / (double)sc : 0.0;
+    const double rx = sc != 0.0f ? rcp64((double)sc) : 0.0;
     if (blockIdx.x == 0 && threadIdx.x == 0) *w_scale = sc;
     for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * blockDim.x) {
         V v = reinterpret_cast<const V*>(W)[c];

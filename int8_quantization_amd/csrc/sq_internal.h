@@ -20,12 +20,22 @@ namespace sq {
 // Device helpers
 // ---------------------------------------------------------------------------
 
-// Correctly rounded fp32 quotient a/b from rb = RN64(1/(double)b).
-// t = RN64(a * rb) is within 2^-51.9 (relative) of a/b, while a quotient of two
-// binary32 numbers in the normal range lies at least 2^-49 (relative) away from
-// every binary32 rounding midpoint and is never one itself; so rounding t to
-// binary32 gives the same result as the IEEE division.  Quotients below the
-// normal range take the IEEE division itself.
+// 1/b in fp64 to within 2^-52.9 (relative): v_rcp_f64, then two Newton steps
+// r <- r + r(1 - b r) with fused multiply-adds (each step squares the error and adds
+// at most 2^-53).  Much shorter than the IEEE fp64 division sequence, and accurate
+// enough for div_rcp64 below.
+__device__ __forceinline__ double rcp64(double b) {
+    double r = __builtin_amdgcn_rcp(b);
+    r = __builtin_fma(r, __builtin_fma(-b, r, 1.0), r);
+    return __builtin_fma(r, __builtin_fma(-b, r, 1.0), r);
+}
+
+// Correctly rounded fp32 quotient a/b from rb = rcp64(b), i.e. within 2^-52.9 of 1/b.
+// t = RN64(a * rb) is then within 2^-51.9 (relative) of a/b, while a quotient of two
+// binary32 numbers in the normal range lies at least 2^-49 (relative) away from every
+// binary32 rounding midpoint and is never one itself; so rounding t to binary32 gives
+// the same result as the IEEE division.  Quotients below the normal range take the
+// IEEE division itself.
 __device__ __forceinline__ float div_rcp64(float a, double rb, float b) {
     float q = (float)((double)a * rb);
     if (__builtin_fabsf(q) < 1.17549435e-38f && a != 0.0f) q = a / b;

@@ -58,7 +58,7 @@ struct Cols {
 #pragma unroll
             for (int e = 0; e < N; ++e) {
                 sv[e] = s[c * N + e];
-                rs[e] = 1.0 / (double)sv[e];
+                rs[e] = rcp64((double)sv[e]);
                 guard = guard || !(sv[e] < 0x1p100f);
             }
             if constexpr (sizeof(T) == 4) guard = true;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void static_quant_kernel(const T* __restr
         for (int64_t m = blockIdx.y; m < M; m += gridDim.y) xs_rows[m] = xs_in[0];
     if (c >= nchunk) return;
     const float xs = xs_in[(c * N) / group];
-    const double rx = xs != 0.0f ? 1.0 / (double)xs : 0.0;
+    const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
     Cols<T, SMOOTH> cols;
     cols.init(s, c);
     // rows in batches of RB: the batch's loads are all in flight before its codes are
