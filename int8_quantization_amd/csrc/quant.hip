@@ -7,6 +7,7 @@
 //  - per-tensor weight quantization [basics notes, 量化粒度].
 // All of these are HBM-bound: 16-byte coalesced loads, wave-shuffle reductions,
 // packed int8 stores.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -320,9 +321,13 @@ static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, 
     const int G = 1024 / tpg;                                          // row groups per block
     const int threads = G * tpg;
     auto k = quant_rows_fast<T, VEC, CH, MODE, OUTL, FMT>;
-    static int nb_cache[1025] = {0};
-    int nb = nb_cache[threads];
-    if (nb == 0) nb_cache[threads] = nb = blocks_per_cu(k, threads);
+    // occupancy per block size, computed once (a race between threads only repeats the query)
+    static std::atomic<int> nb_cache[1025];
+    int nb = nb_cache[threads].load(std::memory_order_relaxed);
+    if (nb == 0) {
+        nb = blocks_per_cu(k, threads);
+        nb_cache[threads].store(nb, std::memory_order_relaxed);
+    }
     const int64_t rows_blocks = (M + G - 1) / G;
     const int64_t g = (int64_t)dev_info().cus * nb;
     hipLaunchKernelGGL(k, dim3((unsigned)(g < rows_blocks ? g : rows_blocks)), dim3(threads), 0, st, X, M, K, s, Xq,
