@@ -175,6 +175,43 @@ def bench_fp8(torch, sq, d, wl, steps, warmup):
                 gemm_TOPS=gemm_tops, gemm_mfma_frac=gemm_tops / PEAK_FP8_TOPS)
 
 
+def bench_fp8_decode(torch, sq, d, wl, steps, warmup, copies=3):
+    """FP8 decode rows (M in {1,4,16}) of the 70B FFN-up weight: per-token FP8 codes
+    and the FP8 weight-streaming kernel, three rotated weight copies."""
+    W = wl.weights["w"]
+    N, K = W.shape
+    act = torch.zeros(K, dtype=torch.float32, device="cuda")
+    s = torch.empty(K, dtype=torch.float32, device="cuda")
+    W_d = d(W)
+    sq.sq_smooth_scales(d(wl.calib), W_d, wl.alpha, act, s)
+    Wq0 = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(N, dtype=torch.float32, device="cuda")
+    sq.sq_quantize_weight_fp8(W_d, s, 0, Wq0, ws)
+    del W_d
+    Wqs = [Wq0] + [Wq0.clone() for _ in range(copies - 1)]
+    out = {}
+    for M in wl.decode_rows:
+        X = d(wl.X[:M])
+        Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+        xs = torch.empty(M, dtype=torch.float32, device="cuda")
+        Y = torch.empty(M, N, dtype=torch.float16, device="cuda")
+        it = [0]
+
+        def step(timer):
+            Wq = Wqs[it[0] % copies]
+            it[0] += 1
+            sq.sq_quantize_per_token_fp8(X, s, Xq, xs)
+            g = lambda: sq.fp8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
+            timer.around(g) if timer else g()
+
+        ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
+        _, gemv_ms = time_steps(torch, step, steps, 2)
+        gemv_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
+        out[f"M{M}"] = dict(ms_per_step=ms, gemv_us=gemv_ms * 1e3, gemv_GBps=gemv_bytes / (gemv_ms * 1e-3) / 1e9,
+                            gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+    return out
+
+
 def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
     """M in {1,4,16} against 3 rotated copies of the int8 weight (705 MB > 256 MB MALL)."""
     W = wl.weights["w"]
@@ -458,6 +495,9 @@ def main():
         if args.only in (None, "fp8"):
             log("fp8: 7B prefill projections with FP8 E4M3 codes")
             secondary["fp8_prefill_7b"] = bench_fp8(torch, sq, d, workloads.prefill_7b(), sec_steps, sec_warm)
+            torch.cuda.empty_cache()
+            secondary["fp8_decode_70b"] = bench_fp8_decode(torch, sq, d, workloads.decode_70b(), sec_steps * 2,
+                                                           sec_warm)
             torch.cuda.empty_cache()
         if args.only in (None, "kv_cache"):
             log("kv_cache: 16 x 4096 tokens, 8 heads x 128")

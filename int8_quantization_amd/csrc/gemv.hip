@@ -30,6 +30,15 @@
 // across the chip form a compact front.  Each wave loads the next tile (or
 // chunk) before running the MFMAs of the current one; the 8 partial tiles are
 // summed through LDS and the dequant epilogue stores Y (and acc).
+//
+// FP8 E4M3 variant (FP8 = true): the same loads and tiles; each MFMA,
+// v_mfma_f32_16x16x128_f8f6f4, takes two consecutive steps' 16-byte chunks of a
+// lane concatenated (a zero chunk past an odd step count).  A and B lanes hold
+// the same k bytes in the same operand positions exactly where they do for the
+// int8 instruction, so the diagonal blocks are again the partial products; the
+// partial sums are fp32 and are added in a fixed order.
+#include <type_traits>
+
 #include "sq_internal.h"
 
 namespace sq {
@@ -70,7 +79,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int RPI, int TG, int RG, int PER, bool HOIST, bool OUT_F16>
+template <int RPI, int TG, int RG, int PER, bool HOIST, bool OUT_F16, bool FP8>
 __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
@@ -147,22 +156,39 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
         b.bv = bsrc[bias != nullptr ? n : 0];
     };
 
-    __shared__ v4i part[2][kWaves][RG][TG][64];
-    v4i acc[RG][TG];
+    using AccV = typename std::conditional<FP8, v4f, v4i>::type;
+    __shared__ AccV part[2][kWaves][RG][TG][64];
+    AccV acc[RG][TG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) acc[rg][tg] = v4i{0, 0, 0, 0};
+        for (int tg = 0; tg < TG; ++tg) acc[rg][tg] = AccV{};
 
     // One unit: MFMAs over a chunk, then (last chunk of a tile) the cross-wave sum and epilogue.
+    auto cat = [](const v4i& lo, const v4i& hi) { return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; };
     auto run_unit = [&](int unit, const Buf& b, const v4i (&x)[PER][TG]) {
+        if constexpr (FP8) {
 #pragma unroll
-        for (int s = 0; s < PER; ++s)
+            for (int s = 0; s < PER; s += 2)
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
+                for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-                for (int tg = 0; tg < TG; ++tg)
-                    acc[rg][tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[s][tg], b.w[rg][s], acc[rg][tg], 0, 0, 0);
+                    for (int tg = 0; tg < TG; ++tg) {
+                        const v4i z{0, 0, 0, 0};
+                        const v8i xa = cat(x[s][tg], s + 1 < PER ? x[s + 1][tg] : z);
+                        const v8i wb = cat(b.w[rg][s], s + 1 < PER ? b.w[rg][s + 1] : z);
+                        acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa, wb, acc[rg][tg], 0, 0, 0, 0,
+                                                                                       0, 0);
+                    }
+        } else {
+#pragma unroll
+            for (int s = 0; s < PER; ++s)
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                    for (int tg = 0; tg < TG; ++tg)
+                        acc[rg][tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[s][tg], b.w[rg][s], acc[rg][tg], 0, 0, 0);
+        }
         const int ti = unit / nch;
         if (unit % nch != nch - 1) return;
         const int par = ti & 1;
@@ -172,7 +198,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
 #pragma unroll
             for (int tg = 0; tg < TG; ++tg) {
                 part[par][wave][rg][tg][(lane & 15) * 4 + (lane >> 4)] = acc[rg][tg];
-                acc[rg][tg] = v4i{0, 0, 0, 0};
+                acc[rg][tg] = AccV{};
             }
         // The other parity's buffer is only rewritten after every wave has passed the next barrier,
         // i.e. after every reader of this tile's buffer has finished with it.
@@ -180,8 +206,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
         const int n = (blockIdx.x + ti * gridDim.x) * TROWS + ej;
         if (eact && n < N) {
             const int rg = ej / RPI, jj = ej % RPI, tg = em / RPI, mm = em % RPI;
-            const int* pb = reinterpret_cast<const int*>(&part[par][0][rg][tg][0]);
-            int sum = 0;
+            using Elt = typename std::conditional<FP8, float, int>::type;
+            const Elt* pb = reinterpret_cast<const Elt*>(&part[par][0][rg][tg][0]);
+            Elt sum = 0;
 #pragma unroll
             for (int w8 = 0; w8 < kWaves; ++w8)
 #pragma unroll
@@ -192,7 +219,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
             if (bias != nullptr) y = y + b.bv;
             if constexpr (OUT_F16) reinterpret_cast<_Float16*>(Yv)[(int64_t)em * N + n] = (_Float16)y;
             else reinterpret_cast<float*>(Yv)[(int64_t)em * N + n] = y;
-            if (acc_out != nullptr) acc_out[(int64_t)em * N + n] = sum;
+            if (acc_out != nullptr) acc_out[(int64_t)em * N + n] = __builtin_bit_cast(int32_t, sum);
         }
     };
 
@@ -215,25 +242,24 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     }
 }
 
-template <int RPI, int TG, int RG, int PER, bool HOIST>
+template <int RPI, int TG, int RG, int PER, bool HOIST, bool FP8>
 hipError_t launch_cfg(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                       const float* bias, int M, int N, int K, void* Y, sq_dtype ydt, int32_t* acc_out, int grid,
                       hipStream_t st) {
     if (ydt == SQ_F16)
-        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true>), dim3(grid), dim3(64 * kWaves), 0, st,
-                           Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
+        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true, FP8>), dim3(grid), dim3(64 * kWaves), 0,
+                           st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
     else
-        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false>), dim3(grid), dim3(64 * kWaves), 0, st,
-                           Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
+        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false, FP8>), dim3(grid), dim3(64 * kWaves), 0,
+                           st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
     return hipGetLastError();
 }
 
-}  // namespace
 
-hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
-                       const SideArgs* side, hipStream_t st) {
-    (void)side;
+template <bool FP8>
+hipError_t gemv_dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
+                         const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
+                         hipStream_t st) {
     const int cus = dev_info().cus;
     const int m = (int)M, n = (int)N, k = (int)K;
     // Steps per wave for a load span of `span` bytes; the register-resident chunk is the next power of two.
@@ -243,7 +269,7 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
         return (int)(tiles < (int64_t)per_cu * cus ? tiles : (int64_t)per_cu * cus);
     };
 #define SQ_GEMV(RPI, TG, RG, PER, HOIST, PER_CU) \
-    launch_cfg<RPI, TG, RG, PER, HOIST>(Xq, xs, Wq, ws, ws_stride, bias, m, n, k, Y, ydt, acc_out, \
+    launch_cfg<RPI, TG, RG, PER, HOIST, FP8>(Xq, xs, Wq, ws, ws_stride, bias, m, n, k, Y, ydt, acc_out, \
                                         grid_of(RG * RPI, PER_CU), st)
     if (M <= 4) {
         // 4 rows x 256 bytes per load, one token group.
@@ -269,6 +295,22 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
     if (per <= 8) return SQ_GEMV(8, 2, 2, 8, true, SQ_GV_C_PCU);
     return SQ_GEMV(8, 2, 2, 4, false, SQ_GV_C_PCU);
 #undef SQ_GEMV
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
+                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
+                       const SideArgs* side, hipStream_t st) {
+    (void)side;
+    return gemv_dispatch<false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, st);
+}
+
+hipError_t launch_gemv_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, int ws_stride,
+                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, float* acc_out,
+                           hipStream_t st) {
+    return gemv_dispatch<true>(reinterpret_cast<const int8_t*>(Xq), xs, reinterpret_cast<const int8_t*>(Wq), ws,
+                               ws_stride, bias, M, N, K, Y, ydt, reinterpret_cast<int32_t*>(acc_out), st);
 }
 
 }  // namespace sq

@@ -206,8 +206,10 @@ sq_status fp8_gemm_dequant(const uint8_t* Xq, const float* x_scale, const uint8_
     if (misaligned(Xq) || misaligned(x_scale) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) ||
         (bias && misaligned(bias)) || (acc_out && misaligned(acc_out)))
         return SQ_ERR_ALIGN;
-    return hip_status(launch_gemm_fp8(Xq, x_scale, Wq, w_scale, g == SQ_PER_CHANNEL ? 1 : 0, bias, M, N, K, Y, ydt,
-                                      acc_out, stream));
+    const int stride = g == SQ_PER_CHANNEL ? 1 : 0;
+    if (M <= 16)
+        return hip_status(launch_gemv_fp8(Xq, x_scale, Wq, w_scale, stride, bias, M, N, K, Y, ydt, acc_out, stream));
+    return hip_status(launch_gemm_fp8(Xq, x_scale, Wq, w_scale, stride, bias, M, N, K, Y, ydt, acc_out, stream));
 }
 
 sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,

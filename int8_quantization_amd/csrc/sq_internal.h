@@ -139,6 +139,10 @@ hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
                        sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+// Its FP8 E4M3 variant (fp32 partial sums; acc_out receives their bits).
+hipError_t launch_gemv_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
+                           int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                           sq_dtype ydt, float* acc_out, hipStream_t st);
 
 // LLM.int8(): outlier columns from the column maxima (bit patterns), ascending list,
 // per-column slot (or -1), device-side count; optional copies to user buffers.

@@ -768,7 +768,7 @@ def fp8_acc_bound(orc, Xq, Wq, rows, cols, chunk=256):
     K = Xq.shape[1]
     G = (K + 7) // 8
     u = 2.0 ** -24
-    gam = (G + 8) * u / (1 - (G + 8) * u)
+    gam = (G + 32) * u / (1 - (G + 32) * u)
     out = np.empty(len(rows))
     for i0 in range(0, len(rows), chunk):
         r, c = rows[i0:i0 + chunk], cols[i0:i0 + chunk]
@@ -926,3 +926,53 @@ def test_fp8_accumulation_premise(sq, orc):
     Xc[:, 5] = codes
     acc, _ = gpu_fp8_gemm(sq, Xc, np.ones(256, np.float32), Wq, np.ones(32, np.float32), 0, None, np.float32)
     assert np.array_equal(acc[:, 7], orc.fp8_decode(codes))     # values (-0 sums to +0 from a zero accumulator)
+
+
+@pytest.mark.parametrize("M,N,K,gran,use_bias,out_dt", [
+    (1, 100, 512, 0, False, np.float16), (1, 257, 8192, 0, True, np.float32), (3, 1000, 4112, 1, False, np.float16),
+    (4, 512, 20480, 0, False, np.float16), (8, 777, 1040, 0, True, np.float16), (13, 300, 16400, 0, False, np.float32),
+    (16, 1024, 8192, 1, True, np.float16), (16, 64, 16, 0, False, np.float16)])
+def test_fp8_decode(sq, orc, M, N, K, gran, use_bias, out_dt):
+    """M <= 16 runs on the weight-streaming kernel's FP8 path."""
+    r = np.random.default_rng(M * 11 + N + K)
+    X = (r.standard_normal((M, K)) * 2).astype(np.float16)
+    W = (r.standard_normal((N, K)) * 0.05).astype(np.float16)
+    Xq, xs = orc.fp8_quantize_per_token(X, None)
+    Wq, ws = orc.fp8_quantize_weight(W, None, gran)
+    bias = r.standard_normal(N).astype(np.float32) if use_bias else None
+    acc, Y = gpu_fp8_gemm(sq, Xq, xs, Wq, ws, gran, bias, out_dt)
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    rr, cc = rr.ravel(), cc.ravel()
+    exact, _ = orc.gemm_fp8_sampled(Xq, Wq, rr, cc)
+    check_fp8_acc(orc, acc.ravel(), exact, Xq, Wq, rr, cc, "fp8 decode acc")
+    y = orc.fp8_dequant_sampled(exact, xs, ws, gran, bias, rr, cc).reshape(M, N)
+    assert_close(Y, orc.float_to_half(y) if out_dt == np.float16 else y, 1e-2 if out_dt == np.float16 else 1e-3)
+    y2 = orc.fp8_dequant_sampled(acc.astype(np.float64).ravel(), xs, ws, gran, bias, rr, cc).reshape(M, N)
+    assert_bits_equal(Y, orc.float_to_half(y2) if out_dt == np.float16 else y2, "epilogue from acc")
+    Y2 = gpu_fp8_gemm(sq, Xq, xs, Wq, ws, gran, bias, out_dt, want_acc=False)[1]
+    assert_bits_equal(Y2, Y, "repeat run")
+
+
+def test_fp8_full_decode_70b(sq, orc):
+    """The 70B FFN-up decode rows (M = 1, 4, 16 of 28672 x 8192) in FP8 through the
+    decode kernel: codes bit-exact, accumulators within the bound and outputs within
+    tolerance on sampled entries."""
+    wl = workloads.decode_70b()
+    W = wl.weights["w"]
+    _, s = orc.smooth_scales(wl.calib, W, wl.alpha)
+    Wq, ws = gpu_fp8_quant_weight(sq, W, s, 0)
+    Wq_r, ws_r = orc.fp8_quantize_weight(W, s, 0)
+    assert_bits_equal(ws, ws_r, "w scales")
+    assert_bits_equal(Wq, Wq_r, "w codes")
+    for m in wl.decode_rows:
+        X = wl.X[:m]
+        Xq, xs = gpu_fp8_quant_rows(sq, X, s)
+        Xq_r, xs_r = orc.fp8_quantize_per_token(X, s)
+        assert_bits_equal(Xq, Xq_r, "x codes")
+        acc, Y = gpu_fp8_gemm(sq, Xq, xs, Wq, ws, 0, None, np.float16)
+        N = W.shape[0]
+        rr, cc = sample_positions(m, N, 4000)
+        exact, _ = orc.gemm_fp8_sampled(Xq_r, Wq_r, rr, cc)
+        check_fp8_acc(orc, acc[rr, cc], exact, Xq_r, Wq_r, rr, cc, f"M={m} acc")
+        y = orc.fp8_dequant_sampled(exact, xs_r, ws_r, 0, None, rr, cc)
+        assert_close(Y[rr, cc], orc.float_to_half(y), 1e-2)
