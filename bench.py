@@ -206,9 +206,18 @@ def bench_fp8_decode(torch, sq, d, wl, steps, warmup, copies=3):
 
         ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
         _, gemv_ms = time_steps(torch, step, steps, 2)
+
+        def gemv_only(timer):
+            Wq = Wqs[it[0] % copies]
+            it[0] += 1
+            sq.fp8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
+
+        b2b_ms, _ = time_steps(torch, gemv_only, steps, 2, kernel_events=False)
         gemv_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
         out[f"M{M}"] = dict(ms_per_step=ms, gemv_us=gemv_ms * 1e3, gemv_GBps=gemv_bytes / (gemv_ms * 1e-3) / 1e9,
-                            gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+                            gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            gemv_b2b_us=b2b_ms * 1e3,
+                            gemv_b2b_hbm_frac=gemv_bytes / (b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
     return out
 
 
@@ -233,16 +242,38 @@ def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
             g = lambda: sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
             timer.around(g) if timer else g()
 
-        # the step alone (no per-kernel events in the timed region), then the GEMV launches on their own
+        # the step alone (no per-kernel events in the timed region), then the GEMV launches on their own:
+        # each bracketed by events (dispatch included), and back to back (the stream's kernel rate)
         ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
         _, gemv_ms = time_steps(torch, step, steps, 2)
+
+        def gemv_only(timer):
+            Wq = Wqs[it[0] % copies]
+            it[0] += 1
+            sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
+
+        b2b_ms, _ = time_steps(torch, gemv_only, steps, 2, kernel_events=False)
+        # the same step as one call (M <= 4: quantization in the decode kernel's prologue)
+        lws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_LINEAR, M, N, K), dtype=torch.uint8, device="cuda")
+
+        def linear(timer):
+            Wq = Wqs[it[0] % copies]
+            it[0] += 1
+            sq.sq_w8a8_linear(X, s, Wq, ws, 0, None, Y, lws, xs)
+
+        lin_ms, _ = time_steps(torch, linear, steps, 2, kernel_events=False)
         nbytes = N * K + 4 * N + 2 * M * K + 2 * M * K + 4 * M + 2 * M * N
         gemv_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
         out[f"M{M}"] = dict(ms_per_step=ms, GBps=nbytes / (ms * 1e-3) / 1e9,
                             hbm_frac=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             gemv_us=gemv_ms * 1e3,
                             gemv_GBps=gemv_bytes / (gemv_ms * 1e-3) / 1e9,
-                            gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+                            gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            gemv_b2b_us=b2b_ms * 1e3,
+                            gemv_b2b_hbm_frac=gemv_bytes / (b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            linear_one_call_us=lin_ms * 1e3,
+                            linear_one_call_hbm_frac=(N * K + 4 * N + 2 * M * K + 2 * M * N) / (lin_ms * 1e-3) / 1e9
+                            / PEAK_HBM_GBS)
     out["gemv_traffic_bytes_per_launch"] = traffic_for("gemv_decode_70b", GEMV_SRC)
     return out
 

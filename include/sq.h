@@ -72,7 +72,7 @@ typedef enum {
 
 typedef enum { SQ_F32 = 0, SQ_F16 = 1 } sq_dtype;
 typedef enum { SQ_PER_CHANNEL = 0, SQ_PER_TENSOR = 1 } sq_wgran;
-typedef enum { SQ_OP_QUANT_WEIGHT = 0, SQ_OP_OUTLIER = 1, SQ_OP_CALIB_STATIC = 2 } sq_op;
+typedef enum { SQ_OP_QUANT_WEIGHT = 0, SQ_OP_OUTLIER = 1, SQ_OP_CALIB_STATIC = 2, SQ_OP_LINEAR = 3 } sq_op;
 
 /* Static, human-readable name of a status code. */
 const char* sq_status_string(sq_status st);
@@ -82,6 +82,7 @@ const char* sq_status_string(sq_status st);
  *   SQ_OP_OUTLIER:      for int8_outlier_matmul; sized for the worst case of
  *                       all K columns being outliers: (M + N) * K * 2 + 16 * K + 1024.
  *   SQ_OP_CALIB_STATIC: for sq_calibrate_static_scale (N ignored): 8448 bytes.
+ *   SQ_OP_LINEAR:       for sq_w8a8_linear: M * K and 4 * M bytes, each rounded up to 256.
  * Returns 0 for an unknown op or sizes out of range. */
 size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K);
 
@@ -147,6 +148,24 @@ sq_status w8a8_gemm_dequant(const int8_t* Xq, const float* x_scale, const int8_t
                             const float* w_scale, sq_wgran g, const float* bias,
                             int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
                             int32_t* acc_out, hipStream_t stream);
+
+/* The whole W8A8 layer for one activation batch: per-token quantization of X (with the
+ * smoothing division) and the GEMM with the dequantizing epilogue, in one call.
+ * [SmoothQuant page, section 3.4: the forward of the quantized linear layer, scaling,
+ *  quantization, INT8 GEMM and dequantization.]
+ *   X, xdt, M, K, s  as for sq_quantize_per_token;  Wq, w_scale, g, bias, N, Y, ydt as
+ *                    for w8a8_gemm_dequant.
+ *   x_scale  device float [M] or NULL: receives the per-token scales.
+ *   ws       device workspace >= sq_workspace_size(SQ_OP_LINEAR, M, N, K) (holds Xq; the
+ *            decode case below leaves it untouched).
+ * Results are bit-identical to sq_quantize_per_token followed by w8a8_gemm_dequant.
+ * With fp16 X, M <= 2 and K <= 8192 (decode) one kernel does both: every block of the
+ * weight-streaming kernel quantizes the activation rows in its prologue.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
+sq_status sq_w8a8_linear(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
+                         const int8_t* Wq, const float* w_scale, sq_wgran g, const float* bias,
+                         int64_t N, void* Y, sq_dtype ydt, float* x_scale, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /* LLM.int8() linear layer (no smoothing).
  * [LLM.int8() page, section 2.1: column-wise absmax of the input, columns above

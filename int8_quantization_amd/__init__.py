@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
 
 SQ_F32, SQ_F16 = 0, 1
 SQ_PER_CHANNEL, SQ_PER_TENSOR = 0, 1
-SQ_OP_QUANT_WEIGHT, SQ_OP_OUTLIER, SQ_OP_CALIB_STATIC = 0, 1, 2
+SQ_OP_QUANT_WEIGHT, SQ_OP_OUTLIER, SQ_OP_CALIB_STATIC, SQ_OP_LINEAR = 0, 1, 2, 3
 
 
 class SqError(RuntimeError):
@@ -46,6 +46,7 @@ def _load():
         "sq_layernorm_quantize_per_token": (I, [P, I, I64, I64, P, P, F, P, P, P]),
         "sq_calibrate_static_scale": (I, [P, I, I64, I64, P, C.c_double, P, P, SZ, P]),
         "sq_quantize_static": (I, [P, I, I64, I64, P, P, P, P, P]),
+        "sq_w8a8_linear": (I, [P, I, I64, I64, P, P, P, I, P, I64, P, I, P, P, SZ, P]),
         "sq_quantize_per_token_fp8": (I, [P, I, I64, I64, P, P, P, P]),
         "sq_quantize_weight_fp8": (I, [P, I, I64, I64, P, I, P, P, P, SZ, P]),
         "fp8_gemm_dequant": (I, [P, P, P, P, I, P, I64, I64, I64, P, I, P, P]),
@@ -66,7 +67,7 @@ EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quan
            "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
            "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static",
            "sq_kv_calibrate_per_head", "sq_kv_quantize_per_head", "sq_dequantize", "sq_quantize_per_token_fp8",
-           "sq_quantize_weight_fp8", "fp8_gemm_dequant")
+           "sq_quantize_weight_fp8", "fp8_gemm_dequant", "sq_w8a8_linear")
 
 
 def _p(t):
@@ -228,3 +229,14 @@ def fp8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
     _check("fp8_gemm_dequant", _lib.fp8_gemm_dequant(
         _p(Xq), _p(x_scale), _p(Wq), _p(w_scale), int(gran), _p(bias), M, N, K, _p(Y), _dt(Y),
         _p(acc_out), _stream()))
+
+
+def sq_w8a8_linear(X, s, Wq, w_scale, gran, bias, Y, ws, x_scale=None):
+    """Per-token quantization of X (with smoothing s) and the W8A8 GEMM + dequant in one call."""
+    _dense(X, s, Wq, w_scale, bias, Y, ws, x_scale)
+    M, K = X.shape
+    N = Wq.shape[0]
+    nbytes = ws.numel() * ws.element_size()
+    _check("sq_w8a8_linear", _lib.sq_w8a8_linear(
+        _p(X), _dt(X), M, K, _p(s), _p(Wq), _p(w_scale), int(gran), _p(bias), N, _p(Y), _dt(Y), _p(x_scale),
+        _p(ws), nbytes, _stream()))

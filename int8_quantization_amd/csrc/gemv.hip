@@ -37,6 +37,8 @@
 // the same k bytes in the same operand positions exactly where they do for the
 // int8 instruction, so the diagonal blocks are again the partial products; the
 // partial sums are fp32 and are added in a fixed order.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "sq_internal.h"
@@ -72,6 +74,14 @@ constexpr int kWaves = 8;
 #define SQ_GV_C_PCU 1
 #endif
 
+// Inputs of the fused decode layer (FUSED kernels only): the fp16 activations, the
+// smoothing factors (or null) and an optional output for the per-token scales.
+struct FusedIn {
+    const _Float16* X;
+    const float* s;
+    float* xs_out;
+};
+
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
@@ -79,11 +89,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int RPI, int TG, int RG, int PER, bool HOIST, bool OUT_F16, bool FP8>
+template <int RPI, int TG, int RG, int PER, bool HOIST, bool OUT_F16, bool FP8, int FUSED>
 __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
-    void* __restrict__ Yv, int32_t* __restrict__ acc_out) {
+    void* __restrict__ Yv, int32_t* __restrict__ acc_out, FusedIn fin) {
+    static_assert(!FUSED || (HOIST && TG == 1 && RPI == 4 && !FP8), "fused decode: M <= 2, register-resident X");
     constexpr int SPAN = 1024 / RPI;      // bytes of one row per load instruction
     constexpr int TROWS = RG * RPI;       // weight rows per tile
     constexpr int NB = 16 / RPI;          // diagonal blocks of one MFMA output
@@ -118,6 +129,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
         v4i x[PER][TG];
         float wsv, bv;
     };
+    extern __shared__ __attribute__((aligned(16))) int8_t sxq[];   // FUSED: the block's copy of Xq [M x K]
     auto load_x = [&](int ch, v4i (&x)[PER][TG]) {
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
@@ -125,15 +137,109 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
 #pragma unroll
             for (int tg = 0; tg < TG; ++tg) {
                 const int m = tg * RPI + lrow;
-                const uint32_t off = (k >= 0 && m < M) ? (uint32_t)(m * K + k) : kOut;
-                x[s][tg] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+                if constexpr (FUSED) {
+                    x[s][tg] = (k >= 0 && m < M) ? *reinterpret_cast<const v4i*>(sxq + m * K + k) : v4i{0, 0, 0, 0};
+                } else {
+                    const uint32_t off = (k >= 0 && m < M) ? (uint32_t)(m * K + k) : kOut;
+                    x[s][tg] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+                }
             }
         }
     };
-    // Epilogue role of this thread: output (token em, tile row ej) when active.
+    // Fused decode: every block quantizes the (one or two) activation rows itself, exactly as
+    // the per-token quantizer does (x' = fl32(x / s_j) by the fp64 reciprocal product,
+    // xs = fl32(max |x'| / 127), codes of fl32(x' / xs)), into LDS.  Thread t owns the
+    // 16 columns [16t, 16t + 16) of every row (K <= 8192); the row maxima meet in LDS.
+    __shared__ float sred[kWaves][4];
+    __shared__ float sxs[4];
+    // The loads of X and s are issued first, then the first weight unit's, so the
+    // prologue's arithmetic overlaps the weight latency.
+    constexpr int MR = FUSED > 0 ? FUSED : 1;   // rows (tokens) of the fused layer
+    const int c0 = (int)threadIdx.x * 16;
+    const bool fact = FUSED > 0 && c0 < K;
+    h8 fxv[MR][2];
+    v4f fsv[4];
+    auto fused_load = [&]() {
+        if (!fact) return;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const h8* src = reinterpret_cast<const h8*>(fin.X + (int64_t)m * K + c0);
+            fxv[m][0] = src[0];
+            fxv[m][1] = src[1];
+        }
+        if (fin.s != nullptr)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fsv[q] = reinterpret_cast<const v4f*>(fin.s + c0)[q];
+    };
+    auto fused_compute = [&]() {
+        static_assert(FUSED <= 4, "at most 4 fused rows");
+        float xp[MR][16];
+        if (fact) {
+            // the smoothing division: the fp64 reciprocal product, with the IEEE division only
+            // where a quotient could leave the normal range (some s_j >= 2^100)
+            if (fin.s != nullptr) {
+                bool guard = false;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) guard = guard || !(fsv[e >> 2][e & 3] < 0x1p100f);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float sj = fsv[e >> 2][e & 3];
+                    const double r = rcp64((double)sj);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        const float x = (float)fxv[m][e >> 3][e & 7];
+                        xp[m][e] = guard ? div_rcp64(x, r, sj) : (float)((double)x * r);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) xp[m][e] = (float)fxv[m][e >> 3][e & 7];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float mx = 0.0f;
+            if (fact)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(xp[m][e]));
+            mx = wave_max(mx);
+            if (lane == 0) sred[wave][m] = mx;
+        }
+        lds_barrier();
+        if ((int)threadIdx.x < MR) {
+            float a = sred[0][threadIdx.x];
+            for (int w = 1; w < kWaves; ++w) a = __builtin_fmaxf(a, sred[w][threadIdx.x]);
+            const float x_s = a / 127.0f;
+            sxs[threadIdx.x] = x_s;
+            if (fin.xs_out != nullptr && blockIdx.x == 0) fin.xs_out[threadIdx.x] = x_s;
+        }
+        lds_barrier();
+        if (fact) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float x_s = sxs[m];
+                const double rx = x_s != 0.0f ? rcp64((double)x_s) : 0.0;
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int code = x_s == 0.0f ? 0 : code_of((float)((double)xp[m][4 * q + e] * rx));
+                        v |= (uint32_t)(code & 0xff) << (8 * e);
+                    }
+                    w[q] = v;
+                }
+                *reinterpret_cast<v4i*>(sxq + m * K + c0) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+            }
+        }
+        lds_barrier();
+    };
     const bool eact = (int)threadIdx.x < M * TROWS;
     const int em = eact ? (int)threadIdx.x / TROWS : 0, ej = (int)threadIdx.x % TROWS;
-    const float xsv = xs[em];
+    float xsv = FUSED ? 0.0f : xs[em];   // FUSED: set after the prologue
     const float* bsrc = bias != nullptr ? bias : ws;
     auto load_unit = [&](int unit, Buf& b) {
         const int tile = blockIdx.x + (unit / nch) * gridDim.x;
@@ -224,8 +330,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     };
 
     Buf ba, bb;
-    if (HOIST) load_x(0, ba.x);
-    if (nunits > 0) load_unit(0, ba);
+    if constexpr (FUSED) {
+        fused_load();
+        if (nunits > 0) load_unit(0, ba);
+        fused_compute();
+        xsv = sxs[em];
+        load_x(0, ba.x);
+    } else {
+        if (HOIST) load_x(0, ba.x);
+        if (nunits > 0) load_unit(0, ba);
+    }
     // Drain the prologue loads so that the waits inside the loop count only the loads in flight there.
     __builtin_amdgcn_s_waitcnt(0x0070);
     // Ping-pong between two buffers.  The next unit is always loaded, also past the end (every load of
@@ -242,16 +356,17 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     }
 }
 
-template <int RPI, int TG, int RG, int PER, bool HOIST, bool FP8>
+template <int RPI, int TG, int RG, int PER, bool HOIST, bool FP8, int FUSED = 0>
 hipError_t launch_cfg(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                       const float* bias, int M, int N, int K, void* Y, sq_dtype ydt, int32_t* acc_out, int grid,
-                      hipStream_t st) {
+                      hipStream_t st, FusedIn fin = FusedIn{nullptr, nullptr, nullptr}) {
+    const size_t dyn = FUSED ? (size_t)FUSED * K : 0;   // the block's Xq copy
     if (ydt == SQ_F16)
-        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true, FP8>), dim3(grid), dim3(64 * kWaves), 0,
-                           st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
+        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true, FP8, FUSED>), dim3(grid), dim3(64 * kWaves),
+                           dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin);
     else
-        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false, FP8>), dim3(grid), dim3(64 * kWaves), 0,
-                           st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out);
+        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false, FP8, FUSED>), dim3(grid),
+                           dim3(64 * kWaves), dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin);
     return hipGetLastError();
 }
 
@@ -304,6 +419,50 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
                        const SideArgs* side, hipStream_t st) {
     (void)side;
     return gemv_dispatch<false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, st);
+}
+
+namespace {
+template <int PER, bool OUT_F16, int MR>
+int fused_blocks_per_cu() {
+    static std::atomic<int> cached{0};
+    int nb = cached.load(std::memory_order_relaxed);
+    if (nb == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &nb, gemv_i8_kernel<4, 1, SQ_GV_A_RG, PER, true, OUT_F16, false, MR>, 64 * kWaves, MR * 8192) !=
+                hipSuccess ||
+            nb <= 0)
+            nb = 1;
+        nb = nb < SQ_GV_A_PCU ? nb : SQ_GV_A_PCU;
+        cached.store(nb, std::memory_order_relaxed);
+    }
+    return nb;
+}
+}  // namespace
+
+// Fused decode layer, M <= 2, K <= 8192, fp16 X: quantization in every block's prologue
+// (measured on the 70B FFN-up rows: M = 1 38.2 vs 40.7 us for quantizer + decode kernel,
+// M = 2 39.3 vs 40.4; from M = 3 the prologue costs what the separate launch saves).
+hipError_t launch_linear_decode(const _Float16* X, const float* s, const int8_t* Wq, const float* ws, int ws_stride,
+                                const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                                float* x_scale, hipStream_t st) {
+    const int cus = dev_info().cus;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    const FusedIn fin{X, s, x_scale};
+    const int per = ((k + 255) / 256 + kWaves - 1) / kWaves;
+    const int64_t tiles = (N + SQ_GV_A_RG * 4 - 1) / (SQ_GV_A_RG * 4);
+    // Persistent blocks: as many per CU as are resident at once (the prologue's registers
+    // can lower it below the unfused kernel's count; the LDS copy of Xq, at most 32 KB,
+    // never does).  Queried once per kernel.
+#define SQ_FUSED(PER, MR)                                                                                        \
+    launch_cfg<4, 1, SQ_GV_A_RG, PER, true, false, MR>(                                                          \
+        nullptr, nullptr, Wq, ws, ws_stride, bias, m, n, k, Y, ydt, nullptr,                                     \
+        (int)std::min<int64_t>(tiles, (int64_t)cus * (ydt == SQ_F16 ? fused_blocks_per_cu<PER, true, MR>()      \
+                                                                    : fused_blocks_per_cu<PER, false, MR>())),   \
+        st, fin)
+    if (per <= 1) return m == 1 ? SQ_FUSED(1, 1) : SQ_FUSED(1, 2);
+    if (per <= 2) return m == 1 ? SQ_FUSED(2, 1) : SQ_FUSED(2, 2);
+    return m == 1 ? SQ_FUSED(4, 1) : SQ_FUSED(4, 2);
+#undef SQ_FUSED
 }
 
 hipError_t launch_gemv_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, int ws_stride,

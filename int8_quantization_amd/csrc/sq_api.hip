@@ -79,6 +79,10 @@ size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
         if (bad_shape(M, 1, K)) return 0;
         return kStaticWorkspaceBytes;
     }
+    if (op == SQ_OP_LINEAR) {
+        if (bad_shape(M, N, K)) return 0;
+        return align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
+    }
     return 0;
 }
 
@@ -169,6 +173,28 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, 
     SQ_TRY(launch_gather_cols(static_cast<const _Float16*>(W16), N, K, idx, count, wo, stream));
     SideArgs side{xo, wo, count, K};
     return hip_status(launch_gemm(xq, xs, Wq, w_scale, 1, bias, M, N, K, Y, SQ_F16, acc_out, &side, stream));
+}
+
+sq_status sq_w8a8_linear(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, const int8_t* Wq,
+                         const float* w_scale, sq_wgran g, const float* bias, int64_t N, void* Y, sq_dtype ydt,
+                         float* x_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!X || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt) || bad_dtype(ydt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if (!ws || ws_bytes < sq_workspace_size(SQ_OP_LINEAR, M, N, K)) return SQ_ERR_WORKSPACE;
+    if (misaligned(X) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) || misaligned(ws) ||
+        (s && misaligned(s)) || (bias && misaligned(bias)) || (x_scale && misaligned(x_scale)))
+        return SQ_ERR_ALIGN;
+    const int stride = g == SQ_PER_CHANNEL ? 1 : 0;
+    if (xdt == SQ_F16 && M <= 2 && K <= 8192)
+        return hip_status(launch_linear_decode(static_cast<const _Float16*>(X), s, Wq, w_scale, stride, bias, M, N, K,
+                                               Y, ydt, x_scale, stream));
+    int8_t* xq = static_cast<int8_t*>(ws);
+    float* xs = x_scale ? x_scale : reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)M * K));
+    SQ_TRY(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, xq, xs, nullptr, nullptr, stream));
+    if (M <= 16)
+        return hip_status(launch_gemv(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
+    return hip_status(launch_gemm(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
 }
 
 sq_status sq_quantize_per_token_fp8(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, uint8_t* Xq,

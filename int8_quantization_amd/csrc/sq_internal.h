@@ -139,6 +139,12 @@ hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
                        sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+// Fused decode layer (M <= 2, K <= 8192, fp16 X): per-token quantization of X (with
+// x / s_j when s is given) in every block's prologue, then the decode kernel; x_scale
+// (may be null) receives the per-token scales.
+hipError_t launch_linear_decode(const _Float16* X, const float* s, const int8_t* Wq, const float* ws,
+                                int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                                sq_dtype ydt, float* x_scale, hipStream_t st);
 // Its FP8 E4M3 variant (fp32 partial sums; acc_out receives their bits).
 hipError_t launch_gemv_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
                            int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,

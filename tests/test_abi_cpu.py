@@ -37,6 +37,7 @@ def lib():
     lib.sq_layernorm_quantize_per_token.argtypes = [V, I, I64, I64, V, V, F, V, V, V]
     lib.sq_calibrate_static_scale.argtypes = [V, I, I64, I64, V, C.c_double, V, V, SZ, V]
     lib.sq_quantize_static.argtypes = [V, I, I64, I64, V, V, V, V, V]
+    lib.sq_w8a8_linear.argtypes = [V, I, I64, I64, V, V, V, I, V, I64, V, I, V, V, SZ, V]
     lib.sq_quantize_per_token_fp8.argtypes = [V, I, I64, I64, V, V, V, V]
     lib.sq_quantize_weight_fp8.argtypes = [V, I, I64, I64, V, I, V, V, V, SZ, V]
     lib.fp8_gemm_dequant.argtypes = [V, V, V, V, I, V, I64, I64, I64, V, I, V, V]
@@ -264,3 +265,28 @@ def test_fp8_validation(lib):
     assert g(P, P, P, P, 0, None, 32, 32, 64, P, 9, None, None) == DTYPE
     assert g(P, P, P, P, 0, MIS, 32, 32, 64, P, 1, None, None) == ALIGN
     assert g(P, P, P, P, 0, None, 32, 32, 64, P, 1, MIS, None) == ALIGN
+
+
+def test_linear_validation(lib):
+    f = lib.sq_w8a8_linear
+    need = lib.sq_workspace_size(3, 5, 64, 100 * 16)
+    assert need == 8192 + 256 and lib.sq_workspace_size(3, 5, 64, 1000) == 0     # 5 * 1600 -> 8192, 20 -> 256
+    args = lambda **kw: [kw.get("X", P), kw.get("xdt", 1), kw.get("M", 5), kw.get("K", 1600), kw.get("s", None),
+                         kw.get("Wq", P), kw.get("wsc", P), kw.get("g", 0), kw.get("bias", None), kw.get("N", 64),
+                         kw.get("Y", P), kw.get("ydt", 1), kw.get("xs", None), kw.get("ws", P),
+                         kw.get("nb", need), None]
+    assert f(*args(X=None)) == NULL
+    assert f(*args(Wq=None)) == NULL
+    assert f(*args(wsc=None)) == NULL
+    assert f(*args(Y=None)) == NULL
+    assert f(*args(M=0)) == SHAPE
+    assert f(*args(K=1601)) == SHAPE
+    assert f(*args(N=0)) == SHAPE
+    assert f(*args(xdt=2)) == DTYPE
+    assert f(*args(ydt=3)) == DTYPE
+    assert f(*args(g=2)) == DTYPE
+    assert f(*args(ws=None)) == WORKSPACE
+    assert f(*args(nb=need - 1)) == WORKSPACE
+    assert f(*args(X=MIS)) == ALIGN
+    assert f(*args(xs=MIS)) == ALIGN
+    assert f(*args(bias=MIS)) == ALIGN

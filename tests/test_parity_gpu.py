@@ -976,3 +976,74 @@ def test_fp8_full_decode_70b(sq, orc):
         check_fp8_acc(orc, acc[rr, cc], exact, Xq_r, Wq_r, rr, cc, f"M={m} acc")
         y = orc.fp8_dequant_sampled(exact, xs_r, ws_r, 0, None, rr, cc)
         assert_close(Y[rr, cc], orc.float_to_half(y), 1e-2)
+
+
+# ---------------------------------------------------------------------------
+# The whole layer in one call (SmoothQuant page, section 3.4): fused decode
+# kernel for M <= 4, quantizer + GEMM otherwise
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K,dt,smooth,gran,use_bias,out_dt", [
+    (1, 300, 16, np.float16, True, 0, False, np.float16), (1, 28672, 8192, np.float16, True, 0, False, np.float16),
+    (2, 1000, 1040, np.float16, False, 1, True, np.float32), (3, 777, 4096, np.float16, True, 0, True, np.float16),
+    (4, 4100, 8192, np.float16, True, 0, False, np.float16), (2, 64, 8208, np.float16, True, 0, False, np.float16),
+    (2, 28672, 8192, np.float16, True, 1, True, np.float32), (1, 4100, 8192, np.float16, False, 0, True, np.float16),
+    (3, 500, 2048, np.float32, True, 0, False, np.float16), (5, 1000, 1024, np.float16, True, 0, True, np.float16),
+    (16, 512, 8192, np.float16, True, 0, False, np.float16), (300, 400, 1040, np.float16, True, 0, False, np.float16)])
+def test_w8a8_linear(sq, orc, M, N, K, dt, smooth, gran, use_bias, out_dt):
+    r = np.random.default_rng(M * 13 + N + K)
+    X = (r.standard_normal((M, K)) * r.uniform(0.5, 4.0, (M, 1))).astype(dt)
+    X[:, r.choice(K, max(1, K // 300), replace=False)] *= 40.0
+    if M > 1:
+        X[1] = 0                                                        # an all-zero token
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float16)
+    s = r.uniform(0.1, 10.0, K).astype(np.float32) if smooth else None
+    Wq, ws = orc.quantize_weight(W, s, gran)
+    bias = r.standard_normal(N).astype(np.float32) if use_bias else None
+    Xq_r, xs_r = orc.quantize_per_token(X, s)
+    ydt = torch.float16 if out_dt == np.float16 else torch.float32
+    Y = Guarded((M, N), ydt)
+    xs = Guarded((M,), torch.float32, fill=-1.0)
+    wsp = torch.empty(sq.sq_workspace_size(sq.SQ_OP_LINEAR, M, N, K), dtype=torch.uint8, device="cuda")
+    sq.sq_w8a8_linear(dev(X), None if s is None else dev(s), dev(Wq), dev(ws), gran,
+                      None if bias is None else dev(bias), Y.t, wsp, xs.t)
+    torch.cuda.synchronize()
+    assert_bits_equal(xs.np(), xs_r, "per-token scales")
+    # the two-step path on the same inputs
+    acc2, Y2 = gpu_gemm(sq, Xq_r, xs_r, Wq, ws, gran, bias, out_dt)
+    assert_bits_equal(Y.np(), Y2, "one call vs quantize + GEMM")
+    rr, cc = sample_positions(M, N, 3000)
+    acc_r = orc.gemm_i8_sampled(Xq_r, Wq, rr, cc)
+    assert_bits_equal(acc2[rr, cc], acc_r, "acc (sampled)")
+    y = orc.dequant_sampled(acc_r, xs_r, ws, gran, bias, rr, cc)
+    assert_bits_equal(Y.np()[rr, cc], orc.float_to_half(y) if out_dt == np.float16 else y, "Y vs oracle (sampled)")
+
+
+def test_w8a8_linear_decode_special(sq, orc):
+    """The fused decode prologue on the smoothing divide's edge cases: some s_j >= 2^100
+    (quotients below the fp32 normal range take the IEEE division), fp16 subnormals,
+    signed zeros, and an all-zero token."""
+    K, N = 256, 200
+    r = np.random.default_rng(77)
+    s = r.uniform(0.5, 2.0, K).astype(np.float32)
+    s[3], s[100], s[200] = np.float32(2.0 ** 110), np.float32(2.0 ** 120), np.float32(2.0 ** -20)
+    for M in (1, 2):
+        X = r.standard_normal((M, K)).astype(np.float16)
+        X[0, :8] = np.float16(6e-8)                                      # fp16 subnormals
+        X[0, 8:12] = np.float16(-0.0)
+        X[0, 3], X[0, 100] = np.float16(1000.0), np.float16(-3.0)       # divided by 2^110 / 2^120
+        X[0, 200] = np.float16(1e-3)                                     # divided by 2^-20
+        if M == 2:
+            X[1] = 0
+        W = (r.standard_normal((N, K)) * 0.05).astype(np.float16)
+        Wq, ws = orc.quantize_weight(W, s, 0)
+        Xq_r, xs_r = orc.quantize_per_token(X, s)
+        Y = Guarded((M, N), torch.float16)
+        xs = Guarded((M,), torch.float32, fill=-1.0)
+        wsp = torch.empty(sq.sq_workspace_size(sq.SQ_OP_LINEAR, M, N, K), dtype=torch.uint8, device="cuda")
+        sq.sq_w8a8_linear(dev(X), dev(s), dev(Wq), dev(ws), 0, None, Y.t, wsp, xs.t)
+        torch.cuda.synchronize()
+        assert_bits_equal(xs.np(), xs_r, f"M={M} scales")
+        acc_r = orc.gemm_i8(Xq_r, Wq)
+        rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        y = orc.dequant_sampled(acc_r.ravel(), xs_r, ws, 0, None, rr.ravel(), cc.ravel()).reshape(M, N)
+        assert_bits_equal(Y.np(), orc.float_to_half(y), f"M={M} Y")
