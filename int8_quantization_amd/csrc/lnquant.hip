@@ -6,8 +6,8 @@
 // Offline: gamma' = fl32(gamma / s), beta' = fl32(beta / s).
 // Per forward, for each row of X (binary16, K values):
 //   every finite x is n * 2^-24 with an integer n, |n| < 2^40, so
-//   S1 = sum n (int64) and S2 = sum n^2 (128-bit) are exact and independent of
-//   the order of summation;
+//   S1 = sum n (int64) and S2 = sum n^2 (128-bit, accumulated as two exact fp64
+//   sums) are exact and independent of the order of summation;
 //   mu   = fl64( fl64(S1) / (K * 2^24) )
 //   var  = fl64( fl64(K*S2 - S1^2) / (K^2 * 2^48) )          population variance
 //   rstd = fl64( 1 / fl64(sqrt( fl64(var + eps) )) )
@@ -36,37 +36,36 @@ __device__ __forceinline__ void lds_sync() {
     asm volatile("" ::: "memory");
 }
 
-// Partial sums of one thread.  S1 = sum n: every n is an integer below 2^40 and a
-// thread adds at most 128 of them, so the fp64 sum of x * 2^24 (one FMA per value)
-// stays an integer below 2^53 and is exact; it goes to int64 before the cross-lane
-// reduction.  S2 = sum n^2 as a 128-bit (hi, lo) pair: with significand f (11
-// bits, implicit bit included) and exponent e, n = f << (e - 1) and
-// n^2 = f^2 << (2e - 2), f^2 < 2^22 (a 24-bit multiply): one shift and a carry add.
+// Partial sums of one thread.  Each binary16 x is n * 2^-24 for an integer n with at
+// most 11 significant bits (|n| < 2^40).  S1 = sum n: a thread adds at most 2^13
+// values, so the fp64 sum of x * 2^24 stays an integer below 2^53 and is exact.
+// S2 = sum n^2: n^2 has at most 22 significant bits, so it is exact in fp64, and it is
+// split exactly into q * 2^40 + r with q = floor(n^2 / 2^40) and r = n^2 - q 2^40,
+// both integers below 2^40; their per-thread sums stay below 2^53, exact in fp64.
+// Before the cross-lane reduction the thread's sums become integers: S1 in int64 and
+// S2 = Q 2^40 + R as a 128-bit (hi, lo) pair.
 struct Sums {
     int64_t s1;
     uint64_t lo, hi;
 };
 
 struct Acc {
-    double s1;
-    uint64_t lo, hi;
+    double s1, q, r;
 };
 
-__device__ __forceinline__ void add_half(Acc& t, uint16_t h, float x) {
-    t.s1 = __builtin_fma((double)x, 0x1p24, t.s1);
-    const uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
-    const uint32_t f = e ? 1024u + m : m;
-    const uint32_t s2 = e ? 2 * e - 2 : 0;                     // n^2 = f^2 << s2, s2 <= 58
-    const uint64_t f2 = (uint64_t)(f * f);                     // < 2^22 (a 24-bit multiply)
-    const uint64_t add_lo = f2 << s2;
-    const uint64_t add_hi = s2 ? f2 >> (64 - s2) : 0;
-    const uint64_t lo = t.lo + add_lo;
-    t.hi += add_hi + (lo < add_lo ? 1u : 0u);
-    t.lo = lo;
+__device__ __forceinline__ void add_half(Acc& t, float x) {
+    const double n = (double)x * 0x1p24;                       // exact
+    t.s1 += n;
+    const double n2 = n * n;                                   // exact (22 significant bits)
+    const double q = __builtin_floor(n2 * 0x1p-40);            // exact
+    t.q += q;
+    t.r += __builtin_fma(-q, 0x1p40, n2);                      // exact: n^2 - q 2^40 in [0, 2^40)
 }
 
 __device__ __forceinline__ Sums to_sums(const Acc& a) {
-    return Sums{(int64_t)a.s1, a.lo, a.hi};                   // a.s1 is an exact integer
+    const uint64_t q = (uint64_t)a.q, r = (uint64_t)a.r;      // exact integers below 2^53
+    const uint64_t lo = (q << 40) + r;
+    return Sums{(int64_t)a.s1, lo, (q >> 24) + (lo < r ? 1u : 0u)};
 }
 
 __device__ __forceinline__ Sums wave_sums(Sums t) {
@@ -188,11 +187,11 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
         // the row loop into registers (which would cost the occupancy that hides latency)
         asm volatile("" : "+s"(lbase));
         if constexpr (PF) load(m + nwv, nxt);
-        Acc ta{0.0, 0, 0};
+        Acc ta{0.0, 0.0, 0.0};
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add_half(ta, hbits(cur[i], e), half_bits_to_float(hbits(cur[i], e)));   // zeros add nothing
+            for (int e = 0; e < 8; ++e) add_half(ta, half_bits_to_float(hbits(cur[i], e)));   // zeros add nothing
             __builtin_amdgcn_sched_barrier(0);
         }
         const Sums t = wave_sums(to_sums(ta));
@@ -288,11 +287,11 @@ __global__ __launch_bounds__(1024) void ln_quant_rows(const uint16_t* __restrict
 #pragma unroll
         for (int i = 0; i < CH; ++i) h[i] = __builtin_bit_cast(U16x8, buf[0][i]);
         // exact integer sums
-        Acc ta{0.0, 0, 0};
+        Acc ta{0.0, 0.0, 0.0};
 #pragma unroll
         for (int i = 0; i < CH; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add_half(ta, h[i].v[e], half_bits_to_float(h[i].v[e]));   // zeros for invalid chunks
+            for (int e = 0; e < 8; ++e) add_half(ta, half_bits_to_float(h[i].v[e]));   // zeros for invalid chunks
         Sums t = wave_sums(to_sums(ta));
         if (lane == 0) sred[p][wave] = t;
         lds_sync();
@@ -354,11 +353,11 @@ __global__ __launch_bounds__(1024) void ln_quant_long(const uint16_t* __restrict
         const v4i* src = reinterpret_cast<const v4i*>(X + m * K);
         Sums t{0, 0, 0};
         for (int64_t c0 = threadIdx.x; c0 < nchunk; c0 += 16 * (int64_t)blockDim.x) {
-            Acc ta{0.0, 0, 0};                 // at most 128 values per fp64 partial sum
+            Acc ta{0.0, 0.0, 0.0};             // at most 128 values per fp64 partial sum
             for (int64_t c = c0; c < nchunk && c < c0 + 16 * (int64_t)blockDim.x; c += blockDim.x) {
                 const U16x8 h = __builtin_bit_cast(U16x8, src[c]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) add_half(ta, h.v[e], half_bits_to_float(h.v[e]));
+                for (int e = 0; e < 8; ++e) add_half(ta, half_bits_to_float(h.v[e]));
             }
             add_sums(t, to_sums(ta));
         }
