@@ -8,10 +8,12 @@ int8 MFMA GEMM with the dequant epilogue writing fp16 Y.  Weight preparation
 (calibration, smoothing factors, weight quantization) happens once, before the
 timed region.  Inputs are resident in HBM when timing starts.
 
-value = 2*M*(N_qkv + N_up)*K / step time, in TOPS, quantization included.
+value = 2*M*(N_qkv + N_up)*K / step time, in TOPS, quantization included; the
+timed steps have no events between their kernels.
 roofline: the GEMM kernel, its algorithmic 2MNK ops per launch over its
-average launch time (HIP events around each launch, inside the timed region),
-against the 5.0 POP/s dense int8 MFMA peak.
+average launch time (HIP events around each launch, recorded on the stream the
+library launches on, over a second timed pass of the same steps), against the
+5.0 POP/s dense int8 MFMA peak.
 cpu_baseline: the CPU oracle doing the same per-token work on a bounded
 number of token rows, on this host's cores.
 secondary: the decode (GB/s), LLM.int8() and 530B-slice workloads, same method.
@@ -135,7 +137,10 @@ def bench_w8a8(torch, sq, d, wl, steps, warmup):
             g = lambda: sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, wl.gran, None, Y)
             timer.around(g) if timer else g()
 
-    ms, gemm_ms = time_steps(torch, step, steps, warmup)
+    # the step as a user runs it (no events between its kernels), then the same steps again
+    # with HIP events around each GEMM launch for the kernel's average launch duration
+    ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
+    _, gemm_ms = time_steps(torch, step, steps, 5)
     ops = sum(2.0 * M * p[2].shape[0] * K for p in projs)
     return dict(ms=ms, gemm_ms=gemm_ms, ops=ops, gemm_ops_per_launch=ops / len(projs),
                 Ns=[p[2].shape[0] for p in projs])
@@ -168,7 +173,8 @@ def bench_fp8(torch, sq, d, wl, steps, warmup):
             g = lambda: sq.fp8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
             timer.around(g) if timer else g()
 
-    ms, gemm_ms = time_steps(torch, step, steps, warmup)
+    ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
+    _, gemm_ms = time_steps(torch, step, steps, 5)
     ops = sum(2.0 * M * p[1].shape[0] * K for p in projs)
     gemm_tops = ops / len(projs) / (gemm_ms * 1e-3) / 1e12
     return dict(ms_per_step=ms, TOPS=ops / (ms * 1e-3) / 1e12, gemm_us_per_launch=gemm_ms * 1e3,
@@ -445,7 +451,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones (the clocks settle within about 100 steps)")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
