@@ -99,6 +99,33 @@ def time_steps(torch, step, steps, warmup, kernel_events=True):
     return t0.elapsed_time(t1) / steps, (timer.mean_ms() if timer else None)
 
 
+def step_percentiles(torch, step, n):
+    """p10 / p50 / p90 of single-step times (ms): HIP events between steps only."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        step(None)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    return dict(p10=float(np.percentile(t, 10)), p50=float(np.percentile(t, 50)), p90=float(np.percentile(t, 90)))
+
+
+def gpu_info(torch):
+    """Device name, CU count and the shader clock rocm-smi reports right after the timed
+    steps (best effort; a snapshot, not the sustained clock)."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "cus": p.multi_processor_count}
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        info["sclk_after_timing"] = next(v for k, v in card.items() if "sclk" in k.lower())
+    except Exception as e:   # the tool may be missing or print another format
+        info["sclk_after_timing"] = f"unavailable ({type(e).__name__})"
+    return info
+
+
 def prepare_weight(torch, sq, d, X_cal, W, alpha, gran):
     """Offline: calibration max, smoothing factors, smoothed weight quantization (GPU)."""
     N, K = W.shape
@@ -141,9 +168,16 @@ def bench_w8a8(torch, sq, d, wl, steps, warmup):
     # with HIP events around each GEMM launch for the kernel's average launch duration
     ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
     _, gemm_ms = time_steps(torch, step, steps, 5)
+    pct = step_percentiles(torch, step, steps)
+    # the fused smoothing + per-token quantizer on its own (2MK + MK + 4M bytes)
+    s0 = projs[0][1]
+    q_ms, _ = time_steps(torch, lambda t: sq.sq_quantize_per_token(X, s0, Xq, xs), steps, 5, kernel_events=False)
+    qb = 3 * M * K + 4 * M
     ops = sum(2.0 * M * p[2].shape[0] * K for p in projs)
     return dict(ms=ms, gemm_ms=gemm_ms, ops=ops, gemm_ops_per_launch=ops / len(projs),
-                Ns=[p[2].shape[0] for p in projs])
+                Ns=[p[2].shape[0] for p in projs], pct=pct,
+                quantize=dict(us=q_ms * 1e3, GBps=qb / (q_ms * 1e-3) / 1e9,
+                              hbm_frac=qb / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS))
 
 
 def bench_fp8(torch, sq, d, wl, steps, warmup):
@@ -259,6 +293,10 @@ def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
             sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
 
         b2b_ms, _ = time_steps(torch, gemv_only, steps, 2, kernel_events=False)
+        # warm cache: the same weight copy every step (it stays in the 256 MB MALL)
+        warm_ms, _ = time_steps(torch, lambda t: (sq.sq_quantize_per_token(X, s, Xq, xs),
+                                                  sq.w8a8_gemm_dequant(Xq, xs, Wq0, ws, 0, None, Y)),
+                                steps, 2, kernel_events=False)
         # the same step as one call (M <= 4: quantization in the decode kernel's prologue)
         lws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_LINEAR, M, N, K), dtype=torch.uint8, device="cuda")
 
@@ -277,6 +315,7 @@ def bench_decode(torch, sq, d, wl, steps, warmup, copies=3):
                             gemv_hbm_frac=gemv_bytes / (gemv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             gemv_b2b_us=b2b_ms * 1e3,
                             gemv_b2b_hbm_frac=gemv_bytes / (b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            warm_cache_step_us=warm_ms * 1e3,
                             linear_one_call_us=lin_ms * 1e3,
                             linear_one_call_hbm_frac=(N * K + 4 * N + 2 * M * K + 2 * M * N) / (lin_ms * 1e-3) / 1e9
                             / PEAK_HBM_GBS)
@@ -504,6 +543,9 @@ def main():
                        "weight_scale": "per_channel", "act_scale": "per_token", "out_dtype": "fp16",
                        "parallelism": "single_gpu"},
             "mfma_frac_incl_quant": round(tops / PEAK_INT8_TOPS, 4),
+            "step_ms_percentiles": {k: round(v, 5) for k, v in r["pct"].items()},
+            "quantize_7b": r["quantize"],
+            "gpu": gpu_info(torch),
             "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                          "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                          "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue)",
