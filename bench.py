@@ -117,6 +117,10 @@ def gpu_info(torch):
     import subprocess
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "cus": p.multi_processor_count}
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        # under rocprofv3 the child process would start with the profiler's library loaded
+        info["sclk_after_timing"] = "not read under a profiler"
+        return info
     try:
         out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20).stdout
         card = next(iter(json.loads(out).values()))
