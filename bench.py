@@ -507,7 +507,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs the layer on a single MI355X).", flush=True)
+              "(the layer runs on a single MI355X).", flush=True)
         sys.exit(2)
 
     import torch
