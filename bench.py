@@ -463,10 +463,49 @@ def bench_kv_cache(torch, sq, d, steps, warmup, copies=3, batch=16):
                                    hbm_frac=db / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_one_thread(wl, rows=16):
+    """The oracle's forward path (quantize, int8 GEMM, dequant, store; LLM.int8()
+    adds its outlier split and fp16 side product) on one thread, over the first
+    `rows` token rows.  Weight preparation runs beforehand on every thread, untimed."""
+    import oracle
+    prepared = []
+    for W in wl.weights.values():
+        s = oracle.smooth_scales(wl.calib, W, wl.alpha)[1] if wl.alpha is not None else None
+        prepared.append((W,) + (s,) + tuple(oracle.quantize_weight(W, s, wl.gran)))
+    rows = min(rows, wl.X.shape[0])
+    sel = np.arange(rows)
+    n0 = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        for W, s, Wq, ws in prepared:
+            if wl.threshold is not None:
+                oracle.llm_int8_linear(wl.X, W, Wq, ws, wl.threshold, None, sel)
+            else:
+                oracle.w8a8_linear(wl.X[:rows], s, Wq, ws, wl.gran, None, wl.out_dtype)
+        t = time.perf_counter() - t
+    finally:
+        oracle.set_num_threads(n0)
+    ops = sum(2.0 * rows * W.shape[0] * W.shape[1] for W in wl.weights.values())
+    return dict(rows=rows, seconds=round(t, 3), GOPs=round(ops / t / 1e9, 3))
+
+
 def cpu_baseline(wl, target_s):
     """The oracle on the same per-token work (quantize + int8 GEMM + dequant +
     fp16 store, every projection) for a bounded number of token rows."""
     import oracle
+    import workloads
     prepared = []
     for name, W in wl.weights.items():
         s = oracle.smooth_scales(wl.calib, W, wl.alpha)[1] if wl.alpha is not None else None
@@ -487,7 +526,10 @@ def cpu_baseline(wl, target_s):
     ops = sum(2.0 * rows * W.shape[0] * K for W in wl.weights.values())
     return dict(value=ops / t / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
                 sample=f"first {rows} of {wl.X.shape[0]} token rows, all {len(wl.weights)} projections "
-                       f"({ops / 1e9:.1f} GOP in {t:.1f} s)")
+                       f"({ops / 1e9:.1f} GOP in {t:.1f} s)",
+                cpu_model=cpu_model(),
+                one_thread={"single_w8a8_16x512x512": oracle_one_thread(workloads.single_w8a8()),
+                            wl.name + "_16_rows": oracle_one_thread(wl)})
 
 
 def main():
@@ -564,10 +606,18 @@ def main():
         sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
         if args.only in (None, "decode_70b"):
             log("decode_70b: generating inputs")
-            secondary["decode_70b"] = bench_decode(torch, sq, d, workloads.decode_70b(), sec_steps * 2, sec_warm)
+            wl3 = workloads.decode_70b()
+            secondary["decode_70b"] = bench_decode(torch, sq, d, wl3, sec_steps * 2, sec_warm)
+            if not args.no_cpu_baseline:
+                secondary["decode_70b"]["cpu_oracle_one_thread"] = oracle_one_thread(wl3)
+            del wl3
         if args.only in (None, "llm_int8"):
             log("llm_int8: generating inputs")
-            secondary["llm_int8"] = bench_llm_int8(torch, sq, d, workloads.llm_int8_4096(), sec_steps, sec_warm)
+            wl4 = workloads.llm_int8_4096()
+            secondary["llm_int8"] = bench_llm_int8(torch, sq, d, wl4, sec_steps, sec_warm)
+            if not args.no_cpu_baseline:
+                secondary["llm_int8"]["cpu_oracle_one_thread"] = oracle_one_thread(wl4)
+            del wl4
         if args.only in (None, "layernorm_quant"):
             log("layernorm_quant: prefill activation")
             secondary["layernorm_quant_7b"] = bench_layernorm_quant(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
@@ -593,6 +643,8 @@ def main():
             r = bench_w8a8(torch, sq, d, wl5, sec_steps, sec_warm)
             secondary["slice_530b"] = dict(ms_per_step=r["ms"], TOPS=r["ops"] / (r["ms"] * 1e-3) / 1e12,
                                            gemm_TOPS=r["gemm_ops_per_launch"] / (r["gemm_ms"] * 1e-3) / 1e12)
+            if not args.no_cpu_baseline:
+                secondary["slice_530b"]["cpu_oracle_one_thread"] = oracle_one_thread(wl5)
             del wl5
         torch.cuda.empty_cache()
         result["secondary"] = secondary

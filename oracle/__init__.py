@@ -34,6 +34,7 @@ def _load():
         "orc_half_to_float_array": (None, [P, P, I64]),
         "orc_float_to_half_array": (None, [P, P, I64]),
         "orc_num_threads": (I, []),
+        "orc_set_num_threads": (None, [I]),
         "orc_col_absmax": (None, [P, I, I64, I64, P]),
         "orc_smooth_from_maxima": (None, [P, P, I64, F, P]),
         "orc_smooth_scales": (None, [P, I, I64, P, I, I64, I64, F, P, P]),
@@ -93,6 +94,11 @@ def _fp(a):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (timing only; results do not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def half_to_float(h):

@@ -132,6 +132,16 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Thread count for the OpenMP loops that follow (timing only; results do not depend on it). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* Calibration statistic and smoothing factors (SmoothQuant page,       */
 /* sections 2.1, 3.2, 3.3).                                             */
