@@ -173,6 +173,8 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
     double rs[MODE == 1 ? CH : 1][VEC];
     float sv[MODE == 2 ? CH : 1][VEC];
     unsigned omask[OUTL ? CH : 1];            // bit e: element e of the chunk is an outlier column
+    int opos[OUTL ? CH : 1][OUTL ? VEC : 1];  // its slot among the outlier columns (kept in registers: a
+                                              // load in the row loop would also wait for the row prefetch)
     bool guard = false;                       // some x/s_j may fall below the normal range
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -188,7 +190,8 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
             if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
             if constexpr (OUTL) {
                 if (e == 0) omask[i] = 0;
-                if (valid[i] && pos[cc * VEC + e] >= 0) omask[i] |= 1u << e;
+                opos[i][e] = valid[i] ? pos[cc * VEC + e] : -1;
+                if (opos[i][e] >= 0) omask[i] |= 1u << e;
             }
         }
     }
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
                     bool skip = false;
                     if constexpr (OUTL) {
                         skip = (omask[i] >> e) & 1u;
-                        if (skip && live) Xo[m * K + pos[c * VEC + e]] = (_Float16)rc[i][e];
+                        if (skip && live) Xo[m * K + opos[i][e]] = (_Float16)rc[i][e];
                     }
                     if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
                 }
