@@ -410,7 +410,18 @@ __global__ __launch_bounds__(256) void colmax_kernel(const T* __restrict__ X, in
 #pragma unroll
     for (int e = 0; e < VEC; ++e) mx[e] = 0.0f;
     if (c < nchunk) {
-        for (int64_t r = r0 + lr; r < r1; r += 8) {
+        // 8 rows per batch: the loads of a batch are all in flight before the first max
+        int64_t r = r0 + lr;
+        for (; r + 7 * 8 < r1; r += 8 * 8) {
+            V v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const V*>(X + (r + 8 * u) * K + c * VEC);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) mx[e] = __builtin_fmaxf(mx[e], __builtin_fabsf((float)v[u][e]));
+        }
+        for (; r < r1; r += 8) {
             V v = *reinterpret_cast<const V*>(X + r * K + c * VEC);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) mx[e] = __builtin_fmaxf(mx[e], __builtin_fabsf((float)v[e]));
