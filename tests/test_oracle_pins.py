@@ -840,3 +840,24 @@ def test_fp8_linear_error_bound(orc):
     p2x, p2w = np.exp2(np.arange(-2, 30) % 5 - 2).astype(np.float32), np.exp2(np.arange(48) % 3 - 1).astype(np.float32)
     yd = orc.fp8_dequant_sampled(acc.ravel(), p2x, p2w, 0, None, rr.ravel(), cc.ravel()).reshape(32, 48)
     assert np.array_equal(yd, (acc.astype(np.float32) * p2x[:, None]) * p2w[None, :])
+
+
+def test_results_do_not_depend_on_thread_count(orc):
+    """The oracle's OpenMP loops partition rows and columns only; every output must be
+    bit-identical on one thread and on all of them (the bench times it both ways)."""
+    rng = np.random.default_rng(7)
+    X = (rng.standard_normal((37, 1040)) * 3).astype(np.float16)
+    W = (rng.standard_normal((129, 1040)) * 0.02).astype(np.float16)
+    n0 = orc.num_threads()
+    outs = []
+    for n in (1, max(2, n0)):
+        orc.set_num_threads(n)
+        try:
+            s = orc.smooth_scales(X, W, 0.5)[1]
+            Wq, ws = orc.quantize_weight(W, s, 0)
+            outs.append((s, Wq, ws) + tuple(orc.w8a8_linear(X, s, Wq, ws, 0, None, np.float16)))
+        finally:
+            orc.set_num_threads(n0)
+    for a, b in zip(*outs):
+        assert a.dtype == b.dtype and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert orc.num_threads() == n0
