@@ -238,6 +238,45 @@ def test_gemm_column_split_sampled(sq, orc, gran, use_bias, out_dt):
         assert_bits_equal(Y[r, cc], half(orc.dequant_sampled(a, xs, ws, gran, bias, r, cc)), f"Y column {c}")
 
 
+def test_two_streams_at_once(sq):
+    """No hidden per-call state: two layers (tile kernel and decode kernel) running at once
+    on two streams give the same bits as each run alone."""
+    rng = np.random.default_rng(11)
+    ins = []
+    for (M, N, K) in [(300, 520, 4112), (16, 4100, 8192)]:
+        X = rng.standard_normal((M, K)).astype(np.float16)
+        Wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+        ws = (rng.random(N) * 1e-3).astype(np.float32)
+        ins.append((dev(X), dev(Wq), dev(ws)))
+
+    def run(X, Wq, ws):
+        M, K = X.shape
+        N = Wq.shape[0]
+        Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        xs = torch.empty(M, dtype=torch.float32, device="cuda")
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        sq.sq_quantize_per_token(X, None, Xq, xs)
+        sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y, acc)
+        return Xq, xs, Y, acc
+
+    alone = []
+    for a in ins:
+        alone.append(run(*a))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in ins]      # default priority
+    for _ in range(3):
+        together = []
+        for a, st in zip(ins, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                together.append(run(*a))
+        torch.cuda.synchronize()
+        for x, y in zip(alone, together):
+            for u, v in zip(x, y):
+                assert torch.equal(u, v)
+
+
 def test_gemm_deterministic(sq):
     Xq, xs, Wq, ws, _ = _gemm_case(3, 640, 1024, 2048, 0)
     outs = [gpu_gemm(sq, Xq, xs, Wq, ws, 0, None, np.float16) for _ in range(3)]
