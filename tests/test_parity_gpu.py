@@ -1086,3 +1086,75 @@ def test_w8a8_linear_decode_special(sq, orc):
         rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
         y = orc.dequant_sampled(acc_r.ravel(), xs_r, ws, 0, None, rr.ravel(), cc.ravel()).reshape(M, N)
         assert_bits_equal(Y.np(), orc.float_to_half(y), f"M={M} Y")
+
+
+def test_graph_replay(sq):
+    """Captured in a HIP graph (torch.cuda.CUDAGraph), the two-step decode layer, the fused
+    one-call layer and the LLM.int8() layer (whose outlier count stays on the device) replay
+    to the eager bits.  Each replay gets new inputs copied in first, with eager work and
+    synchronisation between replays."""
+    rng = np.random.default_rng(5)
+    M, N, K = 16, 1000, 4096
+    Wq = dev(rng.integers(-127, 128, (N, K), dtype=np.int8))
+    ws = dev((rng.random(N) * 1e-3).astype(np.float32))
+    s = dev(rng.uniform(0.5, 2.0, K).astype(np.float32))
+    X = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    X1 = torch.empty((1, K), dtype=torch.float16, device="cuda")
+    Y1 = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    xs1 = torch.empty(1, dtype=torch.float32, device="cuda")
+    wsp1 = torch.empty(sq.sq_workspace_size(sq.SQ_OP_LINEAR, 1, N, K), dtype=torch.uint8, device="cuda")
+    M3, N3, K3 = 64, 256, 512
+    W16 = (rng.standard_normal((N3, K3)) * 0.02).astype(np.float16)
+    W16d = dev(W16)
+    Wq3 = dev(rng.integers(-127, 128, (N3, K3), dtype=np.int8))
+    ws3 = dev((rng.random(N3) * 1e-3).astype(np.float32))
+    X3 = torch.empty((M3, K3), dtype=torch.float16, device="cuda")
+    Y3 = torch.empty((M3, N3), dtype=torch.float16, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsp3 = torch.empty(sq.sq_workspace_size(sq.SQ_OP_OUTLIER, M3, N3, K3), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sq.sq_quantize_per_token(X, s, Xq, xs)
+        sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Y)
+        sq.sq_w8a8_linear(X1, s, Wq, ws, 0, None, Y1, wsp1, xs1)
+        sq.int8_outlier_matmul(X3, W16d, Wq3, ws3, None, 6.0, Y3, wsp3, cnt)
+
+    def fill(seed):
+        r = np.random.default_rng(seed)
+        X.copy_(dev(r.standard_normal((M, K)).astype(np.float16)))
+        X1.copy_(dev(r.standard_normal((1, K)).astype(np.float16)))
+        x3 = r.standard_normal((M3, K3)).astype(np.float16)
+        x3[:, r.choice(K3, 1 + seed % 5, replace=False)] = np.float16(30.0)   # outlier set changes per seed
+        X3.copy_(dev(x3))
+
+    def outs():
+        return [t.clone() for t in (Xq, xs, Y, Y1, xs1, Y3, cnt)]
+
+    fill(0)
+    side = torch.cuda.Stream()                  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                  # warm-up off the capture (occupancy queries, first launches)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        fill(seed)
+        step()
+        torch.cuda.synchronize()
+        ref = outs()
+        fill(seed + 100)
+        step()                                  # eager work between replays, on other inputs
+        torch.cuda.synchronize()
+        fill(seed)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs()):
+            assert torch.equal(a, b)
+        assert int(cnt.item()) == 1 + seed % 5
