@@ -290,3 +290,14 @@ def test_linear_validation(lib):
     assert f(*args(X=MIS)) == ALIGN
     assert f(*args(xs=MIS)) == ALIGN
     assert f(*args(bias=MIS)) == ALIGN
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so, before any GPU call."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout
