@@ -180,6 +180,21 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
     for (int i = 0; i < CH; ++i) {
         const int64_t c = tid + (int64_t)i * tpg;
         const int64_t cc = valid[i] ? c : 0;
+        if constexpr (OUTL) {
+            // the chunk's VEC slots in 16-byte loads: every block reads this same small array at
+            // start-up, and one 4-byte load per element made that a hot spot in L2
+            static_assert(VEC % 4 == 0, "slot loads are 16 bytes");
+            omask[i] = 0;
+#pragma unroll
+            for (int q = 0; q < VEC / 4; ++q) {
+                const v4i pq = valid[i] ? *reinterpret_cast<const v4i*>(pos + cc * VEC + 4 * q) : v4i{-1, -1, -1, -1};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    opos[i][4 * q + u] = pq[u];
+                    if (pq[u] >= 0) omask[i] |= 1u << (4 * q + u);
+                }
+            }
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             if constexpr (MODE == 1) {
@@ -188,11 +203,6 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
                 guard = guard || !(sj < 0x1p100f);
             }
             if constexpr (MODE == 2) sv[i][e] = s[cc * VEC + e];
-            if constexpr (OUTL) {
-                if (e == 0) omask[i] = 0;
-                opos[i][e] = valid[i] ? pos[cc * VEC + e] : -1;
-                if (opos[i][e] >= 0) omask[i] |= 1u << e;
-            }
         }
     }
     if constexpr (sizeof(T) == 4) guard = true;   // fp32 inputs can be subnormal
