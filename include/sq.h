@@ -82,8 +82,8 @@ const char* sq_status_string(sq_status st);
  *   SQ_OP_OUTLIER:      for int8_outlier_matmul; sized for the worst case of
  *                       all K columns being outliers: (M + N) * K * 2 fp16 side panels,
  *                       M * K int8 codes, 4 * M scales, 12 * K bytes of column data and a
- *                       16-byte count,
- *                       each region rounded up to 256 bytes (under 2 KB in total).
+ *                       16-byte count, each region rounded up to 256 bytes (under 2 KB
+ *                       of padding in total).
  *   SQ_OP_CALIB_STATIC: for sq_calibrate_static_scale (N ignored): 8448 bytes.
  *   SQ_OP_LINEAR:       for sq_w8a8_linear: M * K and 4 * M bytes, each rounded up to 256.
  * Returns 0 for an unknown op or sizes out of range. */
