@@ -1,22 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized INT8 linear layer on one MI355X.
 
-One step = one forward of the W8A8 layer on the 7B-shaped prefill workload:
-for each of the fused QKV (12288 x 4096) and FFN-up (11008 x 4096) weights,
-fused smoothing + per-token quantization of X [2048 x 4096] fp16, then the
-int8 MFMA GEMM with the dequant epilogue writing fp16 Y.  Weight preparation
-(calibration, smoothing factors, weight quantization) happens once, before the
-timed region.  Inputs are resident in HBM when timing starts.
+One step = one forward of the W8A8 layer on the largest single-GPU workload,
+the 530B-class FFN-up column slice (one GPU's share of a tensor-parallel
+layer): fused smoothing (alpha 0.7) + per-token quantization of X
+[4096 x 20480] fp16, then the int8 MFMA GEMM against the per-tensor-quantized
+W [10240 x 20480] with the dequant epilogue writing fp16 Y.  Weight
+preparation (calibration, smoothing factors, weight quantization) happens once,
+before the timed region.  Inputs are resident in HBM when timing starts.
 
-value = 2*M*(N_qkv + N_up)*K / step time, in TOPS, quantization included; the
-timed steps have no events between their kernels.
-roofline: the GEMM kernel, its algorithmic 2MNK ops per launch over its
-average launch time (HIP events around each launch, recorded on the stream the
-library launches on, over a second timed pass of the same steps), against the
-5.0 POP/s dense int8 MFMA peak.
-cpu_baseline: the CPU oracle doing the same per-token work on a bounded
-number of token rows, on this host's cores.
-secondary: the decode (GB/s), LLM.int8() and 530B-slice workloads, same method.
+Before the W warm-up steps the step runs untimed for at least 0.5 s of GPU time
+(the shader clock settles over that time); the JSON line reports how many
+steps that took (clock_settle_steps) and the p10/p50/p90 of single-step times
+beside the mean over the K timed steps, which is `value`.
+
+value = 2*M*N*K / step time, in TOPS, quantization included; the timed steps
+have no events between their kernels.
+roofline: the GEMM kernel (for this shape two launches of the same kernel:
+256 x 256 tiles over the first 8192 output columns, 128 x 128 tiles over the
+last 2048), algorithmic 2MNK ops per call over the call's average duration
+(HIP events around each call, recorded on the stream the library launches on,
+over a second timed pass of the same steps), against the 5.0 POP/s dense int8
+MFMA peak.
+cpu_baseline: the CPU oracle doing the same per-token work on a bounded number
+of token rows, on this host's cores.
+secondary: the 7B prefill projections, decode (GB/s), LLM.int8(), LayerNorm +
+quantization, static scale, FP8 and KV-cache workloads, same method.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -111,23 +120,44 @@ def step_percentiles(torch, step, n):
     return dict(p10=float(np.percentile(t, 10)), p50=float(np.percentile(t, 50)), p90=float(np.percentile(t, 90)))
 
 
+def shader_clock():
+    """The current shader clock level from the amdgpu driver's sysfs table (a plain
+    file read; the line marked '*' is the active level).  Best effort."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return line.split(":", 1)[1].strip(" *\n")
+        except OSError:
+            continue
+    return "unavailable"
+
+
 def gpu_info(torch):
-    """Device name, CU count and the shader clock rocm-smi reports right after the timed
-    steps (best effort; a snapshot, not the sustained clock)."""
-    import subprocess
+    """Device name, CU count and the shader clock level read right after the timed
+    steps (a snapshot, not the sustained clock)."""
     p = torch.cuda.get_device_properties(0)
-    info = {"name": p.name, "cus": p.multi_processor_count}
-    if any(k.startswith("ROCPROF") for k in os.environ):
-        # under rocprofv3 the child process would start with the profiler's library loaded
-        info["sclk_after_timing"] = "not read under a profiler"
-        return info
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        info["sclk_after_timing"] = next(v for k, v in card.items() if "sclk" in k.lower())
-    except Exception as e:   # the tool may be missing or print another format
-        info["sclk_after_timing"] = f"unavailable ({type(e).__name__})"
-    return info
+    return {"name": p.name, "cus": p.multi_processor_count, "sclk_after_timing": shader_clock()}
+
+
+def settle(torch, step, seconds=0.5, min_steps=20, max_steps=5000):
+    """Run the step untimed until `seconds` of GPU time have passed (the shader clock
+    ramps up over roughly that long); returns the number of steps run."""
+    n, batch = 0, min_steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    while n < max_steps:
+        for _ in range(batch):
+            step(None)
+        n += batch
+        t1.record()
+        torch.cuda.synchronize()
+        if t0.elapsed_time(t1) >= seconds * 1e3:
+            break
+    return n
 
 
 def prepare_weight(torch, sq, d, X_cal, W, alpha, gran):
@@ -149,7 +179,7 @@ def prepare_weight(torch, sq, d, X_cal, W, alpha, gran):
     return s, Wq, ws
 
 
-def bench_w8a8(torch, sq, d, wl, steps, warmup):
+def bench_w8a8(torch, sq, d, wl, steps, warmup, settle_s=0.5):
     """Prefill-style W8A8 forward over every weight of the workload."""
     M, K = wl.X.shape
     X = d(wl.X)
@@ -168,18 +198,19 @@ def bench_w8a8(torch, sq, d, wl, steps, warmup):
             g = lambda: sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, wl.gran, None, Y)
             timer.around(g) if timer else g()
 
+    settled = settle(torch, step, settle_s)
     # the step as a user runs it (no events between its kernels), then the same steps again
-    # with HIP events around each GEMM launch for the kernel's average launch duration
+    # with HIP events around each GEMM call for the kernel's average duration
     ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
-    _, gemm_ms = time_steps(torch, step, steps, 5)
     pct = step_percentiles(torch, step, steps)
+    _, gemm_ms = time_steps(torch, step, steps, 5)
     # the fused smoothing + per-token quantizer on its own (2MK + MK + 4M bytes)
     s0 = projs[0][1]
     q_ms, _ = time_steps(torch, lambda t: sq.sq_quantize_per_token(X, s0, Xq, xs), steps, 5, kernel_events=False)
-    qb = 3 * M * K + 4 * M
+    qb = X.element_size() * M * K + M * K + 4 * M
     ops = sum(2.0 * M * p[2].shape[0] * K for p in projs)
     return dict(ms=ms, gemm_ms=gemm_ms, ops=ops, gemm_ops_per_launch=ops / len(projs),
-                Ns=[p[2].shape[0] for p in projs], pct=pct,
+                Ns=[p[2].shape[0] for p in projs], pct=pct, settle_steps=settled,
                 quantize=dict(us=q_ms * 1e3, GBps=qb / (q_ms * 1e-3) / 1e9,
                               hbm_frac=qb / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS))
 
@@ -340,6 +371,7 @@ def bench_llm_int8(torch, sq, d, wl, steps, warmup):
     def step(timer):
         sq.int8_outlier_matmul(Xd, Wd, Wq, ws, None, wl.threshold, Y, wsp, cnt)
 
+    settle(torch, step)
     ms, _ = time_steps(torch, step, steps, warmup)
     ops = 2.0 * M * N * K
     return dict(ms_per_step=ms, TOPS=ops / (ms * 1e-3) / 1e12, mfma_frac=ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
@@ -451,7 +483,7 @@ def bench_kv_cache(torch, sq, d, steps, warmup, copies=3, batch=16):
         j = it[0] % copies
         it[0] += 1
         for i in range(2):
-            sq.sq_dequantize(q[j][i], sc[i], 0, D, Y[j][i])
+            sq.sq_dequantize(q[j][i].view(T, H * D), sc[i], 0, D, Y[j][i])
 
     ms_d, _ = time_steps(torch, deq, steps, warmup, kernel_events=False)
     n = 2 * T * H * D
@@ -535,14 +567,14 @@ def cpu_baseline(wl, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps before the timed ones (the clocks settle within about 100 steps)")
-    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed steps before the timed ones (after the clock-settle phase)")
+    ap.add_argument("--quick", action="store_true", help="headline workload (the 530B slice) only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default=None,
-                    help="run one workload: prefill_7b|decode_70b|llm_int8|slice_530b|layernorm_quant|static_quant|kv_cache|fp8")
+                    help="run one workload: slice_530b|prefill_7b|decode_70b|llm_int8|layernorm_quant|static_quant|kv_cache|fp8")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -573,37 +605,61 @@ def main():
 
     result = {}
     secondary = {}
-    if args.only in (None, "prefill_7b"):
-        log("prefill_7b: generating inputs")
-        wl = workloads.prefill_7b()
-        log("prefill_7b: timing")
+    if args.only in (None, "slice_530b"):
+        log("slice_530b: generating inputs")
+        wl = workloads.slice_530b()
+        log("slice_530b: timing")
         r = bench_w8a8(torch, sq, d, wl, args.steps, args.warmup)
+        M, K, N = wl.M, wl.K, r["Ns"][0]
         tops = r["ops"] / (r["ms"] * 1e-3) / 1e12
         gemm_tops = r["gemm_ops_per_launch"] / (r["gemm_ms"] * 1e-3) / 1e12
-        traffic = traffic_for("gemm_prefill_7b", GEMM_SRC)
+        traffic = traffic_for("gemm_slice_530b", GEMM_SRC)
         result = {
             "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(r["ms"], 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": r["Ns"], "alpha": wl.alpha,
-                       "weight_scale": "per_channel", "act_scale": "per_token", "out_dtype": "fp16",
+            "config": {"workload": wl.name, "M": M, "K": K, "N": N, "alpha": wl.alpha,
+                       "weight_scale": "per_tensor", "act_scale": "per_token", "out_dtype": "fp16",
                        "parallelism": "single_gpu"},
             "mfma_frac_incl_quant": round(tops / PEAK_INT8_TOPS, 4),
+            "clock_settle_steps": r["settle_steps"],
             "step_ms_percentiles": {k: round(v, 5) for k, v in r["pct"].items()},
-            "quantize_7b": r["quantize"],
+            "tops_at_p50": round(r["ops"] / (r["pct"]["p50"] * 1e-3) / 1e12, 2),
+            "quantize_530b": r["quantize"],
             "gpu": gpu_info(torch),
             "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                          "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                         "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue)",
-                         "gemm_us_per_launch": round(r["gemm_ms"] * 1e3, 2),
-                         "algorithmic_ops_per_launch": r["gemm_ops_per_launch"]},
+                         "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue), two launches per call",
+                         "launches": [
+                             {"tiles": "256x256", "output_columns": [0, 8192], "tile_count": 512,
+                              "algorithmic_ops": 2.0 * M * 8192 * K},
+                             {"tiles": "128x128", "output_columns": [8192, N], "tile_count": 512,
+                              "algorithmic_ops": 2.0 * M * (N - 8192) * K}],
+                         "gemm_us_per_call": round(r["gemm_ms"] * 1e3, 2),
+                         "algorithmic_ops_per_call": r["gemm_ops_per_launch"]},
         }
         if not args.no_cpu_baseline:
-            log("prefill_7b: CPU oracle baseline")
+            log("slice_530b: CPU oracle baseline")
             result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-        del wl
+        del wl, r
+        torch.cuda.empty_cache()
     if not args.quick:
         sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
+        if args.only in (None, "prefill_7b"):
+            log("prefill_7b: generating inputs")
+            wl2 = workloads.prefill_7b()
+            r = bench_w8a8(torch, sq, d, wl2, sec_steps * 2, sec_warm)
+            gemm_tops = r["gemm_ops_per_launch"] / (r["gemm_ms"] * 1e-3) / 1e12
+            tops = r["ops"] / (r["ms"] * 1e-3) / 1e12
+            secondary["prefill_7b"] = dict(
+                workload=wl2.name, ms_per_step=r["ms"], TOPS=tops, mfma_frac_incl_quant=tops / PEAK_INT8_TOPS,
+                step_ms_percentiles=r["pct"], gemm_us_per_launch=r["gemm_ms"] * 1e3, gemm_TOPS=gemm_tops,
+                gemm_mfma_frac=gemm_tops / PEAK_INT8_TOPS, quantize_7b=r["quantize"],
+                gemm_traffic_bytes_per_launch=traffic_for("gemm_prefill_7b", GEMM_SRC))
+            if not args.no_cpu_baseline:
+                secondary["prefill_7b"]["cpu_oracle_one_thread"] = oracle_one_thread(wl2)
+            del wl2
+            torch.cuda.empty_cache()
         if args.only in (None, "decode_70b"):
             log("decode_70b: generating inputs")
             wl3 = workloads.decode_70b()
@@ -637,15 +693,6 @@ def main():
             log("kv_cache: 16 x 4096 tokens, 8 heads x 128")
             secondary["kv_cache"] = bench_kv_cache(torch, sq, d, sec_steps * 2, sec_warm)
             torch.cuda.empty_cache()
-        if args.only in (None, "slice_530b"):
-            log("slice_530b: generating inputs")
-            wl5 = workloads.slice_530b()
-            r = bench_w8a8(torch, sq, d, wl5, sec_steps, sec_warm)
-            secondary["slice_530b"] = dict(ms_per_step=r["ms"], TOPS=r["ops"] / (r["ms"] * 1e-3) / 1e12,
-                                           gemm_TOPS=r["gemm_ops_per_launch"] / (r["gemm_ms"] * 1e-3) / 1e12)
-            if not args.no_cpu_baseline:
-                secondary["slice_530b"]["cpu_oracle_one_thread"] = oracle_one_thread(wl5)
-            del wl5
         torch.cuda.empty_cache()
         result["secondary"] = secondary
     if not result.get("metric"):
