@@ -86,10 +86,59 @@ def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dense(*ts):
-    for t in ts:
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+def _on_gpu(t):
+    """True when t lives on the current GPU (the device the library launches on)."""
+    return t.is_cuda and t.device.index == torch.cuda.current_device()
+
+
+F16, F32, I8, U8, I32 = torch.float16, torch.float32, torch.int8, torch.uint8, torch.int32
+FLOAT = (F16, F32)
+
+
+def _need(fn, name, t, dtypes, shape=None, numel=None, min_numel=None, ndim=None, optional=False):
+    """Checks one tensor argument before anything reaches the library: present (unless
+    optional), on the current GPU, contiguous, of an accepted dtype, and of the shape or
+    element count the call implies.  Raises ValueError (TypeError for a non-tensor)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{fn}: {name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch.Tensor, got {type(t).__name__}")
+    if not _on_gpu(t):
+        raise ValueError(f"{fn}: {name} must be on the current GPU, got device {t.device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{fn}: {name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{fn}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{fn}: {name} must hold {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{fn}: {name} must hold at least {min_numel} elements, got {t.numel()}")
+
+
+def _workspace(fn, ws):
+    """A workspace is any contiguous tensor on the current GPU; its byte size goes to the
+    library, which rejects one that is too small."""
+    if ws is None:
+        raise ValueError(f"{fn}: workspace is required")
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{fn}: workspace must be a torch.Tensor")
+    if not _on_gpu(ws):
+        raise ValueError(f"{fn}: workspace must be on the current GPU, got device {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError(f"{fn}: workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
+def _gran(fn, gran, N):
+    if int(gran) not in (SQ_PER_CHANNEL, SQ_PER_TENSOR):
+        raise ValueError(f"{fn}: gran must be 0 (per channel) or 1 (per tensor), got {gran}")
+    return N if int(gran) == SQ_PER_CHANNEL else 1
 
 
 def _check(fn, code):
@@ -107,136 +156,220 @@ def sq_workspace_size(op: int, M: int, N: int, K: int) -> int:
 
 def sq_smooth_scales(X_cal, W, alpha, act_max, s):
     """act_max [K] fp32 (running max, in/out); s [K] fp32 out. X_cal or W may be None."""
-    _dense(X_cal, W, act_max, s)
+    fn = "sq_smooth_scales"
+    _need(fn, "act_max", act_max, (F32,), ndim=1)
     K = act_max.shape[0]
+    _need(fn, "X_cal", X_cal, FLOAT, ndim=2, optional=True)
+    if X_cal is not None and X_cal.shape[1] != K:
+        raise ValueError(f"{fn}: X_cal has {X_cal.shape[1]} columns, act_max {K}")
+    _need(fn, "W", W, FLOAT, ndim=2, optional=True)
+    if W is not None and W.shape[1] != K:
+        raise ValueError(f"{fn}: W has {W.shape[1]} columns, act_max {K}")
+    _need(fn, "s", s, (F32,), numel=K, optional=W is None)
     Mc = 0 if X_cal is None else X_cal.shape[0]
     N = 0 if W is None else W.shape[0]
-    _check("sq_smooth_scales", _lib.sq_smooth_scales(
+    _check(fn, _lib.sq_smooth_scales(
         _p(X_cal), SQ_F32 if X_cal is None else _dt(X_cal), Mc, _p(W), SQ_F32 if W is None else _dt(W),
         N, K, float(alpha), _p(act_max), _p(s), _stream()))
 
 
-def sq_quantize_per_token(X, s, Xq, x_scale):
-    _dense(X, s, Xq, x_scale)
+def _rows_in(fn, X, s, dtypes=FLOAT):
+    """[M, K] activation (or weight) rows and the optional smoothing vector s [K]."""
+    _need(fn, "X", X, dtypes, ndim=2)
     M, K = X.shape
-    _check("sq_quantize_per_token", _lib.sq_quantize_per_token(
-        _p(X), _dt(X), M, K, _p(s), _p(Xq), _p(x_scale), _stream()))
+    _need(fn, "s", s, (F32,), numel=K, optional=True)
+    return M, K
+
+
+def sq_quantize_per_token(X, s, Xq, x_scale):
+    fn = "sq_quantize_per_token"
+    M, K = _rows_in(fn, X, s)
+    _need(fn, "Xq", Xq, (I8,), shape=(M, K))
+    _need(fn, "x_scale", x_scale, (F32,), numel=M)
+    _check(fn, _lib.sq_quantize_per_token(_p(X), _dt(X), M, K, _p(s), _p(Xq), _p(x_scale), _stream()))
 
 
 def sq_quantize_weight(W, s, gran, Wq, w_scale, ws=None):
-    _dense(W, s, Wq, w_scale, ws)
-    N, K = W.shape
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("sq_quantize_weight", _lib.sq_quantize_weight(
+    fn = "sq_quantize_weight"
+    N, K = _rows_in(fn, W, s)
+    _need(fn, "Wq", Wq, (I8,), shape=(N, K))
+    _need(fn, "w_scale", w_scale, (F32,), numel=_gran(fn, gran, N))
+    nbytes = 0 if ws is None else _workspace(fn, ws)
+    _check(fn, _lib.sq_quantize_weight(
         _p(W), _dt(W), N, K, _p(s), int(gran), _p(Wq), _p(w_scale), _p(ws), nbytes, _stream()))
 
 
-def w8a8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
-    _dense(Xq, x_scale, Wq, w_scale, bias, Y, acc_out)
+def _gemm_args(fn, Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out, code_dtype, acc_dtype):
+    _need(fn, "Xq", Xq, (code_dtype,), ndim=2)
     M, K = Xq.shape
+    _need(fn, "Wq", Wq, (code_dtype,), ndim=2)
     N = Wq.shape[0]
-    _check("w8a8_gemm_dequant", _lib.w8a8_gemm_dequant(
+    if Wq.shape[1] != K:
+        raise ValueError(f"{fn}: Wq has {Wq.shape[1]} columns, Xq {K}")
+    _need(fn, "x_scale", x_scale, (F32,), numel=M)
+    _need(fn, "w_scale", w_scale, (F32,), numel=_gran(fn, gran, N))
+    _need(fn, "bias", bias, (F32,), numel=N, optional=True)
+    _need(fn, "Y", Y, FLOAT, shape=(M, N))
+    _need(fn, "acc_out", acc_out, (acc_dtype,), shape=(M, N), optional=True)
+    return M, N, K
+
+
+def w8a8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
+    fn = "w8a8_gemm_dequant"
+    M, N, K = _gemm_args(fn, Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out, I8, I32)
+    _check(fn, _lib.w8a8_gemm_dequant(
         _p(Xq), _p(x_scale), _p(Wq), _p(w_scale), int(gran), _p(bias), M, N, K, _p(Y), _dt(Y),
         _p(acc_out), _stream()))
 
 
 def int8_outlier_matmul(X, W16, Wq, w_scale, bias, threshold, Y, ws, n_outliers=None,
                         outlier_idx=None, acc_out=None):
-    _dense(X, W16, Wq, w_scale, bias, Y, ws, n_outliers, outlier_idx, acc_out)
+    fn = "int8_outlier_matmul"
+    _need(fn, "X", X, (F16,), ndim=2)
     M, K = X.shape
+    _need(fn, "W16", W16, (F16,), ndim=2)
     N = W16.shape[0]
-    nbytes = ws.numel() * ws.element_size()
-    _check("int8_outlier_matmul", _lib.int8_outlier_matmul(
+    if W16.shape[1] != K:
+        raise ValueError(f"{fn}: W16 has {W16.shape[1]} columns, X {K}")
+    _need(fn, "Wq", Wq, (I8,), shape=(N, K))
+    _need(fn, "w_scale", w_scale, (F32,), numel=N)
+    _need(fn, "bias", bias, (F32,), numel=N, optional=True)
+    _need(fn, "Y", Y, (F16,), shape=(M, N))
+    _need(fn, "n_outliers", n_outliers, (I32,), min_numel=1, optional=True)
+    _need(fn, "outlier_idx", outlier_idx, (I32,), min_numel=K, optional=True)
+    _need(fn, "acc_out", acc_out, (I32,), shape=(M, N), optional=True)
+    nbytes = _workspace(fn, ws)
+    _check(fn, _lib.int8_outlier_matmul(
         _p(X), _p(W16), _p(Wq), _p(w_scale), _p(bias), M, N, K, float(threshold), _p(Y), _p(ws),
         nbytes, _p(n_outliers), _p(outlier_idx), _p(acc_out), _stream()))
 
 
 def sq_fold_smoothing_layernorm(gamma, beta, s, gamma_out, beta_out=None):
-    _dense(gamma, beta, s, gamma_out, beta_out)
+    fn = "sq_fold_smoothing_layernorm"
+    _need(fn, "gamma", gamma, (F32,), ndim=1)
     K = gamma.numel()
-    _check("sq_fold_smoothing_layernorm", _lib.sq_fold_smoothing_layernorm(
+    _need(fn, "s", s, (F32,), numel=K)
+    _need(fn, "gamma_out", gamma_out, (F32,), numel=K)
+    _need(fn, "beta", beta, (F32,), numel=K, optional=True)
+    _need(fn, "beta_out", beta_out, (F32,), numel=K, optional=beta is None)
+    if beta is None and beta_out is not None:
+        raise ValueError(f"{fn}: beta_out given without beta")
+    _check(fn, _lib.sq_fold_smoothing_layernorm(
         _p(gamma), _p(beta), _p(s), K, _p(gamma_out), _p(beta_out), _stream()))
 
 
 def sq_layernorm_quantize_per_token(X, gamma, beta, eps, Xq, x_scale):
-    _dense(X, gamma, beta, Xq, x_scale)
+    fn = "sq_layernorm_quantize_per_token"
+    _need(fn, "X", X, (F16,), ndim=2)
     M, K = X.shape
-    _check("sq_layernorm_quantize_per_token", _lib.sq_layernorm_quantize_per_token(
+    _need(fn, "gamma", gamma, (F32,), numel=K)
+    _need(fn, "beta", beta, (F32,), numel=K, optional=True)
+    _need(fn, "Xq", Xq, (I8,), shape=(M, K))
+    _need(fn, "x_scale", x_scale, (F32,), numel=M)
+    _check(fn, _lib.sq_layernorm_quantize_per_token(
         _p(X), _dt(X), M, K, _p(gamma), _p(beta), float(eps), _p(Xq), _p(x_scale), _stream()))
 
 
 def sq_calibrate_static_scale(X_cal, s, percentile, x_scale, ws):
-    _dense(X_cal, s, x_scale, ws)
-    M, K = X_cal.shape
-    nbytes = ws.numel() * ws.element_size()
-    _check("sq_calibrate_static_scale", _lib.sq_calibrate_static_scale(
+    fn = "sq_calibrate_static_scale"
+    M, K = _rows_in(fn, X_cal, s)
+    _need(fn, "x_scale", x_scale, (F32,), min_numel=1)
+    nbytes = _workspace(fn, ws)
+    _check(fn, _lib.sq_calibrate_static_scale(
         _p(X_cal), _dt(X_cal), M, K, _p(s), float(percentile), _p(x_scale), _p(ws), nbytes, _stream()))
 
 
 def sq_quantize_static(X, s, x_scale, Xq, x_scale_rows=None):
-    _dense(X, s, x_scale, Xq, x_scale_rows)
-    M, K = X.shape
-    _check("sq_quantize_static", _lib.sq_quantize_static(
+    fn = "sq_quantize_static"
+    M, K = _rows_in(fn, X, s)
+    _need(fn, "x_scale", x_scale, (F32,), min_numel=1)
+    _need(fn, "Xq", Xq, (I8,), shape=(M, K))
+    _need(fn, "x_scale_rows", x_scale_rows, (F32,), numel=M, optional=True)
+    _check(fn, _lib.sq_quantize_static(
         _p(X), _dt(X), M, K, _p(s), _p(x_scale), _p(Xq), _p(x_scale_rows), _stream()))
 
 
 def sq_kv_calibrate_per_head(KV, margin, scale):
     """KV [T, H, D] fp16/fp32; scale [H] fp32 out."""
-    _dense(KV, scale)
+    fn = "sq_kv_calibrate_per_head"
+    _need(fn, "KV", KV, FLOAT, ndim=3)
     T, H, D = KV.shape
-    _check("sq_kv_calibrate_per_head", _lib.sq_kv_calibrate_per_head(
+    _need(fn, "scale", scale, (F32,), numel=H)
+    _check(fn, _lib.sq_kv_calibrate_per_head(
         _p(KV), _dt(KV), T, H, D, float(margin), _p(scale), _stream()))
 
 
 def sq_kv_quantize_per_head(KV, scale, q):
     """KV [T, H, D] fp16/fp32; scale [H] fp32; q [T, H, D] int8 out."""
-    _dense(KV, scale, q)
+    fn = "sq_kv_quantize_per_head"
+    _need(fn, "KV", KV, FLOAT, ndim=3)
     T, H, D = KV.shape
-    _check("sq_kv_quantize_per_head", _lib.sq_kv_quantize_per_head(
+    _need(fn, "scale", scale, (F32,), numel=H)
+    _need(fn, "q", q, (I8,), shape=(T, H, D))
+    _check(fn, _lib.sq_kv_quantize_per_head(
         _p(KV), _dt(KV), T, H, D, _p(scale), _p(q), _stream()))
 
 
 def sq_dequantize(q, scale, scale_row_stride, group, Y):
-    """q [M, K] int8 (or any shape whose last dimension is K); Y the same shape, fp16/fp32 out."""
-    _dense(q, Y)
+    """q [M, K] int8 (or any shape whose last dimension is K); Y fp16/fp32 out with as many
+    elements, in the same row-major order."""
+    fn = "sq_dequantize"
+    _need(fn, "q", q, (I8,))
+    if q.dim() < 1 or q.numel() == 0:
+        raise ValueError(f"{fn}: q must be non-empty")
     K = q.shape[-1]
     M = q.numel() // K
-    _check("sq_dequantize", _lib.sq_dequantize(
-        _p(q), M, K, _p(scale), int(scale_row_stride), int(group), _p(Y), _dt(Y), _stream()))
+    _need(fn, "Y", Y, FLOAT, numel=q.numel())
+    group, stride = int(group), int(scale_row_stride)
+    if group <= 0 or K % group != 0 or stride < 0:
+        raise ValueError(f"{fn}: group must divide K = {K} and the row stride be >= 0")
+    _need(fn, "scale", scale, (F32,), min_numel=(M - 1) * stride + K // group)
+    _check(fn, _lib.sq_dequantize(
+        _p(q), M, K, _p(scale), stride, group, _p(Y), _dt(Y), _stream()))
 
 
 def sq_quantize_per_token_fp8(X, s, Xq, x_scale):
     """Xq: uint8 [M, K] (FP8 E4M3 code bytes) out; x_scale fp32 [M] out."""
-    _dense(X, s, Xq, x_scale)
-    M, K = X.shape
-    _check("sq_quantize_per_token_fp8", _lib.sq_quantize_per_token_fp8(
+    fn = "sq_quantize_per_token_fp8"
+    M, K = _rows_in(fn, X, s)
+    _need(fn, "Xq", Xq, (U8,), shape=(M, K))
+    _need(fn, "x_scale", x_scale, (F32,), numel=M)
+    _check(fn, _lib.sq_quantize_per_token_fp8(
         _p(X), _dt(X), M, K, _p(s), _p(Xq), _p(x_scale), _stream()))
 
 
 def sq_quantize_weight_fp8(W, s, gran, Wq, w_scale, ws=None):
-    _dense(W, s, Wq, w_scale, ws)
-    N, K = W.shape
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("sq_quantize_weight_fp8", _lib.sq_quantize_weight_fp8(
+    fn = "sq_quantize_weight_fp8"
+    N, K = _rows_in(fn, W, s)
+    _need(fn, "Wq", Wq, (U8,), shape=(N, K))
+    _need(fn, "w_scale", w_scale, (F32,), numel=_gran(fn, gran, N))
+    nbytes = 0 if ws is None else _workspace(fn, ws)
+    _check(fn, _lib.sq_quantize_weight_fp8(
         _p(W), _dt(W), N, K, _p(s), int(gran), _p(Wq), _p(w_scale), _p(ws), nbytes, _stream()))
 
 
 def fp8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
     """Xq uint8 [M, K], Wq uint8 [N, K] (FP8 E4M3 codes); Y fp16/fp32 [M, N]; acc_out fp32 [M, N]."""
-    _dense(Xq, x_scale, Wq, w_scale, bias, Y, acc_out)
-    M, K = Xq.shape
-    N = Wq.shape[0]
-    _check("fp8_gemm_dequant", _lib.fp8_gemm_dequant(
+    fn = "fp8_gemm_dequant"
+    M, N, K = _gemm_args(fn, Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out, U8, F32)
+    _check(fn, _lib.fp8_gemm_dequant(
         _p(Xq), _p(x_scale), _p(Wq), _p(w_scale), int(gran), _p(bias), M, N, K, _p(Y), _dt(Y),
         _p(acc_out), _stream()))
 
 
 def sq_w8a8_linear(X, s, Wq, w_scale, gran, bias, Y, ws, x_scale=None):
     """Per-token quantization of X (with smoothing s) and the W8A8 GEMM + dequant in one call."""
-    _dense(X, s, Wq, w_scale, bias, Y, ws, x_scale)
-    M, K = X.shape
+    fn = "sq_w8a8_linear"
+    M, K = _rows_in(fn, X, s)
+    _need(fn, "Wq", Wq, (I8,), ndim=2)
     N = Wq.shape[0]
-    nbytes = ws.numel() * ws.element_size()
-    _check("sq_w8a8_linear", _lib.sq_w8a8_linear(
+    if Wq.shape[1] != K:
+        raise ValueError(f"{fn}: Wq has {Wq.shape[1]} columns, X {K}")
+    _need(fn, "w_scale", w_scale, (F32,), numel=_gran(fn, gran, N))
+    _need(fn, "bias", bias, (F32,), numel=N, optional=True)
+    _need(fn, "Y", Y, FLOAT, shape=(M, N))
+    _need(fn, "x_scale", x_scale, (F32,), numel=M, optional=True)
+    nbytes = _workspace(fn, ws)
+    _check(fn, _lib.sq_w8a8_linear(
         _p(X), _dt(X), M, K, _p(s), _p(Wq), _p(w_scale), int(gran), _p(bias), N, _p(Y), _dt(Y), _p(x_scale),
         _p(ws), nbytes, _stream()))
