@@ -42,6 +42,8 @@
  *    inside kernels surface at the caller's next synchronization, as in HIP.
  *    Inputs must be finite (NaN/Inf give unspecified codes).
  *  - Sizes: M, N >= 1; 16 <= K <= 131056 and K % 16 == 0.
+ *  - Codes: dtype arguments (xdt, wdt, ydt, dt) are int holding an sq_dtype value and
+ *    granularity arguments (g) an sq_wgran value; any other value returns SQ_ERR_DTYPE.
  *  - Thread safety: calls are reentrant; calls that share output or workspace
  *    buffers must be ordered by the caller (same stream or events).
  */
@@ -70,12 +72,12 @@ typedef enum {
     SQ_ERR_HIP = 7        /* a HIP launch or device query failed */
 } sq_status;
 
-typedef enum { SQ_F32 = 0, SQ_F16 = 1 } sq_dtype;
-typedef enum { SQ_PER_CHANNEL = 0, SQ_PER_TENSOR = 1 } sq_wgran;
+typedef enum { SQ_F32 = 0, SQ_F16 = 1 } sq_dtype;            /* passed as int */
+typedef enum { SQ_PER_CHANNEL = 0, SQ_PER_TENSOR = 1 } sq_wgran;  /* passed as int */
 typedef enum { SQ_OP_QUANT_WEIGHT = 0, SQ_OP_OUTLIER = 1, SQ_OP_CALIB_STATIC = 2, SQ_OP_LINEAR = 3 } sq_op;
 
 /* Static, human-readable name of a status code. */
-const char* sq_status_string(sq_status st);
+const char* sq_status_string(int st);
 
 /* Bytes of device workspace an entry point needs.
  *   SQ_OP_QUANT_WEIGHT: for sq_quantize_weight (M ignored).
@@ -103,8 +105,8 @@ size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K);
  *           pow in fp64 (the device and host pow may differ in the last fp32 ulp).
  *   alpha   in [0, 1].
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_HIP. */
-sq_status sq_smooth_scales(const void* X_cal, sq_dtype xdt, int64_t M_cal,
-                           const void* W, sq_dtype wdt, int64_t N, int64_t K, float alpha,
+sq_status sq_smooth_scales(const void* X_cal, int xdt, int64_t M_cal,
+                           const void* W, int wdt, int64_t N, int64_t K, float alpha,
                            float* act_max, float* s, hipStream_t stream);
 
 /* Fused smoothing + dynamic per-token activation quantization (every forward).
@@ -116,7 +118,7 @@ sq_status sq_smooth_scales(const void* X_cal, sq_dtype xdt, int64_t M_cal,
  *           x'_j = fl32(x_j / s_j) (x_j when s == NULL).
  *   x_scale device, float [M], out: xs = fl32(max_j |x'_j| / 127).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
-sq_status sq_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K,
+sq_status sq_quantize_per_token(const void* X, int xdt, int64_t M, int64_t K,
                                 const float* s, int8_t* Xq, float* x_scale, hipStream_t stream);
 
 /* Weight smoothing + quantization (offline).
@@ -130,8 +132,8 @@ sq_status sq_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t 
  *   ws      device workspace of ws_bytes >= sq_workspace_size(SQ_OP_QUANT_WEIGHT, 0, N, K)
  *           (only SQ_PER_TENSOR uses it; may be NULL for SQ_PER_CHANNEL).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
-sq_status sq_quantize_weight(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s,
-                             sq_wgran g, int8_t* Wq, float* w_scale, void* ws, size_t ws_bytes,
+sq_status sq_quantize_weight(const void* W, int wdt, int64_t N, int64_t K, const float* s,
+                             int g, int8_t* Wq, float* w_scale, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
 /* int8 GEMM with fused dequantization.
@@ -148,8 +150,8 @@ sq_status sq_quantize_weight(const void* W, sq_dtype wdt, int64_t N, int64_t K, 
  * M <= 16 runs a weight-streaming decode kernel; larger M the MFMA tile kernel.
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
 sq_status w8a8_gemm_dequant(const int8_t* Xq, const float* x_scale, const int8_t* Wq,
-                            const float* w_scale, sq_wgran g, const float* bias,
-                            int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                            const float* w_scale, int g, const float* bias,
+                            int64_t M, int64_t N, int64_t K, void* Y, int ydt,
                             int32_t* acc_out, hipStream_t stream);
 
 /* The whole W8A8 layer for one activation batch: per-token quantization of X (with the
@@ -165,9 +167,9 @@ sq_status w8a8_gemm_dequant(const int8_t* Xq, const float* x_scale, const int8_t
  * With fp16 X, M <= 2 and K <= 8192 (decode) one kernel does both: every block of the
  * weight-streaming kernel quantizes the activation rows in its prologue.
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
-sq_status sq_w8a8_linear(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
-                         const int8_t* Wq, const float* w_scale, sq_wgran g, const float* bias,
-                         int64_t N, void* Y, sq_dtype ydt, float* x_scale, void* ws, size_t ws_bytes,
+sq_status sq_w8a8_linear(const void* X, int xdt, int64_t M, int64_t K, const float* s,
+                         const int8_t* Wq, const float* w_scale, int g, const float* bias,
+                         int64_t N, void* Y, int ydt, float* x_scale, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 
 /* LLM.int8() linear layer (no smoothing).
@@ -225,7 +227,7 @@ sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, con
  *   Xq       device int8 [M x K], out: clamp(rne(fl32(y / xs)), -128, 127).
  *   x_scale  device float [M], out: xs = fl32(max_j |y_j| / 127) (0 and all-zero codes when y == 0).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_HIP. */
-sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K,
+sq_status sq_layernorm_quantize_per_token(const void* X, int xdt, int64_t M, int64_t K,
                                           const float* gamma, const float* beta, float eps,
                                           int8_t* Xq, float* x_scale, hipStream_t stream);
 
@@ -242,7 +244,7 @@ sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M
  *   ws         device workspace >= sq_workspace_size(SQ_OP_CALIB_STATIC, M_cal, 0, K).
  * The rank is found by an exact radix select on the device (no host synchronization).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
-sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_cal, int64_t K,
+sq_status sq_calibrate_static_scale(const void* X_cal, int xdt, int64_t M_cal, int64_t K,
                                     const float* s, double percentile, float* x_scale,
                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -255,7 +257,7 @@ sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_c
  *   x_scale_rows  device float [M] or NULL: when given, every entry is set to xs, so the
  *            codes feed w8a8_gemm_dequant unchanged.
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
-sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
+sq_status sq_quantize_static(const void* X, int xdt, int64_t M, int64_t K, const float* s,
                              const float* x_scale, int8_t* Xq, float* x_scale_rows, hipStream_t stream);
 
 /* FP8 W8A8 variant: FP8 E4M3 codes (OCP "e4m3fn": bias 7, 3 mantissa bits, largest
@@ -268,15 +270,15 @@ sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, 
  *   Xq       device uint8 [M x K], out: e4m3(clamp(fl32(x'_j / xs), -448, 448)), nearest even
  *            (0x00 when xs == 0; -0 codes as 0x80).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
-sq_status sq_quantize_per_token_fp8(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s,
+sq_status sq_quantize_per_token_fp8(const void* X, int xdt, int64_t M, int64_t K, const float* s,
                                     uint8_t* Xq, float* x_scale, hipStream_t stream);
 
 /* FP8 E4M3 weight codes of W' = fl32(W * s_j) (or W), per output channel (w_scale [N]) or
  * per tensor (w_scale [1], workspace as for sq_quantize_weight): scale = fl32(max|W'| / 448),
  * codes as in sq_quantize_per_token_fp8.  Arguments as for sq_quantize_weight.
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
-sq_status sq_quantize_weight_fp8(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s,
-                                 sq_wgran g, uint8_t* Wq, float* w_scale, void* ws, size_t ws_bytes,
+sq_status sq_quantize_weight_fp8(const void* W, int wdt, int64_t N, int64_t K, const float* s,
+                                 int g, uint8_t* Wq, float* w_scale, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
 /* FP8 E4M3 GEMM with the dequantizing epilogue (any M; gfx950 FP8 matrix instructions):
@@ -288,8 +290,8 @@ sq_status sq_quantize_weight_fp8(const void* W, sq_dtype wdt, int64_t N, int64_t
  *   receives the fp32 accumulators.
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
 sq_status fp8_gemm_dequant(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
-                           sq_wgran g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                           sq_dtype ydt, float* acc_out, hipStream_t stream);
+                           int g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
+                           int ydt, float* acc_out, hipStream_t stream);
 
 /* INT8 KV cache, per-head calibration (offline or at cache creation).
  * [SmoothQuant page, section 5.2: the KV cache is stored as int8 with one scale per
@@ -301,7 +303,7 @@ sq_status fp8_gemm_dequant(const uint8_t* Xq, const float* x_scale, const uint8_
  *   scale   device float [H], out: scale_h = fl32(fl32(margin * max_{t,d} |x[t,h,d]|) / 127)
  *           (0 for a head that is all zero).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_VALUE, SQ_ERR_HIP. */
-sq_status sq_kv_calibrate_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D,
+sq_status sq_kv_calibrate_per_head(const void* KV, int dt, int64_t T, int64_t H, int64_t D,
                                    float margin, float* scale, hipStream_t stream);
 
 /* INT8 KV cache, quantization with fixed per-head scales (every appended block).
@@ -314,7 +316,7 @@ sq_status sq_kv_calibrate_per_head(const void* KV, sq_dtype dt, int64_t T, int64
  *   Per-token (per row and head) scales instead: sq_quantize_per_token on the
  *   [T*H x D] view, whose row scales are the per-token-per-head scales.
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
-sq_status sq_kv_quantize_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D,
+sq_status sq_kv_quantize_per_head(const void* KV, int dt, int64_t T, int64_t H, int64_t D,
                                   const float* scale, int8_t* q, hipStream_t stream);
 
 /* Dequantization of int8 codes with grouped scales (reading an INT8 KV cache back).
@@ -329,7 +331,7 @@ sq_status sq_kv_quantize_per_head(const void* KV, sq_dtype dt, int64_t T, int64_
  *   Y        device [M x K] in ydt, out: fl32(q * scale) (rounded to nearest even for fp16).
  * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
 sq_status sq_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t scale_row_stride,
-                        int64_t group, void* Y, sq_dtype ydt, hipStream_t stream);
+                        int64_t group, void* Y, int ydt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -525,15 +525,15 @@ hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float*
     const _Float16* Wo = side ? side->Wo : nullptr;
     const int32_t* cnt = side ? side->count : nullptr;
     const int64_t ldo = side ? side->ldo : 0;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE, FP8>), dim3((unsigned)(tm * tn)),
+    SQ_LAUNCH((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE, FP8>), dim3((unsigned)(tm * tn)),
                        dim3(64 * WM * WN), 0, st, Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out,
                        Xo, Wo, cnt, ldo, ldy, tm, tn);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                    const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, sq_dtype ydt,
+                    const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int ydt,
                     int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st) {
     if (fp8) {
         if constexpr (BN == 256) {
@@ -568,7 +568,7 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
 // full rounds take the leading tile columns and the remaining columns go out as
 // a second launch that picks its own tiles, if that is estimated faster.
 hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, sq_dtype ydt,
+                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int ydt,
                        int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st, bool may_split) {
     const int64_t cus = dev_info().cus;
     struct Cand { int bm, bn, per_cu; double rate; };
@@ -623,13 +623,13 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
+                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
     return launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, N, ydt, acc_out, side, false, st, true);
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, int ws_stride,
-                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, float* acc_out,
+                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, float* acc_out,
                            hipStream_t st) {
     return launch_cols(reinterpret_cast<const int8_t*>(Xq), xs, reinterpret_cast<const int8_t*>(Wq), ws, ws_stride,
                        bias, M, N, K, Y, N, ydt, reinterpret_cast<int32_t*>(acc_out), nullptr, true, st, true);

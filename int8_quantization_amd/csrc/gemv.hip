@@ -358,22 +358,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
 
 template <int RPI, int TG, int RG, int PER, bool HOIST, bool FP8, int FUSED = 0>
 hipError_t launch_cfg(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                      const float* bias, int M, int N, int K, void* Y, sq_dtype ydt, int32_t* acc_out, int grid,
+                      const float* bias, int M, int N, int K, void* Y, int ydt, int32_t* acc_out, int grid,
                       hipStream_t st, FusedIn fin = FusedIn{nullptr, nullptr, nullptr}) {
     const size_t dyn = FUSED ? (size_t)FUSED * K : 0;   // the block's Xq copy
     if (ydt == SQ_F16)
-        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true, FP8, FUSED>), dim3(grid), dim3(64 * kWaves),
+        SQ_LAUNCH((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true, FP8, FUSED>), dim3(grid), dim3(64 * kWaves),
                            dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin);
     else
-        hipLaunchKernelGGL((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false, FP8, FUSED>), dim3(grid),
+        SQ_LAUNCH((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false, FP8, FUSED>), dim3(grid),
                            dim3(64 * kWaves), dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 
 template <bool FP8>
 hipError_t gemv_dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                         const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
+                         const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out,
                          hipStream_t st) {
     const int cus = dev_info().cus;
     const int m = (int)M, n = (int)N, k = (int)K;
@@ -415,7 +415,7 @@ hipError_t gemv_dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, co
 }  // namespace
 
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
-                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, int32_t* acc_out,
+                       const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
     (void)side;
     return gemv_dispatch<false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, st);
@@ -443,7 +443,7 @@ int fused_blocks_per_cu() {
 // (measured on the 70B FFN-up rows: M = 1 38.2 vs 40.7 us for quantizer + decode kernel,
 // M = 2 39.3 vs 40.4; from M = 3 the prologue costs what the separate launch saves).
 hipError_t launch_linear_decode(const _Float16* X, const float* s, const int8_t* Wq, const float* ws, int ws_stride,
-                                const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                                const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt,
                                 float* x_scale, hipStream_t st) {
     const int cus = dev_info().cus;
     const int m = (int)M, n = (int)N, k = (int)K;
@@ -466,7 +466,7 @@ hipError_t launch_linear_decode(const _Float16* X, const float* s, const int8_t*
 }
 
 hipError_t launch_gemv_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, int ws_stride,
-                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt, float* acc_out,
+                           const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, float* acc_out,
                            hipStream_t st) {
     return gemv_dispatch<true>(reinterpret_cast<const int8_t*>(Xq), xs, reinterpret_cast<const int8_t*>(Wq), ws,
                                ws_stride, bias, M, N, K, Y, ydt, reinterpret_cast<int32_t*>(acc_out), st);

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_kv_calibrate(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, float margin,
+hipError_t launch_kv_calibrate(const void* KV, int dt, int64_t T, int64_t H, int64_t D, float margin,
                                float* scale, hipStream_t st) {
     uint32_t* bits = reinterpret_cast<uint32_t*>(scale);   // the output holds the maxima meanwhile
     hipError_t e = launch_fill_u32(bits, H, 0u, st);
@@ -112,29 +112,29 @@ hipError_t launch_kv_calibrate(const void* KV, sq_dtype dt, int64_t T, int64_t H
     const int64_t HD = H * D;
     if (dt == SQ_F16) {
         const RowPack g = row_pack(T, HD / 8, 32, 256);
-        hipLaunchKernelGGL(kv_headmax_kernel<_Float16>, g.grid, dim3(256), 0, st, static_cast<const _Float16*>(KV),
+        SQ_LAUNCH(kv_headmax_kernel<_Float16>, g.grid, dim3(256), 0, st, static_cast<const _Float16*>(KV),
                            T, HD, D, bits, g.lgp);
     } else {
         const RowPack g = row_pack(T, HD / 4, 32, 256);
-        hipLaunchKernelGGL(kv_headmax_kernel<float>, g.grid, dim3(256), 0, st, static_cast<const float*>(KV), T,
+        SQ_LAUNCH(kv_headmax_kernel<float>, g.grid, dim3(256), 0, st, static_cast<const float*>(KV), T,
                            HD, D, bits, g.lgp);
     }
-    hipLaunchKernelGGL(kv_scale_kernel, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, st, scale, H, margin);
-    return hipGetLastError();
+    SQ_LAUNCH(kv_scale_kernel, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, st, scale, H, margin);
+    return hipSuccess;
 }
 
 hipError_t launch_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t row_stride,
-                             int64_t group, void* Y, sq_dtype ydt, hipStream_t st) {
+                             int64_t group, void* Y, int ydt, hipStream_t st) {
     if (ydt == SQ_F16) {
         const RowPack g = row_pack(M, K / 8, 8, 2048);
-        hipLaunchKernelGGL(dequant_kernel<_Float16>, g.grid, dim3(256), 0, st, q, M, K, scale, row_stride, group,
+        SQ_LAUNCH(dequant_kernel<_Float16>, g.grid, dim3(256), 0, st, q, M, K, scale, row_stride, group,
                            static_cast<_Float16*>(Y), g.lgp);
     } else {
         const RowPack g = row_pack(M, K / 4, 8, 2048);
-        hipLaunchKernelGGL(dequant_kernel<float>, g.grid, dim3(256), 0, st, q, M, K, scale, row_stride, group,
+        SQ_LAUNCH(dequant_kernel<float>, g.grid, dim3(256), 0, st, q, M, K, scale, row_stride, group,
                            static_cast<float*>(Y), g.lgp);
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sq

@@ -419,9 +419,9 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const float* gam
     const int G = 1024 / tpg;                                          // row groups per block
     const int64_t rows_blocks = (M + G - 1) / G;
     const int64_t cap = (int64_t)dev_info().cus;                       // one 1024-thread block per CU
-    hipLaunchKernelGGL((ln_quant_rows<CH, BETA>), dim3((unsigned)(rows_blocks < cap ? rows_blocks : cap)),
+    SQ_LAUNCH((ln_quant_rows<CH, BETA>), dim3((unsigned)(rows_blocks < cap ? rows_blocks : cap)),
                        dim3(G * tpg), 0, st, X, M, K, gamma, beta, eps, Xq, scale, tpg, G);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <int CPL, bool BETA, bool PF>
@@ -431,9 +431,9 @@ hipError_t launch_wave(const uint16_t* X, int64_t M, int64_t K, const float* gam
     const int64_t blocks = (M + kWaves - 1) / kWaves;
     const int64_t cap = (int64_t)dev_info().cus * 8;
     const size_t lds = (size_t)K * sizeof(float) * (BETA ? 2 : 1);
-    hipLaunchKernelGGL((ln_quant_wave<CPL, BETA, PF>), dim3((unsigned)(blocks < cap ? blocks : cap)),
+    SQ_LAUNCH((ln_quant_wave<CPL, BETA, PF>), dim3((unsigned)(blocks < cap ? blocks : cap)),
                        dim3(64 * kWaves), lds, st, X, M, K, gamma, beta, eps, Xq, scale);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <bool BETA>
@@ -449,9 +449,9 @@ hipError_t launch_ln(const uint16_t* X, int64_t M, int64_t K, const float* gamma
     if (K <= 8192) return launch_wave<16, BETA, false>(X, M, K, gamma, beta, eps, Xq, scale, st);
     if (K <= 16384) return launch_rows<2, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
     const int64_t cap = (int64_t)dev_info().cus * 2;
-    hipLaunchKernelGGL((ln_quant_long<BETA>), dim3((unsigned)(M < cap ? M : cap)), dim3(1024), 0, st, X, M, K,
+    SQ_LAUNCH((ln_quant_long<BETA>), dim3((unsigned)(M < cap ? M : cap)), dim3(1024), 0, st, X, M, K,
                        gamma, beta, eps, Xq, scale);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace
@@ -466,9 +466,9 @@ hipError_t launch_ln_quant(const _Float16* X, int64_t M, int64_t K, const float*
 hipError_t launch_fold_layernorm(const float* gamma, const float* beta, const float* s, int64_t K, float* gamma_out,
                                  float* beta_out, hipStream_t st) {
     const int64_t blocks = (K + 255) / 256;
-    hipLaunchKernelGGL(fold_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, gamma, beta,
+    SQ_LAUNCH(fold_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, gamma, beta,
                        s, K, gamma_out, beta_out);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sq

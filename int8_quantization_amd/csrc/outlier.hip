@@ -90,15 +90,15 @@ __global__ __launch_bounds__(256) void gather_cols_kernel(const _Float16* __rest
 
 hipError_t launch_outlier_compact(const uint32_t* cmax_bits, int64_t K, float threshold, int32_t* idx, int32_t* pos,
                                   int32_t* count, int32_t* user_count, int32_t* user_idx, hipStream_t st) {
-    hipLaunchKernelGGL(outlier_compact_kernel, dim3(1), dim3(1024), 0, st, cmax_bits, K, threshold, idx, pos, count,
+    SQ_LAUNCH(outlier_compact_kernel, dim3(1), dim3(1024), 0, st, cmax_bits, K, threshold, idx, pos, count,
                        user_count, user_idx);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_gather_cols(const _Float16* W16, int64_t N, int64_t K, const int32_t* idx, const int32_t* count,
                               _Float16* Wo, hipStream_t st) {
-    hipLaunchKernelGGL(gather_cols_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, W16, N, K, idx, count, Wo);
-    return hipGetLastError();
+    SQ_LAUNCH(gather_cols_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, W16, N, K, idx, count, Wo);
+    return hipSuccess;
 }
 
 }  // namespace sq

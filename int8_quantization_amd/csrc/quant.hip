@@ -45,8 +45,8 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
-    return hipGetLastError();
+    SQ_LAUNCH(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -343,9 +343,9 @@ static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, 
     }
     const int64_t rows_blocks = (M + G - 1) / G;
     const int64_t g = (int64_t)dev_info().cus * nb;
-    hipLaunchKernelGGL(k, dim3((unsigned)(g < rows_blocks ? g : rows_blocks)), dim3(threads), 0, st, X, M, K, s, Xq,
+    SQ_LAUNCH(k, dim3((unsigned)(g < rows_blocks ? g : rows_blocks)), dim3(threads), 0, st, X, M, K, s, Xq,
                        scale, pos, Xo, tpg, G);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // Register-resident variants by row length (elements per thread <= 20), else the
@@ -367,11 +367,11 @@ static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s,
     }
     auto k = quant_rows_generic<T, MODE, OUTL, FMT>;
     const int64_t g = (int64_t)dev_info().cus * 2;
-    hipLaunchKernelGGL(k, dim3((unsigned)(g < M ? g : M)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
-    return hipGetLastError();
+    SQ_LAUNCH(k, dim3((unsigned)(g < M ? g : M)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
+    return hipSuccess;
 }
 
-hipError_t launch_quant_rows(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, int mode,
+hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const float* s, int mode,
                              int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st, int fmt) {
     const bool outl = pos != nullptr;
     if (fmt == 1) {   // FP8 E4M3 codes (no outlier variant)
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void colmax_kernel(const T* __restrict__ X, in
     }
 }
 
-hipError_t launch_colmax(const void* X, sq_dtype dt, int64_t M, int64_t K, uint32_t* amax_bits, hipStream_t st) {
+hipError_t launch_colmax(const void* X, int dt, int64_t M, int64_t K, uint32_t* amax_bits, hipStream_t st) {
     if (M <= 0) return hipSuccess;
     const int vec = dt == SQ_F16 ? 8 : 4;
     const int64_t nchunk = K / vec;
@@ -458,10 +458,10 @@ hipError_t launch_colmax(const void* X, sq_dtype dt, int64_t M, int64_t K, uint3
     if ((M + rpb - 1) / rpb > 65535) rpb = (M + 65534) / 65535;   // grid.y limit
     dim3 grid((unsigned)((nchunk + 31) / 32), (unsigned)((M + rpb - 1) / rpb));
     if (dt == SQ_F16)
-        hipLaunchKernelGGL(colmax_kernel<_Float16>, grid, dim3(256), 0, st, (const _Float16*)X, M, K, rpb, amax_bits);
+        SQ_LAUNCH(colmax_kernel<_Float16>, grid, dim3(256), 0, st, (const _Float16*)X, M, K, rpb, amax_bits);
     else
-        hipLaunchKernelGGL(colmax_kernel<float>, grid, dim3(256), 0, st, (const float*)X, M, K, rpb, amax_bits);
-    return hipGetLastError();
+        SQ_LAUNCH(colmax_kernel<float>, grid, dim3(256), 0, st, (const float*)X, M, K, rpb, amax_bits);
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -480,9 +480,9 @@ __global__ void smooth_pow_kernel(const float* __restrict__ act_max, float* __re
 }
 
 hipError_t launch_smooth_pow(const float* act_max, float* s_wmax, int64_t K, float alpha, hipStream_t st) {
-    hipLaunchKernelGGL(smooth_pow_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, act_max, s_wmax, K,
+    SQ_LAUNCH(smooth_pow_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, act_max, s_wmax, K,
                        alpha);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -549,16 +549,16 @@ static hipError_t quant_tensor_t(const T* W, int64_t N, int64_t K, const float* 
     const int64_t cap = (int64_t)dev_info().cus * 8;
     if (blocks > cap) blocks = cap;
     if (s) {
-        hipLaunchKernelGGL((tensor_max_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
-        hipLaunchKernelGGL((tensor_code_kernel<T, true, FMT>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
+        SQ_LAUNCH((tensor_max_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
+        SQ_LAUNCH((tensor_code_kernel<T, true, FMT>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
     } else {
-        hipLaunchKernelGGL((tensor_max_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
-        hipLaunchKernelGGL((tensor_code_kernel<T, false, FMT>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
+        SQ_LAUNCH((tensor_max_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax);
+        SQ_LAUNCH((tensor_code_kernel<T, false, FMT>), dim3((unsigned)blocks), dim3(256), 0, st, W, nchunks, kchunks, s, gmax, Wq, w_scale);
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
-hipError_t launch_quant_tensor(const void* W, sq_dtype dt, int64_t N, int64_t K, const float* s, int8_t* Wq,
+hipError_t launch_quant_tensor(const void* W, int dt, int64_t N, int64_t K, const float* s, int8_t* Wq,
                                float* w_scale, uint32_t* gmax_bits, hipStream_t st, int fmt) {
     if (fmt == 1) {
         if (dt == SQ_F16) return quant_tensor_t<_Float16, 1>((const _Float16*)W, N, K, s, Wq, w_scale, gmax_bits, st);

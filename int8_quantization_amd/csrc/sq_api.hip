@@ -50,7 +50,7 @@ OutlierLayout outlier_layout(int64_t M, int64_t N, int64_t K) {
 
 extern "C" {
 
-const char* sq_status_string(sq_status st) {
+const char* sq_status_string(int st) {
     switch (st) {
         case SQ_OK: return "SQ_OK";
         case SQ_ERR_NULL: return "SQ_ERR_NULL: a required pointer is NULL";
@@ -86,7 +86,7 @@ size_t sq_workspace_size(int op, int64_t M, int64_t N, int64_t K) {
     return 0;
 }
 
-sq_status sq_smooth_scales(const void* X_cal, sq_dtype xdt, int64_t M_cal, const void* W, sq_dtype wdt, int64_t N,
+sq_status sq_smooth_scales(const void* X_cal, int xdt, int64_t M_cal, const void* W, int wdt, int64_t N,
                            int64_t K, float alpha, float* act_max, float* s, hipStream_t stream) {
     if (!act_max) return SQ_ERR_NULL;
     if (M_cal > 0 && !X_cal) return SQ_ERR_NULL;
@@ -105,7 +105,7 @@ sq_status sq_smooth_scales(const void* X_cal, sq_dtype xdt, int64_t M_cal, const
     return SQ_OK;
 }
 
-sq_status sq_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, int8_t* Xq,
+sq_status sq_quantize_per_token(const void* X, int xdt, int64_t M, int64_t K, const float* s, int8_t* Xq,
                                 float* x_scale, hipStream_t stream) {
     if (!X || !Xq || !x_scale) return SQ_ERR_NULL;
     if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
@@ -114,7 +114,7 @@ sq_status sq_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t 
     return hip_status(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, Xq, x_scale, nullptr, nullptr, stream));
 }
 
-sq_status sq_quantize_weight(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s, sq_wgran g,
+sq_status sq_quantize_weight(const void* W, int wdt, int64_t N, int64_t K, const float* s, int g,
                              int8_t* Wq, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!W || !Wq || !w_scale) return SQ_ERR_NULL;
     if (bad_shape(1, N, K)) return SQ_ERR_SHAPE;
@@ -130,7 +130,7 @@ sq_status sq_quantize_weight(const void* W, sq_dtype wdt, int64_t N, int64_t K, 
 }
 
 sq_status w8a8_gemm_dequant(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
-                            sq_wgran g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                            int g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt,
                             int32_t* acc_out, hipStream_t stream) {
     if (!Xq || !x_scale || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
     if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
@@ -175,8 +175,8 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, 
     return hip_status(launch_gemm(xq, xs, Wq, w_scale, 1, bias, M, N, K, Y, SQ_F16, acc_out, &side, stream));
 }
 
-sq_status sq_w8a8_linear(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, const int8_t* Wq,
-                         const float* w_scale, sq_wgran g, const float* bias, int64_t N, void* Y, sq_dtype ydt,
+sq_status sq_w8a8_linear(const void* X, int xdt, int64_t M, int64_t K, const float* s, const int8_t* Wq,
+                         const float* w_scale, int g, const float* bias, int64_t N, void* Y, int ydt,
                          float* x_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!X || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
     if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
@@ -197,7 +197,7 @@ sq_status sq_w8a8_linear(const void* X, sq_dtype xdt, int64_t M, int64_t K, cons
     return hip_status(launch_gemm(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
 }
 
-sq_status sq_quantize_per_token_fp8(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, uint8_t* Xq,
+sq_status sq_quantize_per_token_fp8(const void* X, int xdt, int64_t M, int64_t K, const float* s, uint8_t* Xq,
                                     float* x_scale, hipStream_t stream) {
     if (!X || !Xq || !x_scale) return SQ_ERR_NULL;
     if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
@@ -207,7 +207,7 @@ sq_status sq_quantize_per_token_fp8(const void* X, sq_dtype xdt, int64_t M, int6
                                         nullptr, stream, 1));
 }
 
-sq_status sq_quantize_weight_fp8(const void* W, sq_dtype wdt, int64_t N, int64_t K, const float* s, sq_wgran g,
+sq_status sq_quantize_weight_fp8(const void* W, int wdt, int64_t N, int64_t K, const float* s, int g,
                                  uint8_t* Wq, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!W || !Wq || !w_scale) return SQ_ERR_NULL;
     if (bad_shape(1, N, K)) return SQ_ERR_SHAPE;
@@ -224,7 +224,7 @@ sq_status sq_quantize_weight_fp8(const void* W, sq_dtype wdt, int64_t N, int64_t
 }
 
 sq_status fp8_gemm_dequant(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
-                           sq_wgran g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y, sq_dtype ydt,
+                           int g, const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt,
                            float* acc_out, hipStream_t stream) {
     if (!Xq || !x_scale || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
     if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
@@ -247,7 +247,7 @@ sq_status sq_fold_smoothing_layernorm(const float* gamma, const float* beta, con
     return hip_status(launch_fold_layernorm(gamma, beta, s, K, gamma_out, beta_out, stream));
 }
 
-sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* gamma,
+sq_status sq_layernorm_quantize_per_token(const void* X, int xdt, int64_t M, int64_t K, const float* gamma,
                                           const float* beta, float eps, int8_t* Xq, float* x_scale,
                                           hipStream_t stream) {
     if (!X || !gamma || !Xq || !x_scale) return SQ_ERR_NULL;
@@ -259,7 +259,7 @@ sq_status sq_layernorm_quantize_per_token(const void* X, sq_dtype xdt, int64_t M
     return hip_status(launch_ln_quant(static_cast<const _Float16*>(X), M, K, gamma, beta, eps, Xq, x_scale, stream));
 }
 
-sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_cal, int64_t K, const float* s,
+sq_status sq_calibrate_static_scale(const void* X_cal, int xdt, int64_t M_cal, int64_t K, const float* s,
                                     double percentile, float* x_scale, void* ws, size_t ws_bytes,
                                     hipStream_t stream) {
     if (!X_cal || !x_scale) return SQ_ERR_NULL;
@@ -275,7 +275,7 @@ sq_status sq_calibrate_static_scale(const void* X_cal, sq_dtype xdt, int64_t M_c
     return hip_status(launch_static_calibrate(X_cal, xdt, M_cal, K, s, (uint32_t)r, x_scale, ws, stream));
 }
 
-sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, const float* s, const float* x_scale,
+sq_status sq_quantize_static(const void* X, int xdt, int64_t M, int64_t K, const float* s, const float* x_scale,
                              int8_t* Xq, float* x_scale_rows, hipStream_t stream) {
     if (!X || !x_scale || !Xq) return SQ_ERR_NULL;
     if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
@@ -286,7 +286,7 @@ sq_status sq_quantize_static(const void* X, sq_dtype xdt, int64_t M, int64_t K, 
     return hip_status(launch_static_quant(X, xdt, M, K, s, x_scale, K, Xq, x_scale_rows, stream));
 }
 
-sq_status sq_kv_calibrate_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, float margin,
+sq_status sq_kv_calibrate_per_head(const void* KV, int dt, int64_t T, int64_t H, int64_t D, float margin,
                                    float* scale, hipStream_t stream) {
     if (!KV || !scale) return SQ_ERR_NULL;
     if (H < 1 || D < 16 || (D % 16) != 0 || H > kMaxK / D || bad_shape(T, 1, H * D)) return SQ_ERR_SHAPE;
@@ -296,7 +296,7 @@ sq_status sq_kv_calibrate_per_head(const void* KV, sq_dtype dt, int64_t T, int64
     return hip_status(launch_kv_calibrate(KV, dt, T, H, D, margin, scale, stream));
 }
 
-sq_status sq_kv_quantize_per_head(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, const float* scale,
+sq_status sq_kv_quantize_per_head(const void* KV, int dt, int64_t T, int64_t H, int64_t D, const float* scale,
                                   int8_t* q, hipStream_t stream) {
     if (!KV || !scale || !q) return SQ_ERR_NULL;
     if (H < 1 || D < 16 || (D % 16) != 0 || H > kMaxK / D || bad_shape(T, 1, H * D)) return SQ_ERR_SHAPE;
@@ -306,7 +306,7 @@ sq_status sq_kv_quantize_per_head(const void* KV, sq_dtype dt, int64_t T, int64_
 }
 
 sq_status sq_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t scale_row_stride,
-                        int64_t group, void* Y, sq_dtype ydt, hipStream_t stream) {
+                        int64_t group, void* Y, int ydt, hipStream_t stream) {
     if (!q || !scale || !Y) return SQ_ERR_NULL;
     if (bad_shape(M, 1, K) || group < 16 || (group % 16) != 0 || (K % group) != 0 || scale_row_stride < 0 ||
         scale_row_stride > kMaxK)

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "../../include/sq.h"
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -64,6 +67,29 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 // Host-side launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
 
+// Kernel launch that reports this launch's own status, hipLaunchKernel's return value
+// (hipGetLastError() would also return, and clear, an error left by an earlier,
+// unrelated HIP call on the thread).  The arguments are first converted to the
+// kernel's parameter types, because hipLaunchKernel reads each one through a pointer
+// to that type.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t st, A&&... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> vals(static_cast<P>(std::forward<A>(args))...);
+    void* ptrs[sizeof...(P) == 0 ? 1 : sizeof...(P)];
+    std::apply([&ptrs](auto&... v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, st);
+}
+// Launch, and return from the enclosing launcher on a failed launch.
+#define SQ_LAUNCH(...)                                      \
+    do {                                                    \
+        const hipError_t sq_e_ = ::sq::launch(__VA_ARGS__); \
+        if (sq_e_ != hipSuccess) return sq_e_;              \
+    } while (0)
+
 // Device properties cached once per device.
 struct DevInfo {
     int cus;
@@ -101,13 +127,13 @@ inline RowPack row_pack(int64_t M, int64_t nchunk, int64_t rows_per_thread, int6
 // mode 0: no smoothing; 1: x / s_j; 2: x * s_j.  pos/Xo (LLM.int8() only): pos[j] >= 0
 // marks an outlier column, whose value is copied to Xo[m*K + pos[j]] and whose code is 0.
 // fmt 0: int8 codes, scale max/127; fmt 1: FP8 E4M3 code bytes, scale max/448 (no pos).
-hipError_t launch_quant_rows(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s,
+hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const float* s,
                              int mode, int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo,
                              hipStream_t st, int fmt = 0);
 
 // Running column absolute maximum: amax_bits[j] = max(amax_bits[j], bits(max_m |X[m,j]|)),
 // where amax_bits holds non-negative floats as their bit patterns (monotone as uint32).
-hipError_t launch_colmax(const void* X, sq_dtype dt, int64_t M, int64_t K, uint32_t* amax_bits,
+hipError_t launch_colmax(const void* X, int dt, int64_t M, int64_t K, uint32_t* amax_bits,
                          hipStream_t st);
 
 // s_j from act_max and the W column maxima held in s (overwritten in place).
@@ -115,7 +141,7 @@ hipError_t launch_smooth_pow(const float* act_max, float* s_wmax, int64_t K, flo
                              hipStream_t st);
 
 // Per-tensor weight quantization: global max then codes.
-hipError_t launch_quant_tensor(const void* W, sq_dtype dt, int64_t N, int64_t K, const float* s,
+hipError_t launch_quant_tensor(const void* W, int dt, int64_t N, int64_t K, const float* s,
                                int8_t* Wq, float* w_scale, uint32_t* gmax_bits, hipStream_t st, int fmt = 0);
 
 // int8 GEMM + dequant epilogue (M > 16).  side != nullptr adds the LLM.int8() fp16 side
@@ -128,27 +154,27 @@ struct SideArgs {
 };
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                       sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+                       int ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
 // FP8 E4M3 GEMM (fp32 accumulation) + the same dequant epilogue; acc_out receives the
 // fp32 accumulators' bits.
 hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
                            int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                           sq_dtype ydt, float* acc_out, hipStream_t st);
+                           int ydt, float* acc_out, hipStream_t st);
 
 // Weight-streaming decode kernel, M <= 16.
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                       sq_dtype ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+                       int ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
 // Fused decode layer (M <= 2, K <= 8192, fp16 X): per-token quantization of X (with
 // x / s_j when s is given) in every block's prologue, then the decode kernel; x_scale
 // (may be null) receives the per-token scales.
 hipError_t launch_linear_decode(const _Float16* X, const float* s, const int8_t* Wq, const float* ws,
                                 int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                                sq_dtype ydt, float* x_scale, hipStream_t st);
+                                int ydt, float* x_scale, hipStream_t st);
 // Its FP8 E4M3 variant (fp32 partial sums; acc_out receives their bits).
 hipError_t launch_gemv_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws,
                            int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
-                           sq_dtype ydt, float* acc_out, hipStream_t st);
+                           int ydt, float* acc_out, hipStream_t st);
 
 // LLM.int8(): outlier columns from the column maxima (bit patterns), ascending list,
 // per-column slot (or -1), device-side count; optional copies to user buffers.
@@ -168,19 +194,19 @@ hipError_t launch_ln_quant(const _Float16* X, int64_t M, int64_t K, const float*
 // select in the workspace: a 2048-bin histogram, then the selection state).
 constexpr size_t kStaticHistBytes = 2048 * 4;
 constexpr size_t kStaticWorkspaceBytes = 8448;
-hipError_t launch_static_calibrate(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, uint32_t rank,
+hipError_t launch_static_calibrate(const void* X, int dt, int64_t M, int64_t K, const float* s, uint32_t rank,
                                    float* x_scale, void* ws, hipStream_t st);
 // Quantization with calibrated scales: column j uses xs[j / group]; xs_rows (may be null)
 // receives xs[0] per row.
-hipError_t launch_static_quant(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, const float* xs,
+hipError_t launch_static_quant(const void* X, int dt, int64_t M, int64_t K, const float* s, const float* xs,
                                int64_t group, int8_t* Xq, float* xs_rows, hipStream_t st);
 
 // KV cache [T x H x D]: per-head calibration scale_h = fl32(fl32(margin * max|x|) / 127).
-hipError_t launch_kv_calibrate(const void* KV, sq_dtype dt, int64_t T, int64_t H, int64_t D, float margin,
+hipError_t launch_kv_calibrate(const void* KV, int dt, int64_t T, int64_t H, int64_t D, float margin,
                                float* scale, hipStream_t st);
 // y[m, j] = fl32(q[m, j] * scale[m * row_stride + j / group]), stored as ydt.
 hipError_t launch_dequantize(const int8_t* q, int64_t M, int64_t K, const float* scale, int64_t row_stride,
-                             int64_t group, void* Y, sq_dtype ydt, hipStream_t st);
+                             int64_t group, void* Y, int ydt, hipStream_t st);
 
 // gamma_out = gamma / s, beta_out = beta / s (beta may be null).
 hipError_t launch_fold_layernorm(const float* gamma, const float* beta, const float* s, int64_t K,

@@ -242,29 +242,29 @@ hipError_t calibrate_t(const T* X, int64_t M, int64_t K, const float* s, uint32_
     uint32_t* hist = static_cast<uint32_t*>(ws);
     SelState* state = reinterpret_cast<SelState*>(static_cast<char*>(ws) + kStaticHistBytes);
     const dim3 g = grid_of(M, K, Chunk16<T>::N);
-    hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(256), 0, st, hist, state, rank);
-    hipLaunchKernelGGL((hist_kernel<T, SMOOTH, 0>), g, dim3(kThreads), 0, st, X, M, K, s, state, hist);
-    hipLaunchKernelGGL(select_kernel<0>, dim3(1), dim3(1024), 0, st, hist, state);
-    hipLaunchKernelGGL((hist_kernel<T, SMOOTH, 1>), g, dim3(kThreads), 0, st, X, M, K, s, state, hist);
-    hipLaunchKernelGGL(select_kernel<1>, dim3(1), dim3(1024), 0, st, hist, state);
-    hipLaunchKernelGGL((hist_kernel<T, SMOOTH, 2>), g, dim3(kThreads), 0, st, X, M, K, s, state, hist);
-    hipLaunchKernelGGL(select_kernel<2>, dim3(1), dim3(1024), 0, st, hist, state);
-    hipLaunchKernelGGL(select_finish_kernel, dim3(1), dim3(64), 0, st, state, x_scale);
-    return hipGetLastError();
+    SQ_LAUNCH(select_init_kernel, dim3(1), dim3(256), 0, st, hist, state, rank);
+    SQ_LAUNCH((hist_kernel<T, SMOOTH, 0>), g, dim3(kThreads), 0, st, X, M, K, s, state, hist);
+    SQ_LAUNCH(select_kernel<0>, dim3(1), dim3(1024), 0, st, hist, state);
+    SQ_LAUNCH((hist_kernel<T, SMOOTH, 1>), g, dim3(kThreads), 0, st, X, M, K, s, state, hist);
+    SQ_LAUNCH(select_kernel<1>, dim3(1), dim3(1024), 0, st, hist, state);
+    SQ_LAUNCH((hist_kernel<T, SMOOTH, 2>), g, dim3(kThreads), 0, st, X, M, K, s, state, hist);
+    SQ_LAUNCH(select_kernel<2>, dim3(1), dim3(1024), 0, st, hist, state);
+    SQ_LAUNCH(select_finish_kernel, dim3(1), dim3(64), 0, st, state, x_scale);
+    return hipSuccess;
 }
 
 template <typename T, bool SMOOTH>
 hipError_t quant_t(const T* X, int64_t M, int64_t K, const float* s, const float* xs, int64_t group, int8_t* Xq,
                    float* xs_rows, hipStream_t st) {
     const RowPack g = row_pack(M, K / Chunk16<T>::N, 8, 1024);
-    hipLaunchKernelGGL((static_quant_kernel<T, SMOOTH>), g.grid, dim3(kThreads), 0, st, X, M, K, s, xs, group, Xq,
+    SQ_LAUNCH((static_quant_kernel<T, SMOOTH>), g.grid, dim3(kThreads), 0, st, X, M, K, s, xs, group, Xq,
                        xs_rows, g.lgp);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_static_calibrate(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, uint32_t rank,
+hipError_t launch_static_calibrate(const void* X, int dt, int64_t M, int64_t K, const float* s, uint32_t rank,
                                    float* x_scale, void* ws, hipStream_t st) {
     if (dt == SQ_F16) {
         if (s) return calibrate_t<_Float16, true>((const _Float16*)X, M, K, s, rank, x_scale, ws, st);
@@ -274,7 +274,7 @@ hipError_t launch_static_calibrate(const void* X, sq_dtype dt, int64_t M, int64_
     return calibrate_t<float, false>((const float*)X, M, K, s, rank, x_scale, ws, st);
 }
 
-hipError_t launch_static_quant(const void* X, sq_dtype dt, int64_t M, int64_t K, const float* s, const float* xs,
+hipError_t launch_static_quant(const void* X, int dt, int64_t M, int64_t K, const float* s, const float* xs,
                                int64_t group, int8_t* Xq, float* xs_rows, hipStream_t st) {
     if (dt == SQ_F16) {
         if (s) return quant_t<_Float16, true>((const _Float16*)X, M, K, s, xs, group, Xq, xs_rows, st);
