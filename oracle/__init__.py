@@ -26,9 +26,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    lib = C.CDLL(_build.LIB)
+    path = os.environ.get("SQ_ORACLE_LIB")       # another build of the same source (sanitizer runs)
+    if path is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+    lib = C.CDLL(path)
     P, I64, F, D, I = C.c_void_p, C.c_int64, C.c_float, C.c_double, C.c_int
     sig = {
         "orc_half_to_float_array": (None, [P, P, I64]),
@@ -70,8 +73,33 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
-    return lib
+    lib.orc_rounding_enter.restype = I
+    lib.orc_rounding_enter.argtypes = []
+    lib.orc_rounding_leave.restype = None
+    lib.orc_rounding_leave.argtypes = [I]
+    _lib = _NearestEven(lib, sig)
+    return _lib
+
+
+class _NearestEven:
+    """The oracle library with every entry point run under round-to-nearest-even (the
+    caller's rounding mode is restored afterwards)."""
+
+    def __init__(self, lib, names):
+        self._raw = lib
+        for name in names:
+            setattr(self, name, self._wrap(getattr(lib, name)))
+
+    def _wrap(self, fn):
+        raw = self._raw
+
+        def call(*args):
+            prev = raw.orc_rounding_enter()
+            try:
+                return fn(*args)
+            finally:
+                raw.orc_rounding_leave(prev)
+        return call
 
 
 def _ptr(a):

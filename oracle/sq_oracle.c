@@ -37,6 +37,7 @@
  *
  * Dtype codes used by this file only: 0 = float32, 1 = float16 (raw bits).
  */
+#include <fenv.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -121,6 +122,27 @@ static int8_t quant_code(float v)
     if (r > 127.0f) r = 127.0f;
     if (r < -128.0f) r = -128.0f;
     return (int8_t)r;
+}
+
+/* Rounding mode.  Every step above and below assumes round-to-nearest-even, the
+ * IEEE default; a caller could have left its thread in another mode.  The Python
+ * wrapper brackets every call into this file with these two functions: the first
+ * sets nearest-even on the calling thread and on every thread of the OpenMP team
+ * and returns the caller's mode, the second restores that mode. */
+int orc_rounding_enter(void)
+{
+    int prev = fegetround();
+    fesetround(FE_TONEAREST);
+#ifdef _OPENMP
+#pragma omp parallel
+    fesetround(FE_TONEAREST);
+#endif
+    return prev;
+}
+
+void orc_rounding_leave(int prev)
+{
+    fesetround(prev);
 }
 
 int orc_num_threads(void)

@@ -861,3 +861,34 @@ def test_results_do_not_depend_on_thread_count(orc):
     for a, b in zip(*outs):
         assert a.dtype == b.dtype and np.array_equal(a.view(np.uint8), b.view(np.uint8))
     assert orc.num_threads() == n0
+
+
+# --------------------------------------------------------------------------
+# The oracle fixes its own rounding mode: round-half-to-even whatever mode the
+# calling thread is in, and the caller's mode comes back afterwards
+# --------------------------------------------------------------------------
+
+def test_oracle_runs_nearest_even_under_another_mode(orc):
+    import ctypes
+    libm = ctypes.CDLL("libm.so.6")
+    FE_TONEAREST, FE_UPWARD = 0x000, 0x800          # x86-64 <fenv.h> values
+    r = np.random.default_rng(42)
+    X = r.uniform(-1.0, 1.0, (64, 64)).astype(np.float32)
+    Xq_ref, xs_ref = orc.quantize_per_token(X, None)
+    Xq_raw = np.empty_like(Xq_ref)
+    xs_raw = np.empty_like(xs_ref)
+    raw = orc._load()._raw                           # the C entry point without the mode guard
+    assert libm.fegetround() == FE_TONEAREST
+    libm.fesetround(FE_UPWARD)
+    try:
+        raw.orc_quantize_per_token(orc._ptr(X), 0, 64, 64, None, None, orc._ptr(Xq_raw), orc._ptr(xs_raw))
+        Xq_got, xs_got = orc.quantize_per_token(X, None)
+        mode_after = libm.fegetround()
+    finally:
+        libm.fesetround(FE_TONEAREST)
+    # the mode matters for this input: unguarded, some scale (max/127) rounds differently
+    assert not np.array_equal(xs_raw.view(np.uint32), xs_ref.view(np.uint32))
+    # the guarded entry point gives the round-to-nearest-even results and restores the mode
+    assert np.array_equal(xs_got.view(np.uint32), xs_ref.view(np.uint32))
+    assert np.array_equal(Xq_got, Xq_ref)
+    assert mode_after == FE_UPWARD
