@@ -61,5 +61,38 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out_dir: str) -> str:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer on its host
+    code only (argument validation, dispatch); the gfx950 device code is built as usual.
+    Load it with clang's ASan runtime preloaded (host_asan_runtime())."""
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-O1", "-g", "-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in FLAGS if f != "-O3"] + san
+
+    def one(src):
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        r = subprocess.run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(min(len(SOURCES), max(1, os.cpu_count() or 4))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libsq_host_sanitized.so")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libasan",
+                    "-Xarch_host", "-fsanitize=address,undefined", "-o", lib, *objs], check=True)
+    return lib
+
+
+def host_asan_runtime() -> str:
+    """clang's shared ASan runtime (it carries the UBSan handlers too)."""
+    import glob
+    found = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*",
+                                          "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under the ROCm LLVM")
+    return found[-1]
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -21,5 +21,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The oracle with AddressSanitizer and UndefinedBehaviorSanitizer (any report is
+    fatal); load it with gcc's libasan preloaded (asan_runtime())."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "liboracle_sanitized.so")
+    cmd = ["gcc", "-std=c99", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-o", lib, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return lib
+
+
+def asan_runtime() -> str:
+    return subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                          check=True).stdout.strip()
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -10,7 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sq.h")
-LIB = os.path.join(ROOT, "int8_quantization_amd", "libsq.so")
+LIB = os.environ.get("SQ_LIB") or os.path.join(ROOT, "int8_quantization_amd", "libsq.so")   # or a sanitizer build
 
 OK, NULL, SHAPE, ALIGN, DTYPE, VALUE, WORKSPACE, HIP = range(8)
 P = 0x100000          # a 16-byte-aligned address that is never dereferenced
