@@ -172,6 +172,29 @@ sq_status sq_w8a8_linear(const void* X, int xdt, int64_t M, int64_t K, const flo
                          int64_t N, void* Y, int ydt, float* x_scale, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* Limits of sq_w8a8_linear_noalloc's built-in scratch. */
+#define SQ_NOALLOC_XQ_BYTES ((size_t)16 << 20) /* int8 activation codes: M * K <= 16 MiB */
+#define SQ_NOALLOC_MAX_M 16384                 /* per-token scales held there when x_scale is NULL */
+
+/* sq_w8a8_linear without a workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It calls no allocating routine.  The int8 activation codes (and the per-token scales
+ * when x_scale is NULL) go to a fixed array in the library's device memory,
+ * SQ_NOALLOC_XQ_BYTES + 4 * SQ_NOALLOC_MAX_M bytes (16.06 MiB), which each GPU the
+ * library runs on holds until the process ends.
+ *   Arguments and results as for sq_w8a8_linear, without ws and ws_bytes; the outputs are
+ *   bit-identical to sq_w8a8_linear's.
+ *   Limits: M * K <= SQ_NOALLOC_XQ_BYTES, and M <= SQ_NOALLOC_MAX_M when x_scale is NULL;
+ *   larger inputs return SQ_ERR_WORKSPACE before anything is enqueued (use sq_w8a8_linear).
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ *   (nothing in it needs to start at zero): calls that can overlap on one GPU (streams
+ *   not ordered against each other, or several host threads) race on it, and the caller
+ *   must order them.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP. */
+sq_status sq_w8a8_linear_noalloc(const void* X, int xdt, int64_t M, int64_t K, const float* s,
+                                 const int8_t* Wq, const float* w_scale, int g, const float* bias,
+                                 int64_t N, void* Y, int ydt, float* x_scale, hipStream_t stream);
+
 /* LLM.int8() linear layer (no smoothing).
  * [LLM.int8() page, section 2.1: column-wise absmax of the input, columns above
  *  the threshold are outliers; section 3.1: bitmask of outlier columns, int8 GEMM

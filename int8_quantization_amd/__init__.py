@@ -47,6 +47,7 @@ def _load():
         "sq_calibrate_static_scale": (I, [P, I, I64, I64, P, C.c_double, P, P, SZ, P]),
         "sq_quantize_static": (I, [P, I, I64, I64, P, P, P, P, P]),
         "sq_w8a8_linear": (I, [P, I, I64, I64, P, P, P, I, P, I64, P, I, P, P, SZ, P]),
+        "sq_w8a8_linear_noalloc": (I, [P, I, I64, I64, P, P, P, I, P, I64, P, I, P, P]),
         "sq_quantize_per_token_fp8": (I, [P, I, I64, I64, P, P, P, P]),
         "sq_quantize_weight_fp8": (I, [P, I, I64, I64, P, I, P, P, P, SZ, P]),
         "fp8_gemm_dequant": (I, [P, P, P, P, I, P, I64, I64, I64, P, I, P, P]),
@@ -67,7 +68,7 @@ EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quan
            "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
            "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static",
            "sq_kv_calibrate_per_head", "sq_kv_quantize_per_head", "sq_dequantize", "sq_quantize_per_token_fp8",
-           "sq_quantize_weight_fp8", "fp8_gemm_dequant", "sq_w8a8_linear")
+           "sq_quantize_weight_fp8", "fp8_gemm_dequant", "sq_w8a8_linear", "sq_w8a8_linear_noalloc")
 
 
 def _p(t):
@@ -373,3 +374,26 @@ def sq_w8a8_linear(X, s, Wq, w_scale, gran, bias, Y, ws, x_scale=None):
     _check(fn, _lib.sq_w8a8_linear(
         _p(X), _dt(X), M, K, _p(s), _p(Wq), _p(w_scale), int(gran), _p(bias), N, _p(Y), _dt(Y), _p(x_scale),
         _p(ws), nbytes, _stream()))
+
+
+SQ_NOALLOC_XQ_BYTES = 16 << 20
+SQ_NOALLOC_MAX_M = 16384
+
+
+def sq_w8a8_linear_noalloc(X, s, Wq, w_scale, gran, bias, Y, x_scale=None):
+    """sq_w8a8_linear without a workspace: the library's own fixed device scratch holds Xq
+    (M * K <= 16 MiB; M <= 16384 when x_scale is None).  Calls that can overlap on one GPU
+    share that scratch and must be ordered by the caller."""
+    fn = "sq_w8a8_linear_noalloc"
+    M, K = _rows_in(fn, X, s)
+    _need(fn, "Wq", Wq, (I8,), ndim=2)
+    N = Wq.shape[0]
+    if Wq.shape[1] != K:
+        raise ValueError(f"{fn}: Wq has {Wq.shape[1]} columns, X {K}")
+    _need(fn, "w_scale", w_scale, (F32,), numel=_gran(fn, gran, N))
+    _need(fn, "bias", bias, (F32,), numel=N, optional=True)
+    _need(fn, "Y", Y, FLOAT, shape=(M, N))
+    _need(fn, "x_scale", x_scale, (F32,), numel=M, optional=True)
+    _check(fn, _lib.sq_w8a8_linear_noalloc(
+        _p(X), _dt(X), M, K, _p(s), _p(Wq), _p(w_scale), int(gran), _p(bias), N, _p(Y), _dt(Y), _p(x_scale),
+        _stream()))

@@ -2,9 +2,17 @@
 // caller's stream.  No allocation, no host synchronization, no device-to-host copy.
 #include <math.h>
 
+#include <mutex>
+
 #include "sq_internal.h"
 
 using namespace sq;
+
+// Scratch of sq_w8a8_linear_noalloc: the int8 codes of the activation rows, then their
+// per-token scales.  Each GPU the library runs on holds its own copy from the code
+// object's load until the process ends.  In host code this name is a host-side stand-in:
+// kernels get the device address that scratch_base() looks up.
+static __device__ __align__(256) int8_t scratch[SQ_NOALLOC_XQ_BYTES + 4 * SQ_NOALLOC_MAX_M];
 
 namespace {
 
@@ -45,6 +53,35 @@ OutlierLayout outlier_layout(int64_t M, int64_t N, int64_t K) {
     L.total = o;
     return L;
 }
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) by hipGetSymbolAddress; nullptr when the lookup failed.
+int8_t* scratch_base() {
+    constexpr int kMaxDevices = 64;
+    static int8_t* base[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(once[dev], [dev]() {
+        void* p = nullptr;
+        base[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? static_cast<int8_t*>(p) : nullptr;
+    });
+    return base[dev];
+}
+
+// The layer after validation: the fused decode kernel when it applies, else the
+// quantizer into xq / xs and the GEMM (decode kernel for M <= 16).
+sq_status linear_body(const void* X, int xdt, int64_t M, int64_t K, const float* s, const int8_t* Wq,
+                      const float* w_scale, int g, const float* bias, int64_t N, void* Y, int ydt, float* x_scale,
+                      int8_t* xq, float* xs, hipStream_t stream) {
+    const int stride = g == SQ_PER_CHANNEL ? 1 : 0;
+    SQ_TRY(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, xq, xs, nullptr, nullptr, stream));
+    if (M <= 16)
+        return hip_status(launch_gemv(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
+    return hip_status(launch_gemm(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
+}
+
+bool fused_decode(int xdt, int64_t M, int64_t K) { return xdt == SQ_F16 && M <= 2 && K <= 8192; }
 
 }  // namespace
 
@@ -185,16 +222,32 @@ sq_status sq_w8a8_linear(const void* X, int xdt, int64_t M, int64_t K, const flo
     if (misaligned(X) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) || misaligned(ws) ||
         (s && misaligned(s)) || (bias && misaligned(bias)) || (x_scale && misaligned(x_scale)))
         return SQ_ERR_ALIGN;
-    const int stride = g == SQ_PER_CHANNEL ? 1 : 0;
-    if (xdt == SQ_F16 && M <= 2 && K <= 8192)
-        return hip_status(launch_linear_decode(static_cast<const _Float16*>(X), s, Wq, w_scale, stride, bias, M, N, K,
-                                               Y, ydt, x_scale, stream));
+    if (fused_decode(xdt, M, K))
+        return hip_status(launch_linear_decode(static_cast<const _Float16*>(X), s, Wq, w_scale,
+                                               g == SQ_PER_CHANNEL ? 1 : 0, bias, M, N, K, Y, ydt, x_scale, stream));
     int8_t* xq = static_cast<int8_t*>(ws);
     float* xs = x_scale ? x_scale : reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)M * K));
-    SQ_TRY(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, xq, xs, nullptr, nullptr, stream));
-    if (M <= 16)
-        return hip_status(launch_gemv(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
-    return hip_status(launch_gemm(xq, xs, Wq, w_scale, stride, bias, M, N, K, Y, ydt, nullptr, nullptr, stream));
+    return linear_body(X, xdt, M, K, s, Wq, w_scale, g, bias, N, Y, ydt, x_scale, xq, xs, stream);
+}
+
+sq_status sq_w8a8_linear_noalloc(const void* X, int xdt, int64_t M, int64_t K, const float* s, const int8_t* Wq,
+                                 const float* w_scale, int g, const float* bias, int64_t N, void* Y, int ydt,
+                                 float* x_scale, hipStream_t stream) {
+    if (!X || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt) || bad_dtype(ydt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if ((uint64_t)M * (uint64_t)K > (uint64_t)SQ_NOALLOC_XQ_BYTES || (!x_scale && M > SQ_NOALLOC_MAX_M))
+        return SQ_ERR_WORKSPACE;
+    if (misaligned(X) || misaligned(Wq) || misaligned(w_scale) || misaligned(Y) || (s && misaligned(s)) ||
+        (bias && misaligned(bias)) || (x_scale && misaligned(x_scale)))
+        return SQ_ERR_ALIGN;
+    if (fused_decode(xdt, M, K))
+        return hip_status(launch_linear_decode(static_cast<const _Float16*>(X), s, Wq, w_scale,
+                                               g == SQ_PER_CHANNEL ? 1 : 0, bias, M, N, K, Y, ydt, x_scale, stream));
+    int8_t* base = scratch_base();
+    if (!base) return SQ_ERR_HIP;
+    float* xs = x_scale ? x_scale : reinterpret_cast<float*>(base + SQ_NOALLOC_XQ_BYTES);
+    return linear_body(X, xdt, M, K, s, Wq, w_scale, g, bias, N, Y, ydt, x_scale, base, xs, stream);
 }
 
 sq_status sq_quantize_per_token_fp8(const void* X, int xdt, int64_t M, int64_t K, const float* s, uint8_t* Xq,

@@ -38,6 +38,7 @@ def lib():
     lib.sq_calibrate_static_scale.argtypes = [V, I, I64, I64, V, C.c_double, V, V, SZ, V]
     lib.sq_quantize_static.argtypes = [V, I, I64, I64, V, V, V, V, V]
     lib.sq_w8a8_linear.argtypes = [V, I, I64, I64, V, V, V, I, V, I64, V, I, V, V, SZ, V]
+    lib.sq_w8a8_linear_noalloc.argtypes = [V, I, I64, I64, V, V, V, I, V, I64, V, I, V, V]
     lib.sq_quantize_per_token_fp8.argtypes = [V, I, I64, I64, V, V, V, V]
     lib.sq_quantize_weight_fp8.argtypes = [V, I, I64, I64, V, I, V, V, V, SZ, V]
     lib.fp8_gemm_dequant.argtypes = [V, V, V, V, I, V, I64, I64, I64, V, I, V, V]
@@ -289,6 +290,28 @@ def test_linear_validation(lib):
     assert f(*args(nb=need - 1)) == WORKSPACE
     assert f(*args(X=MIS)) == ALIGN
     assert f(*args(xs=MIS)) == ALIGN
+    assert f(*args(bias=MIS)) == ALIGN
+
+
+def test_linear_noalloc_validation(lib):
+    """The no-allocation layer: the same checks as sq_w8a8_linear, and inputs beyond its
+    fixed scratch (M * K > 16 MiB, or M > 16384 without a caller-provided x_scale) are
+    refused with SQ_ERR_WORKSPACE before anything is enqueued."""
+    f = lib.sq_w8a8_linear_noalloc
+    args = lambda **kw: [kw.get("X", P), kw.get("xdt", 1), kw.get("M", 5), kw.get("K", 1600), kw.get("s", None),
+                         kw.get("Wq", P), kw.get("wsc", P), kw.get("g", 0), kw.get("bias", None), kw.get("N", 64),
+                         kw.get("Y", P), kw.get("ydt", 1), kw.get("xs", None), None]
+    assert f(*args(X=None)) == NULL
+    assert f(*args(Y=None)) == NULL
+    assert f(*args(M=0)) == SHAPE
+    assert f(*args(K=1601)) == SHAPE
+    assert f(*args(xdt=2)) == DTYPE
+    assert f(*args(g=-1)) == DTYPE
+    assert f(*args(M=1025, K=16384)) == WORKSPACE               # 1025 * 16384 > 16 MiB of codes
+    assert f(*args(M=1024, K=16400)) == WORKSPACE
+    assert f(*args(M=16385, K=16)) == WORKSPACE                 # scales would not fit ...
+    assert f(*args(M=16385, K=16, xs=MIS)) == ALIGN             # ... unless the caller takes them
+    assert f(*args(M=1024, K=16384, X=MIS)) == ALIGN            # exactly 16 MiB of codes is accepted
     assert f(*args(bias=MIS)) == ALIGN
 
 

@@ -70,6 +70,8 @@ def _valid():
                                  bias=None, Y=t((M, N), F32), acc_out=t((M, N), F32)),
         "sq_w8a8_linear": dict(X=t((M, K), F16), s=t(K, F32), Wq=t((N, K), I8), w_scale=t(N, F32), gran=0,
                                bias=t(N, F32), Y=t((M, N), F16), ws=ws, x_scale=t(M, F32)),
+        "sq_w8a8_linear_noalloc": dict(X=t((M, K), F32), s=None, Wq=t((N, K), I8), w_scale=t(1, F32), gran=1,
+                                       bias=None, Y=t((M, N), F32), x_scale=None),
     }
 
 
@@ -138,6 +140,10 @@ BAD = [
     ("sq_w8a8_linear", "Y", t((M + 1, N), F16)),
     ("sq_w8a8_linear", "ws", None),
     ("sq_w8a8_linear", "w_scale", t(N, F16)),
+    ("sq_w8a8_linear_noalloc", "Wq", t((N, K - 16), I8)),
+    ("sq_w8a8_linear_noalloc", "Y", t((M, N), I8)),
+    ("sq_w8a8_linear_noalloc", "x_scale", t(M - 1, F32)),
+    ("sq_w8a8_linear_noalloc", "w_scale", t(N, F32)),
 ]
 
 
