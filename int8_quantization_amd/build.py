@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libsq.so")
-SOURCES = ["sq_api.hip", "quant.hip", "gemm.hip", "gemv.hip", "outlier.hip", "lnquant.hip", "static.hip", "kvcache.hip"]
+SOURCES = ["sq_api.hip", "quant.hip", "quant_stream.hip", "gemm.hip", "gemv.hip", "outlier.hip", "lnquant.hip",
+           "static.hip", "kvcache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -92,24 +92,6 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from a buffer resource straight into LDS: the wave's 1 KB
-// lands at LDS byte address lds_addr (through M0), lane l at lds_addr + 16 l.
-// Offsets outside the resource's record range read as zeros.  The resource is
-// the four descriptor words in scalar registers.  M0 is written here only: the
-// kernels that use this helper leave M0 to it (a CPU test checks their ISA).
-__device__ __forceinline__ void dma_to_lds(const v4i& rsrc, uint32_t lds_addr, uint32_t voff, int k0) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds_addr), "v"(voff), "s"(rsrc), "s"(k0)
-                 : "memory");
-}
-
-// Buffer resource over [p, p + nrec) bytes, raw (unformatted) 32-bit records.
-__device__ __forceinline__ v4i buffer_desc(const int8_t* p, int nrec) {
-    const uint64_t a = (uint64_t)p;
-    return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(a >> 32)),
-               __builtin_amdgcn_readfirstlane(nrec), 0x00020000};
-}
-
 template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,

@@ -1,0 +1,356 @@
+// Streaming per-token quantizer for fp16 activations on gfx950: the prefill
+// shapes' hot path of the fused smoothing + per-token quantization
+// ["量化基础与INT8", 量化流程示例: per-row absmax scale, round, clamp;
+// "SmoothQuant量化实战", sections 3.3-3.4: X' = X / s before quantizing], and
+// its LLM.int8() variant ["LLM.int8()技术解析", section 3.1: outlier columns
+// leave the int8 part and are copied out for the fp16 product].
+//
+// Persistent blocks (NT threads: two 512-thread blocks per CU, or one of 1024 for
+// rows over 8192 values) walk steps of G consecutive rows (G row groups of NT/G
+// threads).  Input rows reach LDS by DMA (buffer_load ... lds, no registers),
+// through a ring of R slots: while a step is computed, the next R-1 steps are in
+// flight, which keeps enough bytes moving to stream at HBM rate.  Per step:
+//   wait for this wave's DMA of the step (s_waitcnt vmcnt with the exact count
+//   of vector-memory instructions issued after it), barrier;
+//   pass 1: x' = fl32(x / s_j) from LDS (x_j without smoothing), kept in
+//   registers, |x'| maximum over the group's waves (shuffles, then LDS), barrier;
+//   xs = fl32(max / 127);  pass 2: q = rne(fl32(x' / xs)) packed 4 per dword and
+//   stored through a buffer resource; then the DMA of step + R into the slot the
+//   step used.
+// Counting: every wave issues exactly L DMA and CH code-store instructions per
+// step (tail chunks, rows past M and steps past the block's last store to
+// offsets outside the buffer range, which drops them, or read zeros), so after
+// a step's DMA exactly (R-1)(CH+L) such instructions follow before its wait.
+// Vector memory instructions complete in issue order, and any other load or
+// store only adds to the count after the DMA, so waiting for at most that many
+// outstanding guarantees the step's data.
+//
+// Arithmetic (identical to the register-resident kernel in quant.hip):
+//  - x / s_j and x' / xs are RN32(RN64(a * rcp64(b))), which equals the IEEE
+//    binary32 quotient in the normal range (proof at div_rcp64); an x / s_j
+//    below it takes the IEEE division (possible only when s_j >= 2^100);
+//  - rne of the fp32 quotient v comes from one fp32 addition: v + 1.5 * 2^23
+//    rounds to the integer 1.5 * 2^23 + rne(v) for |v| < 2^22 (the sum lies in
+//    [2^23, 2^24), where the spacing is 1, and 1.5 * 2^23 is even, so ties go to
+//    even), and the low byte of its bit pattern is the two's-complement code.
+//    No clamp is needed: |x'| <= max gives |v| <= 127 (1 + 2^-23), which rounds
+//    to at most 127.
+#include <type_traits>
+
+#include "sq_internal.h"
+
+namespace sq {
+
+namespace {
+
+// NT threads per block: 512 (two blocks per CU, whose phases drift apart, so one
+// computes while the other waits) for rows of up to 8192 values, 1024 (one block per
+// CU) for longer rows, which need the whole block to keep a row in registers.
+template <int NT, int CH> struct Ring {
+    static constexpr int NW = NT / 64;                            // waves
+    static constexpr int L = (CH + 1) / 2;                        // DMA instructions per wave per step
+    static constexpr int SLOT = L * NW * 1024;                    // bytes per slot: NW waves x L x 1 KB
+    static constexpr int LDS = NT == 1024 ? 144 * 1024 : 72 * 1024;   // ring bytes per block
+    static constexpr int R = (LDS / SLOT) < 8 ? (LDS / SLOT) : 8;      // slots
+    // vector-memory instructions counted after the DMA of step j before its wait:
+    // (R-1) L + min(j, R-1) CH (see the kernel)
+    static constexpr int AHEAD = (R - 1) * (CH + L);
+    static_assert(R >= 3, "ring of at least three slots");
+    static_assert(AHEAD <= 63, "vmcnt holds at most 63");
+};
+
+// s_waitcnt vmcnt(N) with the exp/lgkm counts unconstrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+// vmcnt(BASE + STEP * k) for a wave-uniform k in [0, KMAX] (a chain of scalar branches).
+template <int BASE, int STEP, int KMAX> __device__ __forceinline__ void wait_vm_k(int k) {
+    if constexpr (KMAX > 0) {
+        if (k >= KMAX) {
+            wait_vm<BASE + STEP * KMAX>();
+            return;
+        }
+        wait_vm_k<BASE, STEP, KMAX - 1>(k);
+    } else {
+        wait_vm<BASE>();
+    }
+}
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS accesses are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Maximum over the wave of non-negative floats, returned to every lane: four DPP steps
+// give each row of 16 lanes its maximum (quad swaps 1 and 2, then the half-row and
+// row mirrors), and the four row maxima are read out (v_readlane) and combined.  Much
+// shorter than the ds_bpermute butterfly of __shfl_xor.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    auto step = [](float x, int ctrl) -> float {
+        int y;
+        switch (ctrl) {
+            case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+            case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+            case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+            default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false); break; // row_mirror
+        }
+        return __builtin_fmaxf(x, __int_as_float(y));
+    };
+    v = step(v, 0);
+    v = step(v, 1);
+    v = step(v, 2);
+    v = step(v, 3);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
+}
+
+// Code byte of rne(v) for |v| < 2^22, in the low byte of the result.
+__device__ __forceinline__ uint32_t code_bits(float v) { return __float_as_uint(v + 12582912.0f); }
+
+template <int NT, int CH, bool SMOOTH, bool OUTL>
+__global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(const _Float16* __restrict__ X, int M, int K,
+                                                                   const float* __restrict__ s,
+                                                                   int8_t* __restrict__ Xq, float* __restrict__ scale,
+                                                                   const int32_t* __restrict__ pos,
+                                                                   _Float16* __restrict__ Xo, int G, int steps) {
+    using RG = Ring<NT, CH>;
+    constexpr int R = RG::R, L = RG::L, SLOT = RG::SLOT, NW = RG::NW;
+    constexpr bool COLS = SMOOTH || OUTL;         // per-column constants to stage
+    __shared__ __attribute__((aligned(1024))) int8_t ring[R * SLOT];
+    __shared__ __attribute__((aligned(16))) float red[2][NW];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int tpg = NT / G;                       // threads per row group (>= 64)
+    const int g = tid / tpg, t = tid - g * tpg;
+    const int w0 = (g * tpg) >> 6, nwg = tpg >> 6;
+    const int nch = K >> 2;                       // 4-value chunks per row
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const uint32_t step_bytes = (uint32_t)G * row_bytes;
+    const uint32_t nblk = (step_bytes + 1023u) >> 10;   // 1 KB DMA blocks holding the step
+    const uint32_t x_bytes = (uint32_t)M * row_bytes;
+    const v4i rX = buffer_desc(X, x_bytes);
+    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(Xq, 0, M * K, 0x00020000);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)ring;
+    const int nb = gridDim.x;
+    constexpr uint32_t OOB = 0x80000000u;         // beyond every record range: dropped / zeros
+
+    // DMA of the block's step j (rows (j * nb + blockIdx.x) * G + [0, G)) into slot j % R
+    auto dma_step = [&](int j) {
+        const uint64_t src = (uint64_t)((uint32_t)j * (uint32_t)nb + blockIdx.x) * step_bytes;
+        const uint32_t src0 = src < x_bytes ? (uint32_t)src : OOB;
+        const uint32_t slot = (uint32_t)(j % R) * SLOT;
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const uint32_t b = (uint32_t)(wave + NW * l);
+            const uint32_t voff = (b < nblk && src0 != OOB) ? src0 + b * 1024u + (uint32_t)lane * 16u : OOB;
+            dma_to_lds(rX, __builtin_amdgcn_readfirstlane(lds_base + slot + b * 1024u), voff, 0);
+        }
+    };
+
+    // Prologue.  The per-column array (s, or the outlier slots) is DMA'd into the last NP
+    // slots of the ring, the first R - NP steps into the others; once the array has landed
+    // the constants are computed while those steps are in flight, then the remaining steps
+    // are requested.  Every wave issues the same instructions, so the counts below hold
+    // for each wave.
+    const int NP = COLS ? (int)(((uint32_t)K * 4u + SLOT - 1) / SLOT) : 0;   // 1 .. R-1 slots
+    if constexpr (COLS) {
+        const v4i rP = buffer_desc(SMOOTH ? (const void*)s : (const void*)pos, (uint32_t)K * 4u);
+        const uint32_t pbase = lds_base + (uint32_t)(R - NP) * SLOT;
+        // K * 4 <= 16 bytes x NT x CH: at most CH 1 KB blocks per wave; blocks past the array read
+        // zeros, and none is written past the NP slots (a wave-uniform condition; the count
+        // waited for below is of the instructions issued after these)
+        for (int l = 0; l < CH; ++l) {
+            const uint32_t b = (uint32_t)(wave + NW * l);
+            if (b * 1024u < (uint32_t)NP * SLOT)
+                dma_to_lds(rP, __builtin_amdgcn_readfirstlane(pbase + b * 1024u), b * 1024u + (uint32_t)lane * 16u, 0);
+        }
+    }
+    for (int j = 0; j < R - NP; ++j) dma_step(j);
+
+    bool valid[CH];
+    double rs[SMOOTH ? CH : 1][4];
+    unsigned omask[OUTL ? CH : 1];
+    int opos[OUTL ? CH : 1][4];
+    unsigned ochunks = 0;                         // bit i: some lane of this wave has an outlier in chunk i
+    bool guard = false;                           // some x / s_j may fall below the fp32 normal range
+#pragma unroll
+    for (int i = 0; i < CH; ++i) valid[i] = t + i * tpg < nch;
+    if constexpr (COLS) {
+        wait_vm_k<0, L, R - 1>(R - NP);           // the array landed (R - NP steps' DMA issued after it)
+        barrier_lds();
+        const int8_t* P = ring + (R - NP) * SLOT;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int cc = valid[i] ? t + i * tpg : 0;
+            if constexpr (SMOOTH) {
+                const v4f sv = *reinterpret_cast<const v4f*>(P + 16 * cc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    rs[i][e] = rcp64((double)sv[e]);
+                    guard = guard || !(sv[e] < 0x1p100f);
+                }
+            }
+            if constexpr (OUTL) {
+                const v4i pq = *reinterpret_cast<const v4i*>(P + 16 * cc);
+                omask[i] = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    opos[i][e] = pq[e];
+                    if (valid[i] && pq[e] >= 0) omask[i] |= 1u << e;
+                }
+                if (__builtin_amdgcn_ballot_w64(omask[i] != 0) != 0) ochunks |= 1u << i;
+            }
+        }
+        barrier_lds();                            // the array's slots are free again
+        for (int j = R - NP; j < R; ++j) dma_step(j);
+    }
+    const bool guard_wave = __builtin_amdgcn_ballot_w64(guard) != 0;
+
+    for (int j = 0; j < steps; ++j) {
+        // After this wave's DMA of step j it issued (R-1) L DMA instructions (later steps)
+        // and CH code stores for each of the min(j, R-1) steps before j; any other memory
+        // instruction only adds to that.
+        wait_vm_k<(R - 1) * L, CH, R - 1>(j);
+        barrier_lds();                            // every wave's part of step j landed
+        const int row = (j * nb + (int)blockIdx.x) * G + g;
+        const bool live = row < M;
+        const int8_t* rowp = ring + (j % R) * SLOT + g * (int)row_bytes;
+
+        float xv[CH][4];
+        float amax = 0.0f;
+        auto pass1 = [&](auto guarded) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int c = t + i * tpg;
+                const h4 hv = *reinterpret_cast<const h4*>(rowp + 8 * c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = (float)hv[e];
+                    if constexpr (SMOOTH) {
+                        float q = (float)((double)x * rs[i][e]);
+                        if constexpr (decltype(guarded)::value)
+                            if (__builtin_fabsf(q) < 1.17549435e-38f && x != 0.0f && valid[i]) q = x / s[4 * c + e];
+                        x = q;
+                    }
+                    // only the last chunk can lie past the row (CH = ceil(chunks / tpg)); its values
+                    // there are zeroed, which leaves the maximum unchanged
+                    if (i == CH - 1) x = valid[i] ? x : 0.0f;
+                    xv[i][e] = x;
+                }
+                if constexpr (OUTL) {
+                    if ((ochunks >> i) & 1u) {    // wave-uniform: some lane holds an outlier column here
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const bool o = (omask[i] >> e) & 1u;
+                            if (o && live) Xo[(int64_t)row * K + opos[i][e]] = hv[e];
+                            xv[i][e] = o ? 0.0f : xv[i][e];     // out of the maximum; code 0 below
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(xv[i][e]));
+            }
+        };
+        // the IEEE-division check runs only in waves with some s_j >= 2^100 (a uniform branch)
+        if (SMOOTH && guard_wave) pass1(std::true_type{});
+        else pass1(std::false_type{});
+        amax = wave_max_dpp(amax);
+        if (lane == 0) red[j & 1][wave] = amax;
+        barrier_lds();                            // also: every wave is done reading the step's slot
+        float a = red[j & 1][w0];
+        if (nwg >= 4) {                           // the group's wave maxima, 16 bytes per read
+            for (int w = 0; w < nwg; w += 4) {
+                const v4f r4 = *reinterpret_cast<const v4f*>(&red[j & 1][w0 + w]);
+                a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fmaxf(r4[0], r4[1]), __builtin_fmaxf(r4[2], r4[3])));
+            }
+        } else {
+            for (int w = 1; w < nwg; ++w) a = __builtin_fmaxf(a, red[j & 1][w0 + w]);
+        }
+        // xs = fl32(a / 127) as RN32(RN64(a * RN64(1/127))), exact for a normal-range
+        // quotient (the argument at div_rcp64); a quotient below it takes the division
+        float xs = (float)((double)a * (1.0 / 127.0));
+        if (xs < 1.17549435e-38f && a != 0.0f) xs = a / 127.0f;
+        if (live && t == 0) scale[row] = xs;
+        const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;   // xs == 0: every x' is 0, codes 0
+
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = code_bits((float)((double)xv[i][e] * rx));
+            const uint32_t w = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                     __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+            const int c = t + i * tpg;
+            const uint32_t off = (live && valid[i]) ? (uint32_t)row * (uint32_t)K + 4u * (uint32_t)c : OOB;
+            __builtin_amdgcn_raw_buffer_store_b32(w, rQ, (int)off, 0, 0);
+        }
+        dma_step(j + R);                          // into the slot this step used
+    }
+}
+
+template <int NT, int CH, bool SMOOTH, bool OUTL>
+hipError_t launch_ch(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, const int32_t* pos,
+                     _Float16* Xo, int G, hipStream_t st) {
+    const int64_t total = ((int64_t)M + G - 1) / G;               // steps over all blocks
+    const int64_t slots = (int64_t)dev_info().cus * (NT == 1024 ? 1 : 2);
+    const int nb = (int)(total < slots ? total : slots);
+    const int steps = (int)((total + nb - 1) / nb);
+    SQ_LAUNCH((quant_stream_kernel<NT, CH, SMOOTH, OUTL>), dim3((unsigned)nb), dim3(NT), 0, st, X, M, K, s, Xq, scale,
+              pos, Xo, G, steps);
+    return hipSuccess;
+}
+
+template <bool SMOOTH, bool OUTL>
+hipError_t launch_mode(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, const int32_t* pos,
+                       _Float16* Xo, int nt, int G, int ch, hipStream_t st) {
+    if (nt == 512) {
+        switch (ch) {
+            case 1: return launch_ch<512, 1, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+            case 2: return launch_ch<512, 2, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+            case 3: return launch_ch<512, 3, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+            default: return launch_ch<512, 4, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+        }
+    }
+    switch (ch) {
+        case 3: return launch_ch<1024, 3, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+        case 4: return launch_ch<1024, 4, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+        default: return launch_ch<1024, 5, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+    }
+}
+
+}  // namespace
+
+bool quant_stream_applies(int64_t M, int64_t K, bool smooth, bool outliers) {
+    // rows of up to 5 x 4096 values (longer rows would spill the per-column constants);
+    // enough rows for every CU to stream several steps; byte offsets of X (and of the steps
+    // past the last) within 31 bits; no smoothing together with outlier columns (LLM.int8()
+    // does not smooth)
+    return K <= 20480 && M >= 4 * (int64_t)dev_info().cus && (M + 16 * 1024) * K * 2 < ((int64_t)1 << 31) &&
+           !(smooth && outliers);
+}
+
+hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
+                               const int32_t* pos, _Float16* Xo, hipStream_t st) {
+    // Rows of up to 8192 values: 512-thread blocks, G row groups per step, the most that
+    // keep at most 4 chunks per thread (bigger steps spread the per-step reduction and
+    // synchronization over more values).  Longer rows: 1024 threads, one row per step,
+    // up to 5 chunks per thread.
+    const int64_t nch = K / 4;
+    const int nt = K <= 8192 ? 512 : 1024;
+    int G = nt / 64;
+    while (G > 1 && (nch + nt / G - 1) / (nt / G) > 4) G /= 2;
+    const int ch = (int)((nch + nt / G - 1) / (nt / G));
+    if (s) return launch_mode<true, false>(X, (int)M, (int)K, s, Xq, scale, nullptr, nullptr, nt, G, ch, st);
+    if (pos) return launch_mode<false, true>(X, (int)M, (int)K, nullptr, Xq, scale, pos, Xo, nt, G, ch, st);
+    return launch_mode<false, false>(X, (int)M, (int)K, nullptr, Xq, scale, nullptr, nullptr, nt, G, ch, st);
+}
+
+}  // namespace sq

@@ -57,6 +57,28 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// 16 bytes per lane from a buffer resource straight into LDS: the wave's 1 KB
+// lands at LDS byte address lds_addr (through M0), lane l at lds_addr + 16 l.
+// Offsets outside the resource's record range read as zeros.  The resource is
+// the four descriptor words in scalar registers.  M0 is written here only: the
+// kernels that use this helper leave M0 to it (a CPU test checks their ISA).
+// Issued from inline asm: the compiler models the builtin form as an LDS store of
+// unknown address and then waits for it before every later LDS read, which would
+// serialize a prefetch with the reads of the previous stage; callers order it
+// with their own s_waitcnt and barriers.
+__device__ __forceinline__ void dma_to_lds(const v4i& rsrc, uint32_t lds_addr, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
+// Buffer resource over [p, p + nrec) bytes, raw (unformatted) 32-bit records.
+__device__ __forceinline__ v4i buffer_desc(const void* p, uint32_t nrec) {
+    const uint64_t a = (uint64_t)p;
+    return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(a >> 32)),
+               __builtin_amdgcn_readfirstlane((int)nrec), 0x00020000};
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -130,6 +152,13 @@ inline RowPack row_pack(int64_t M, int64_t nchunk, int64_t rows_per_thread, int6
 hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const float* s,
                              int mode, int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo,
                              hipStream_t st, int fmt = 0);
+
+// The streaming fp16 per-token quantizer (int8 codes; s == nullptr: no smoothing; pos / Xo:
+// the LLM.int8() outlier columns as for launch_quant_rows), for the shapes where
+// quant_stream_applies() holds; launch_quant_rows dispatches to it.
+bool quant_stream_applies(int64_t M, int64_t K, bool smooth, bool outliers);
+hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
+                               const int32_t* pos, _Float16* Xo, hipStream_t st);
 
 // Running column absolute maximum: amax_bits[j] = max(amax_bits[j], bits(max_m |X[m,j]|)),
 // where amax_bits holds non-negative floats as their bit patterns (monotone as uint32).

@@ -38,12 +38,12 @@ def gemm_asm():
     return B.device_asm("gemm.hip")
 
 
-def test_gemm_m0_only_written_by_the_dma_asm(gemm_asm):
-    """The tile kernel's operand DMA is issued from inline asm that loads M0
-    itself; nothing the compiler emits may depend on M0 surviving it, so M0 must
-    be written (and buffer ... lds issued) only inside those asm blocks."""
-    ks = {k: v for k, v in kernels(gemm_asm).items() if "gemm_i8_kernel" in k}
-    assert len(ks) >= 6
+@pytest.fixture(scope="module")
+def stream_asm():
+    return B.device_asm("quant_stream.hip")
+
+
+def _check_m0(ks):
     for name, lines in ks.items():
         inside, n_dma = False, 0
         for l in lines:
@@ -66,6 +66,45 @@ def test_gemm_m0_only_written_by_the_dma_asm(gemm_asm):
             elif is_lds_dma:
                 n_dma += 1
         assert n_dma > 0, name
+
+
+def test_gemm_m0_only_written_by_the_dma_asm(gemm_asm):
+    """The tile kernel's operand DMA is issued from inline asm that loads M0
+    itself; nothing the compiler emits may depend on M0 surviving it, so M0 must
+    be written (and buffer ... lds issued) only inside those asm blocks."""
+    ks = {k: v for k, v in kernels(gemm_asm).items() if "gemm_i8_kernel" in k}
+    assert len(ks) >= 6
+    _check_m0(ks)
+
+
+def test_stream_quantizer_m0_only_written_by_the_dma_asm(stream_asm):
+    """The same for the streaming quantizer's row DMA."""
+    ks = {k: v for k, v in kernels(stream_asm).items() if "quant_stream_kernel" in k}
+    assert len(ks) >= 10
+    _check_m0(ks)
+
+
+def test_stream_quantizer_stores_every_step_unconditionally(stream_asm):
+    """Its vmcnt waits count CH code stores and L DMA loads per wave per step, so no
+    branch may skip them: between the last branch target before the step's code
+    stores and the DMA that follows them there is no conditional branch, and the
+    kernel uses no scratch (spill loads and stores would be extra vector-memory
+    instructions in the loop)."""
+    for name, lines in kernels(stream_asm).items():
+        if "quant_stream_kernel" not in name:
+            continue
+        ch = int(re.search(r"quant_stream_kernelILi\d+ELi(\d)E", name).group(1))
+        body = [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
+        stores = [i for i, l in enumerate(body) if l.startswith("buffer_store_dword ")]
+        assert len(stores) == ch, (name, len(stores))
+        dma = [i for i, l in enumerate(body) if l.startswith("buffer_load_dwordx4") and " lds" in l]
+        after = [i for i in dma if i > stores[-1]]
+        assert after, name
+        block_start = max(i for i, l in enumerate(body[:stores[0]]) if l.endswith(":") or l.startswith("s_cbranch"))
+        region = body[block_start + 1:after[0]]
+        assert not any(l.startswith("s_cbranch") for l in region), name
+        assert not any(l.endswith(":") for l in region), name
+        assert "scratch_" not in "\n".join(body), name
 
 
 def test_gemm_kernels_do_not_spill(gemm_asm):

@@ -115,6 +115,47 @@ def test_quantize_deterministic(sq):
         assert_bits_equal(o[1], outs[0][1], "x_scale repeat")
 
 
+# The streaming quantizer (fp16 rows, at least 4 rows per CU, K <= 20480): row groups of
+# 64..1024 threads, 1..5 chunks of 4 values per thread, ragged last chunk and last step,
+# rows past the end of the last step, with and without smoothing
+STREAM_CASES = [
+    (1024, 16, True), (1031, 48, False), (4099, 144, True), (2048, 4096, True), (1500, 4112, True),
+    (1100, 8192, False), (1024, 12304, True), (1030, 16384, True), (1025, 20480, True), (1040, 20464, False),
+    (3000, 1040, True), (1100, 10240, True), (1024, 2048, False), (1200, 256, True),
+]
+
+
+@pytest.mark.parametrize("M,K,smooth", STREAM_CASES)
+def test_quantize_per_token_streaming(sq, orc, M, K, smooth):
+    X, W, _ = workloads.random_layer(500 + M + K, M, K, 8, np.float16, n_outliers=min(4, K // 8))
+    X[5] = 0                                                        # an all-zero row
+    X[M - 1, : min(K, 64)] = np.float16(6e-8)                       # fp16 subnormals
+    s = orc.smooth_scales(X, W, 0.5)[1] if smooth else None
+    got = gpu_quantize_rows(sq, X, s)
+    ref = orc.quantize_per_token(X, s)
+    assert_bits_equal(got[1], ref[1], "x_scale")
+    assert_bits_equal(got[0], ref[0], "Xq")
+
+
+def test_quantize_streaming_ties_and_tiny_quotients(sq, orc):
+    """Rows whose scale is exactly 1 (half-integer ties round to even), and smoothing
+    factors of 2^110 and 2^120 whose quotients x / s_j fall below the fp32 normal range
+    (the IEEE-division path), on the streaming kernel's shapes."""
+    M, K = 1100, 4096
+    r = np.random.default_rng(31)
+    X = r.standard_normal((M, K)).astype(np.float16)
+    X[:40] = (0.5 * r.integers(-254, 255, (40, K))).astype(np.float16)
+    X[:40, 0] = 127.0                                               # max 127 -> scale 1.0
+    s = r.uniform(0.5, 2.0, K).astype(np.float32)
+    s[[7, 1000, 4095]] = np.float32(2.0 ** 110)
+    s[2048] = np.float32(2.0 ** 120)
+    for ss in (None, np.ones(K, np.float32), s):
+        got = gpu_quantize_rows(sq, X, ss)
+        ref = orc.quantize_per_token(X, ss)
+        assert_bits_equal(got[1], ref[1], "x_scale")
+        assert_bits_equal(got[0], ref[0], "Xq")
+
+
 # ---------------------------------------------------------------------------
 # a1-a2: calibration maximum and smoothing factors
 # ---------------------------------------------------------------------------
@@ -311,6 +352,9 @@ def gpu_outlier(sq, X, W16, Wq, ws, bias, thr):
 @pytest.mark.parametrize("M,N,K,n_out,thr", [
     (48, 40, 256, 3, 6.0), (300, 520, 1024, 7, 6.0), (17, 64, 512, 20, 6.0),
     (64, 96, 256, 3, float("inf")), (40, 72, 128, 0, 0.0), (5, 33, 160, 2, 6.0),
+    # the streaming quantizer's outlier variant (at least 4 rows per CU)
+    (1030, 64, 4112, 9, 6.0), (1024, 48, 8192, 70, 6.0), (2000, 40, 1040, 0, float("inf")),
+    (1100, 32, 512, 0, 0.0),
 ])
 def test_outlier_matmul(sq, orc, M, N, K, n_out, thr):
     X, W16, _ = workloads.random_layer(M + N + K, M, K, N, np.float16, n_outliers=n_out, factor=20.0)
