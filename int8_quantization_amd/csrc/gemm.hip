@@ -45,8 +45,9 @@
 //
 // LLM.int8() ["LLM.int8()技术解析", section 3.1]: when a side product is
 // requested, the dequantized tile becomes the C input of
-// v_mfma_f32_32x32x16_f16 over the gathered fp16 outlier columns, so the fp16
-// result adds onto the int8 result inside the same kernel.
+// v_mfma_f32_32x32x16_f16 over the fp16 outlier columns (activations from a
+// gathered panel, weights read at the outlier columns of the fp16 weight's
+// rows), so the fp16 result adds onto the int8 result inside the same kernel.
 #include <algorithm>
 #include <type_traits>
 
@@ -97,7 +98,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
     void* __restrict__ Yv, int32_t* __restrict__ acc_out, const _Float16* __restrict__ Xo,
-    const _Float16* __restrict__ Wo, const int32_t* __restrict__ cnt, int64_t ldo, int64_t ldy, int tiles_m,
+    const _Float16* __restrict__ W16, const int32_t* __restrict__ sidx, const int32_t* __restrict__ cnt, int64_t ldo,
+    int64_t ldy, int tiles_m,
     int tiles_n) {
     constexpr int BK = 128;                  // bytes of K per stage: one cache line per row
     constexpr int S = 2;                     // LDS stages
@@ -320,6 +322,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     block_barrier();                                      // ring no longer read
     // LLM.int8() side operands of this wave's rows and columns for the first 16 outlier columns,
     // loaded in one batch so their latencies overlap (more than 16 columns load per chunk below).
+    // Activations come from the gathered panel Xo [M x ldo]; weights straight from the fp16
+    // weight's rows, at the outlier columns sidx[t].
     auto side_frag = [&](const _Float16* p, bool ok, int tk) {
         h8 v{};
         if (ok) {
@@ -329,8 +333,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         }
         return v;
     };
+    auto wside_frag = [&](const _Float16* row, bool ok, const int* col, int tk) {
+        h8 v{};
+        if (ok)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = tk + e < side_cnt ? row[col[e]] : (_Float16)0.0f;
+        return v;
+    };
     h8 xpre[SIDE ? TM : 1], wpre[SIDE ? TN : 1];
     if constexpr (SIDE) {
+        int col[8];                                      // this lane's outlier columns 8 lk .. 8 lk + 7
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[e] = 8 * lk + e < side_cnt ? sidx[8 * lk + e] : 0;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int arow = m0 + wm * WTM + i * 32 + lrow;
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int bcol = n0 + wn * WTN + j * 32 + lrow;
-            wpre[j] = side_frag(Wo + (int64_t)(bcol < N ? bcol : 0) * ldo, bcol < N && side_cnt > 0, 8 * lk);
+            wpre[j] = wside_frag(W16 + (int64_t)(bcol < N ? bcol : 0) * K, bcol < N && side_cnt > 0, col, 8 * lk);
         }
     }
     if constexpr (SIDE) wait_all_loads();
@@ -421,8 +435,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                     if (side_cnt > 0) y = __builtin_amdgcn_mfma_f32_32x32x16_f16(wpre[j], xpre[i], y, 0, 0, 0);
                     for (int t0 = 16; t0 < side_cnt; t0 += 16) {
                         const int tk = t0 + 8 * lk;   // this lane's 8 k-slots
+                        int col[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) col[e] = tk + e < side_cnt ? sidx[tk + e] : 0;
                         const h8 xa = side_frag(Xo + (int64_t)(arow < M ? arow : 0) * ldo, arow < M, tk);
-                        const h8 wb = side_frag(Wo + (int64_t)(bcol < N ? bcol : 0) * ldo, bcol < N, tk);
+                        const h8 wb = wside_frag(W16 + (int64_t)(bcol < N ? bcol : 0) * K, bcol < N, col, tk);
                         y = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb, xa, y, 0, 0, 0);
                     }
                 }
@@ -504,12 +521,13 @@ hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float*
                const SideArgs* side, hipStream_t st) {
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const _Float16* Xo = side ? side->Xo : nullptr;
-    const _Float16* Wo = side ? side->Wo : nullptr;
+    const _Float16* W16 = side ? side->W16 : nullptr;
+    const int32_t* sidx = side ? side->idx : nullptr;
     const int32_t* cnt = side ? side->count : nullptr;
     const int64_t ldo = side ? side->ldo : 0;
     SQ_LAUNCH((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE, FP8>), dim3((unsigned)(tm * tn)),
                        dim3(64 * WM * WN), 0, st, Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out,
-                       Xo, Wo, cnt, ldo, ldy, tm, tn);
+                       Xo, W16, sidx, cnt, ldo, ldy, tm, tn);
     return hipSuccess;
 }
 
@@ -585,7 +603,7 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
             SideArgs side2{};
             if (side) {
                 side2 = *side;
-                side2.Wo = side->Wo + n_main * side->ldo;     // outlier weight rows of the remaining columns
+                side2.W16 = side->W16 + n_main * K;           // weight rows of the remaining columns
             }
             return launch_cols(Xq, xs, Wq + n_main * K, ws + n_main * ws_stride, ws_stride,
                                bias ? bias + n_main : nullptr, M, N - n_main, K,

@@ -5,10 +5,10 @@
 // The column maxima come from the shared column-absmax kernel.  Here one block
 // turns them into the ascending outlier list, a per-column slot (or -1) and the
 // count, with a block-wide prefix sum of per-thread counts; the count stays on the device and
-// every later kernel reads it, so the host never waits.  A second kernel
-// gathers the weight's outlier columns into a dense [N x count] fp16 panel for
-// the side MFMA product (the activation columns are gathered by the
-// quantization kernel, which reads every row anyway).
+// every later kernel reads it, so the host never waits.  (The activation columns
+// are gathered by the quantization kernel, which reads every row anyway; the
+// GEMM reads the weight's outlier columns in place.)  Rows the streaming
+// quantizer takes do the compaction there instead.
 #include "sq_internal.h"
 
 namespace sq {
@@ -74,30 +74,12 @@ __global__ __launch_bounds__(1024) void outlier_compact_kernel(const uint32_t* _
     }
 }
 
-// Wo[n * ldo + t] = W16[n * K + idx[t]], t < *count; 4 rows per block, 64 lanes per row.
-__global__ __launch_bounds__(256) void gather_cols_kernel(const _Float16* __restrict__ W16, int64_t N, int64_t K,
-                                                          const int32_t* __restrict__ idx,
-                                                          const int32_t* __restrict__ count,
-                                                          _Float16* __restrict__ Wo) {
-    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (n >= N) return;
-    const int c = *count;
-    for (int t = lane; t < c; t += 64) Wo[n * K + t] = W16[n * K + idx[t]];
-}
-
 }  // namespace
 
 hipError_t launch_outlier_compact(const uint32_t* cmax_bits, int64_t K, float threshold, int32_t* idx, int32_t* pos,
                                   int32_t* count, int32_t* user_count, int32_t* user_idx, hipStream_t st) {
     SQ_LAUNCH(outlier_compact_kernel, dim3(1), dim3(1024), 0, st, cmax_bits, K, threshold, idx, pos, count,
                        user_count, user_idx);
-    return hipSuccess;
-}
-
-hipError_t launch_gather_cols(const _Float16* W16, int64_t N, int64_t K, const int32_t* idx, const int32_t* count,
-                              _Float16* Wo, hipStream_t st) {
-    SQ_LAUNCH(gather_cols_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, W16, N, K, idx, count, Wo);
     return hipSuccess;
 }
 

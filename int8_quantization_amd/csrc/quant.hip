@@ -374,8 +374,8 @@ static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s,
 hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const float* s, int mode,
                              int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st, int fmt) {
     const bool outl = pos != nullptr;
-    if (dt == SQ_F16 && fmt == 0 && (mode == 0 || mode == 1) && quant_stream_applies(M, K, mode == 1, outl))
-        return launch_quant_stream(static_cast<const _Float16*>(X), M, K, mode == 1 ? s : nullptr, Xq, scale, pos, Xo,
+    if (dt == SQ_F16 && fmt == 0 && !outl && (mode == 0 || mode == 1) && quant_stream_applies(M, K, mode == 1, false))
+        return launch_quant_stream(static_cast<const _Float16*>(X), M, K, mode == 1 ? s : nullptr, Xq, scale, nullptr,
                                    st);
     if (fmt == 1) {   // FP8 E4M3 codes (no outlier variant)
 #define SQ_QR8(T, MD) return quant_rows_t<T, MD, false, 1>((const T*)X, M, K, s, Xq, scale, nullptr, nullptr, st)

@@ -2,8 +2,12 @@
 // shapes' hot path of the fused smoothing + per-token quantization
 // ["量化基础与INT8", 量化流程示例: per-row absmax scale, round, clamp;
 // "SmoothQuant量化实战", sections 3.3-3.4: X' = X / s before quantizing], and
-// its LLM.int8() variant ["LLM.int8()技术解析", section 3.1: outlier columns
-// leave the int8 part and are copied out for the fp16 product].
+// its LLM.int8() variant ["LLM.int8()技术解析", section 3.1: the columns whose
+// absolute maximum exceeds the threshold leave the int8 part and are multiplied
+// in fp16].  In that variant every block also turns the column maxima into the
+// ascending outlier slots (a block-wide scan; block 0 writes the list and the
+// count) and copies the outlier values of its rows out for the fp16 product, so
+// the bookkeeping needs no launch of its own.
 //
 // Persistent blocks (NT threads: two 512-thread blocks per CU, or one of 1024 for
 // rows over 8192 values) walk steps of G consecutive rows (G row groups of NT/G
@@ -118,13 +122,15 @@ template <int NT, int CH, bool SMOOTH, bool OUTL>
 __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(const _Float16* __restrict__ X, int M, int K,
                                                                    const float* __restrict__ s,
                                                                    int8_t* __restrict__ Xq, float* __restrict__ scale,
-                                                                   const int32_t* __restrict__ pos,
-                                                                   _Float16* __restrict__ Xo, int G, int steps) {
+                                                                   OutlierSplit os, int G, int steps) {
     using RG = Ring<NT, CH>;
     constexpr int R = RG::R, L = RG::L, SLOT = RG::SLOT, NW = RG::NW;
     constexpr bool COLS = SMOOTH || OUTL;         // per-column constants to stage
     __shared__ __attribute__((aligned(1024))) int8_t ring[R * SLOT];
     __shared__ __attribute__((aligned(16))) float red[2][NW];
+    constexpr int CPT_MAX = NT == 512 ? 16 : 20;  // K / NT: outlier-compaction columns per thread
+    __shared__ int ocnt[OUTL ? CPT_MAX * NW : 1];   // per-(q, wave) counts, then their exclusive scan
+    _Float16* __restrict__ Xo = os.Xo;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -155,14 +161,14 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
         }
     };
 
-    // Prologue.  The per-column array (s, or the outlier slots) is DMA'd into the last NP
+    // Prologue.  The per-column array (s, or the column maxima) is DMA'd into the last NP
     // slots of the ring, the first R - NP steps into the others; once the array has landed
     // the constants are computed while those steps are in flight, then the remaining steps
     // are requested.  Every wave issues the same instructions, so the counts below hold
     // for each wave.
     const int NP = COLS ? (int)(((uint32_t)K * 4u + SLOT - 1) / SLOT) : 0;   // 1 .. R-1 slots
     if constexpr (COLS) {
-        const v4i rP = buffer_desc(SMOOTH ? (const void*)s : (const void*)pos, (uint32_t)K * 4u);
+        const v4i rP = buffer_desc(SMOOTH ? (const void*)s : (const void*)os.cmax, (uint32_t)K * 4u);
         const uint32_t pbase = lds_base + (uint32_t)(R - NP) * SLOT;
         // K * 4 <= 16 bytes x NT x CH: at most CH 1 KB blocks per wave; blocks past the array read
         // zeros, and none is written past the NP slots (a wave-uniform condition; the count
@@ -181,12 +187,78 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
     int opos[OUTL ? CH : 1][4];
     unsigned ochunks = 0;                         // bit i: some lane of this wave has an outlier in chunk i
     bool guard = false;                           // some x / s_j may fall below the fp32 normal range
+    // LLM.int8() outlier columns c = tid + NT q (q < cpt) of this thread
+    const int cpt = (K + NT - 1) / NT;
+    unsigned oflags = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
 #pragma unroll
     for (int i = 0; i < CH; ++i) valid[i] = t + i * tpg < nch;
     if constexpr (COLS) {
         wait_vm_k<0, L, R - 1>(R - NP);           // the array landed (R - NP steps' DMA issued after it)
         barrier_lds();
-        const int8_t* P = ring + (R - NP) * SLOT;
+        int8_t* P = ring + (R - NP) * SLOT;
+        if constexpr (OUTL) {
+            // Compaction, in every block: column c is an outlier when its maximum exceeds the
+            // threshold, and slots ascend with c.  Columns are visited as c = tid + NT q, so
+            // every LDS access is conflict-free; the slot of c counts the flagged columns of
+            // the rows q' < q and of the waves w' < w in row q (an exclusive scan of the
+            // per-(q, wave) counts, done by wave 0) plus the flagged lanes below in its wave.
+            // The slots replace the maxima in LDS; block 0 also writes the ascending column
+            // list and the count for the later kernels.
+            int* cnt = ocnt;
+#pragma unroll
+            for (int q = 0; q < CPT_MAX; ++q) {
+                const int c = tid + NT * q;
+                const bool f = q < cpt && c < K &&
+                               __uint_as_float(*reinterpret_cast<const uint32_t*>(P + 4 * c)) > os.threshold;
+                oflags |= (unsigned)f << q;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+                if (lane == 0 && q < cpt) cnt[q * NW + wave] = __builtin_popcountll(m);
+            }
+            barrier_lds();
+            if (wave == 0) {                      // exclusive scan of the cpt * NW counts, E per lane
+                constexpr int E = (CPT_MAX * NW + 63) / 64;
+                const int n = cpt * NW;
+                int a[E], sum = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    a[e] = E * lane + e < n ? cnt[E * lane + e] : 0;
+                    sum += a[e];
+                }
+                int incl = sum;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int u = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += u;
+                }
+                int ex = incl - sum;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (E * lane + e < n) cnt[E * lane + e] = ex;
+                    ex += a[e];
+                }
+                if (lane == 63 && blockIdx.x == 0) {
+                    *os.count = incl;
+                    if (os.user_count) *os.user_count = incl;
+                }
+            }
+            barrier_lds();
+#pragma unroll
+            for (int q = 0; q < CPT_MAX; ++q) {
+                const int c = tid + NT * q;
+                if (q < cpt && c < K) {
+                    const bool f = (oflags >> q) & 1u;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+                    const int slot = cnt[q * NW + wave] + __builtin_popcountll(m & below);
+                    *reinterpret_cast<int32_t*>(P + 4 * c) = f ? slot : -1;
+                    if (f && blockIdx.x == 0) {
+                        os.idx[slot] = c;
+                        if (os.user_idx) os.user_idx[slot] = c;
+                    }
+                }
+            }
+            barrier_lds();                        // every slot is in LDS
+        }
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int cc = valid[i] ? t + i * tpg : 0;
@@ -297,32 +369,32 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
 }
 
 template <int NT, int CH, bool SMOOTH, bool OUTL>
-hipError_t launch_ch(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, const int32_t* pos,
-                     _Float16* Xo, int G, hipStream_t st) {
+hipError_t launch_ch(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, const OutlierSplit& os,
+                     int G, hipStream_t st) {
     const int64_t total = ((int64_t)M + G - 1) / G;               // steps over all blocks
     const int64_t slots = (int64_t)dev_info().cus * (NT == 1024 ? 1 : 2);
     const int nb = (int)(total < slots ? total : slots);
     const int steps = (int)((total + nb - 1) / nb);
     SQ_LAUNCH((quant_stream_kernel<NT, CH, SMOOTH, OUTL>), dim3((unsigned)nb), dim3(NT), 0, st, X, M, K, s, Xq, scale,
-              pos, Xo, G, steps);
+              os, G, steps);
     return hipSuccess;
 }
 
 template <bool SMOOTH, bool OUTL>
-hipError_t launch_mode(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, const int32_t* pos,
-                       _Float16* Xo, int nt, int G, int ch, hipStream_t st) {
+hipError_t launch_mode(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, const OutlierSplit& os,
+                       int nt, int G, int ch, hipStream_t st) {
     if (nt == 512) {
         switch (ch) {
-            case 1: return launch_ch<512, 1, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
-            case 2: return launch_ch<512, 2, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
-            case 3: return launch_ch<512, 3, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
-            default: return launch_ch<512, 4, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+            case 1: return launch_ch<512, 1, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
+            case 2: return launch_ch<512, 2, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
+            case 3: return launch_ch<512, 3, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
+            default: return launch_ch<512, 4, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
         }
     }
     switch (ch) {
-        case 3: return launch_ch<1024, 3, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
-        case 4: return launch_ch<1024, 4, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
-        default: return launch_ch<1024, 5, SMOOTH, OUTL>(X, M, K, s, Xq, scale, pos, Xo, G, st);
+        case 3: return launch_ch<1024, 3, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
+        case 4: return launch_ch<1024, 4, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
+        default: return launch_ch<1024, 5, SMOOTH, OUTL>(X, M, K, s, Xq, scale, os, G, st);
     }
 }
 
@@ -338,7 +410,7 @@ bool quant_stream_applies(int64_t M, int64_t K, bool smooth, bool outliers) {
 }
 
 hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
-                               const int32_t* pos, _Float16* Xo, hipStream_t st) {
+                               const OutlierSplit* os, hipStream_t st) {
     // Rows of up to 8192 values: 512-thread blocks, G row groups per step, the most that
     // keep at most 4 chunks per thread (bigger steps spread the per-step reduction and
     // synchronization over more values).  Longer rows: 1024 threads, one row per step,
@@ -348,9 +420,10 @@ hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const fl
     int G = nt / 64;
     while (G > 1 && (nch + nt / G - 1) / (nt / G) > 4) G /= 2;
     const int ch = (int)((nch + nt / G - 1) / (nt / G));
-    if (s) return launch_mode<true, false>(X, (int)M, (int)K, s, Xq, scale, nullptr, nullptr, nt, G, ch, st);
-    if (pos) return launch_mode<false, true>(X, (int)M, (int)K, nullptr, Xq, scale, pos, Xo, nt, G, ch, st);
-    return launch_mode<false, false>(X, (int)M, (int)K, nullptr, Xq, scale, nullptr, nullptr, nt, G, ch, st);
+    const OutlierSplit none{};
+    if (s) return launch_mode<true, false>(X, (int)M, (int)K, s, Xq, scale, none, nt, G, ch, st);
+    if (os) return launch_mode<false, true>(X, (int)M, (int)K, nullptr, Xq, scale, *os, nt, G, ch, st);
+    return launch_mode<false, false>(X, (int)M, (int)K, nullptr, Xq, scale, none, nt, G, ch, st);
 }
 
 }  // namespace sq

@@ -37,7 +37,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // LLM.int8() workspace layout (byte offsets), sized for K outlier columns.
 struct OutlierLayout {
-    size_t cmax, pos, idx, count, xs, xq, xo, wo, total;
+    size_t cmax, pos, idx, count, xs, xq, xo, total;
 };
 OutlierLayout outlier_layout(int64_t M, int64_t N, int64_t K) {
     OutlierLayout L;
@@ -49,8 +49,8 @@ OutlierLayout outlier_layout(int64_t M, int64_t N, int64_t K) {
     L.xs = o;    o = align256(o + 4 * (size_t)M);
     L.xq = o;    o = align256(o + (size_t)M * (size_t)K);
     L.xo = o;    o = align256(o + 2 * (size_t)M * (size_t)K);
-    L.wo = o;    o = align256(o + 2 * (size_t)N * (size_t)K);
     L.total = o;
+    (void)N;
     return L;
 }
 
@@ -201,14 +201,18 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, 
     float* xs = reinterpret_cast<float*>(base + L.xs);
     int8_t* xq = reinterpret_cast<int8_t*>(base + L.xq);
     _Float16* xo = reinterpret_cast<_Float16*>(base + L.xo);
-    _Float16* wo = reinterpret_cast<_Float16*>(base + L.wo);
 
     SQ_TRY(launch_fill_u32(cmax, K, 0u, stream));
     SQ_TRY(launch_colmax(X, SQ_F16, M, K, cmax, stream));
-    SQ_TRY(launch_outlier_compact(cmax, K, threshold, idx, pos, count, n_outliers, outlier_idx, stream));
-    SQ_TRY(launch_quant_rows(X, SQ_F16, M, K, nullptr, 0, xq, xs, pos, xo, stream));
-    SQ_TRY(launch_gather_cols(static_cast<const _Float16*>(W16), N, K, idx, count, wo, stream));
-    SideArgs side{xo, wo, count, K};
+    if (quant_stream_applies(M, K, false, true)) {
+        // the compaction and the activation gather inside the streaming quantizer
+        const OutlierSplit os{cmax, threshold, idx, count, n_outliers, outlier_idx, xo};
+        SQ_TRY(launch_quant_stream(static_cast<const _Float16*>(X), M, K, nullptr, xq, xs, &os, stream));
+    } else {
+        SQ_TRY(launch_outlier_compact(cmax, K, threshold, idx, pos, count, n_outliers, outlier_idx, stream));
+        SQ_TRY(launch_quant_rows(X, SQ_F16, M, K, nullptr, 0, xq, xs, pos, xo, stream));
+    }
+    SideArgs side{xo, static_cast<const _Float16*>(W16), idx, count, K};
     return hip_status(launch_gemm(xq, xs, Wq, w_scale, 1, bias, M, N, K, Y, SQ_F16, acc_out, &side, stream));
 }
 

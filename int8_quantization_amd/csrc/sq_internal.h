@@ -153,12 +153,26 @@ hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const 
                              int mode, int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo,
                              hipStream_t st, int fmt = 0);
 
-// The streaming fp16 per-token quantizer (int8 codes; s == nullptr: no smoothing; pos / Xo:
-// the LLM.int8() outlier columns as for launch_quant_rows), for the shapes where
-// quant_stream_applies() holds; launch_quant_rows dispatches to it.
+// The LLM.int8() split done inside the streaming quantizer: from the column maxima (float
+// bits) and the threshold, the ascending outlier list and count (written to idx / count and
+// the optional user copies) and the outlier activations Xo [M x K] (row stride K, the first
+// count columns used).
+struct OutlierSplit {
+    const uint32_t* cmax;
+    float threshold;
+    int32_t* idx;
+    int32_t* count;
+    int32_t* user_count;
+    int32_t* user_idx;
+    _Float16* Xo;
+};
+
+// The streaming fp16 per-token quantizer (int8 codes; s == nullptr: no smoothing; os: the
+// LLM.int8() variant, without smoothing), for the shapes where quant_stream_applies()
+// holds; launch_quant_rows dispatches to it for plain and smoothed rows.
 bool quant_stream_applies(int64_t M, int64_t K, bool smooth, bool outliers);
 hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
-                               const int32_t* pos, _Float16* Xo, hipStream_t st);
+                               const OutlierSplit* os, hipStream_t st);
 
 // Running column absolute maximum: amax_bits[j] = max(amax_bits[j], bits(max_m |X[m,j]|)),
 // where amax_bits holds non-negative floats as their bit patterns (monotone as uint32).
@@ -174,10 +188,12 @@ hipError_t launch_quant_tensor(const void* W, int dt, int64_t N, int64_t K, cons
                                int8_t* Wq, float* w_scale, uint32_t* gmax_bits, hipStream_t st, int fmt = 0);
 
 // int8 GEMM + dequant epilogue (M > 16).  side != nullptr adds the LLM.int8() fp16 side
-// product over the first *count columns of Xo [M x ldo] and Wo [N x ldo].
+// product sum_{t < *count} Xo[m, t] * W16[n, idx[t]]: Xo [M x ldo] the gathered outlier
+// activations, W16 [N x K] the fp16 weight, idx the ascending outlier columns.
 struct SideArgs {
     const _Float16* Xo;
-    const _Float16* Wo;
+    const _Float16* W16;
+    const int32_t* idx;
     const int32_t* count;
     int64_t ldo;
 };
@@ -211,9 +227,6 @@ hipError_t launch_outlier_compact(const uint32_t* cmax_bits, int64_t K, float th
                                   int32_t* idx, int32_t* pos, int32_t* count, int32_t* user_count,
                                   int32_t* user_idx, hipStream_t st);
 
-// Wo[n, t] = W16[n, idx[t]] for t < *count.
-hipError_t launch_gather_cols(const _Float16* W16, int64_t N, int64_t K, const int32_t* idx,
-                              const int32_t* count, _Float16* Wo, hipStream_t st);
 
 // LayerNorm (weights with the smoothing folded in) + per-token quantization, fp16 rows.
 hipError_t launch_ln_quant(const _Float16* X, int64_t M, int64_t K, const float* gamma, const float* beta,

@@ -354,7 +354,7 @@ def gpu_outlier(sq, X, W16, Wq, ws, bias, thr):
     (64, 96, 256, 3, float("inf")), (40, 72, 128, 0, 0.0), (5, 33, 160, 2, 6.0),
     # the streaming quantizer's outlier variant (at least 4 rows per CU)
     (1030, 64, 4112, 9, 6.0), (1024, 48, 8192, 70, 6.0), (2000, 40, 1040, 0, float("inf")),
-    (1100, 32, 512, 0, 0.0),
+    (1100, 32, 512, 0, 0.0), (1100, 48, 16384, 30, 6.0), (1030, 40, 20480, 140, 6.0), (1024, 24, 12304, 3, 6.0),
 ])
 def test_outlier_matmul(sq, orc, M, N, K, n_out, thr):
     X, W16, _ = workloads.random_layer(M + N + K, M, K, N, np.float16, n_outliers=n_out, factor=20.0)
