@@ -50,8 +50,8 @@ namespace {
 constexpr int kWaves = 8;
 
 // Row groups per tile and persistent blocks per CU, measured on 70B-class decode shapes: for M <= 4
-// with the activations held in registers (A) or reloaded per k chunk (AC), for M <= 8 (B) and
-// for M <= 16 (C).
+// with the activations held in registers (A) or reloaded per k chunk (AC), for M <= 8 (B, two
+// token groups of 4) and for M <= 16 (C).
 #ifndef SQ_GV_A_RG
 #define SQ_GV_A_RG 1
 #endif
@@ -65,7 +65,7 @@ constexpr int kWaves = 8;
 #define SQ_GV_AC_PCU 2
 #endif
 #ifndef SQ_GV_B_RG
-#define SQ_GV_B_RG 2
+#define SQ_GV_B_RG 1
 #endif
 #ifndef SQ_GV_B_PCU
 #define SQ_GV_B_PCU 1
@@ -396,12 +396,14 @@ hipError_t gemv_dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, co
         return SQ_GEMV(4, 1, SQ_GV_AC_RG, 8, false, SQ_GV_AC_PCU);
     }
     if (M <= 8) {
-        // 8 rows x 128 bytes per load, one token group of 8.
-        const int per = per_of(128);
-        if (per <= 2) return SQ_GEMV(8, 1, SQ_GV_B_RG, 2, true, SQ_GV_B_PCU);
-        if (per <= 4) return SQ_GEMV(8, 1, SQ_GV_B_RG, 4, true, SQ_GV_B_PCU);
-        if (per <= 8) return SQ_GEMV(8, 1, SQ_GV_B_RG, 8, true, SQ_GV_B_PCU);
-        return SQ_GEMV(8, 1, SQ_GV_B_RG, 8, false, SQ_GV_B_PCU);
+        // 4 rows x 256 bytes per load, two token groups of 4 (measured 6-7% faster on the 70B
+        // FFN-up rows at M = 8 than 8 rows x 128 bytes with one group of 8).
+        const int per = per_of(256);
+        if (per <= 1) return SQ_GEMV(4, 2, SQ_GV_B_RG, 1, true, SQ_GV_B_PCU);
+        if (per <= 2) return SQ_GEMV(4, 2, SQ_GV_B_RG, 2, true, SQ_GV_B_PCU);
+        if (per <= 4) return SQ_GEMV(4, 2, SQ_GV_B_RG, 4, true, SQ_GV_B_PCU);
+        if (per <= 8) return SQ_GEMV(4, 2, SQ_GV_B_RG, 8, true, SQ_GV_B_PCU);
+        return SQ_GEMV(4, 2, SQ_GV_B_RG, 8, false, SQ_GV_B_PCU);
     }
     // 8 rows x 128 bytes per load, two token groups.
     const int per = per_of(128);

@@ -220,6 +220,8 @@ GEMM_CASES = [
     # decode kernel with the activation slice reloaded per k chunk (K beyond what a wave keeps in
     # registers), ragged N and K
     (2, 301, 20496), (8, 130, 12304), (16, 257, 12288), (3, 4100, 16400),
+    # M = 5..8: two token groups of 4 (activations in registers, and reloaded per k chunk)
+    (5, 1000, 8192), (6, 301, 20496), (8, 4100, 8192), (7, 9, 272),
     (17, 32, 16), (33, 70, 144), (200, 300, 1040), (256, 256, 256), (300, 520, 4112),
     # the largest K the library accepts: (-128)*(-128)*K = 2147221504 still fits int32; the tile
     # kernel also gets a partial last K tile (131056 % 128 = 112)
