@@ -166,6 +166,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         voff[i] = (uint32_t)(row * K + kc * 16);
         ldsoff[i] = blk * 1024;
     }
+    // Materialized here, so that the prologue's loads do not share registers with them (a
+    // register still feeding an earlier load is rewritten only after that load completes).
+#pragma unroll
+    for (int i = 0; i < L; ++i) asm volatile("" ::"v"(voff[i]));
     auto dma = [&](int stage, int k0) {
 #pragma unroll
         for (int i = 0; i < L; ++i)
@@ -240,19 +244,92 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const bool has_tail = (K % BK) != 0;
     const int nk = nfull + (has_tail ? 1 : 0);
     auto kofs = [&](int j) { return (has_tail ? (j == 0 ? nfull : j - 1) : j) * BK; };
+    // LLM.int8() side operands: 8 consecutive outlier columns from tk on, zero past the count.
+    // Activations come from the panel Xo [M x ldo]; weights straight from the fp16 weight's
+    // rows, at the outlier columns col[e] = sidx[tk + e].
+    auto side_frag = [&](const _Float16* p, bool ok, int tk) {
+        h8 v{};
+        if (ok) {
+            if (tk + 8 <= side_cnt) v = *reinterpret_cast<const h8*>(p + tk);
+            else
+                for (int e = 0; e < 8; ++e) v[e] = tk + e < side_cnt ? p[tk + e] : (_Float16)0.0f;
+        }
+        return v;
+    };
+    auto wside_frag = [&](const _Float16* row, bool ok, const int* col, int tk) {
+        h8 v{};
+        if (ok)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = tk + e < side_cnt ? row[col[e]] : (_Float16)0.0f;
+        return v;
+    };
+    // The tile's side operands for the first 16 outlier columns are read in the prologue, so
+    // that their latency (scattered 2-byte reads of the fp16 weight) overlaps the first K
+    // tile's, and kept in LDS for the epilogue: thread t holds 8 columns (8 (t % 2) on) of
+    // tile row t / 2 and of tile column t / 2.
+    static_assert(!SIDE || (2 * BM <= NT && 2 * BN <= NT), "one side chunk per thread");
+    __shared__ __attribute__((aligned(16))) _Float16 sxo[SIDE ? BM : 1][16], swo[SIDE ? BN : 1][16];
+    const int so_r = tid >> 1, so_c = 8 * (tid & 1);
+    // When the panel rows and the outlier list hold at least 16 entries (the usual case), the
+    // loads are issued unconditionally, in one batch, and the values past the count (or of rows
+    // past M, N) are zeroed when they are stored: columns past the count read column 0 of the
+    // weight row and the panel's unused columns.  Otherwise the guarded per-element form.
+    const bool side_fast = SIDE && ldo >= 16 && K >= 16;
+    h8 xo_v{}, wo_v{};
+    v4i c_lo{}, c_hi{};
+    const int so_row = m0 + (so_r < BM ? so_r : 0), so_col = n0 + (so_r < BN ? so_r : 0);
+    const bool xo_ok = SIDE && so_r < BM && so_row < M, wo_ok = SIDE && so_r < BN && so_col < N;
+    const _Float16* xo_p = SIDE ? Xo + (int64_t)(so_row < M ? so_row : 0) * ldo : nullptr;
+    const _Float16* wo_p = SIDE ? W16 + (int64_t)(so_col < N ? so_col : 0) * K : nullptr;
+    _Float16 wo_r[8];
+    if constexpr (SIDE) {
+        if (side_fast) {
+            // the outlier list first (a few bytes, resident in L2 after the first tile); the
+            // weight columns, the panel row and the scales then go out together
+            c_lo = *reinterpret_cast<const v4i*>(sidx + so_c);
+            c_hi = *reinterpret_cast<const v4i*>(sidx + so_c + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wo_r[e] = wo_p[so_c + e < side_cnt ? (e < 4 ? c_lo[e] : c_hi[e - 4]) : 0];
+            xo_v = *reinterpret_cast<const h8*>(xo_p + so_c);
+        } else {
+            if (xo_ok) xo_v = side_frag(xo_p, side_cnt > 0, so_c);
+            if (wo_ok) {
+                int col[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) col[e] = so_c + e < side_cnt ? sidx[so_c + e] : 0;
+                wo_v = wside_frag(wo_p, side_cnt > 0, col, so_c);
+            }
+        }
+    }
+    // Dequantization scales of the tile's rows and columns: thread t loads row t's and
+    // column t's, all issued before the first K tile's DMA, so that the prologue waits once
+    // for everything; the prologue barrier publishes them.
+    static_assert(BM <= NT && BN <= NT, "one row and one column scale per thread");
+    float xs_v = 0.0f, ws_v = 0.0f, b_v = -0.0f;   // x + (-0.0) == x for every x: no bias
+    if (tid < BM) xs_v = xs[m0 + tid < M ? m0 + tid : M - 1];
+    if (tid < BN) {
+        const int n = n0 + tid < N ? n0 + tid : N - 1;
+        ws_v = ws[(int64_t)n * ws_stride];
+        if (bias != nullptr) b_v = bias[n];
+    }
     if (has_tail) tail_tile(0, kofs(0));
     else dma(0, kofs(0));
-    // Dequantization scales of the tile's rows and columns, loaded while the first
-    // K tile is in flight (the prologue barrier publishes them).
     __shared__ float sxs[BM], sws[BN], sbias[BN];
-    for (int r = tid; r < BM; r += NT) {
-        const int m = m0 + r;
-        sxs[r] = xs[m < M ? m : M - 1];
+    if (tid < BM) sxs[tid] = xs_v;
+    if (tid < BN) {
+        sws[tid] = ws_v;
+        sbias[tid] = b_v;
     }
-    for (int c = tid; c < BN; c += NT) {
-        const int n = n0 + c < N ? n0 + c : N - 1;
-        sws[c] = ws[(int64_t)n * ws_stride];
-        sbias[c] = bias != nullptr ? bias[n] : -0.0f;   // x + (-0.0) == x for every x
+    if constexpr (SIDE) {
+        if (side_fast)   // zero the values past the count and of rows past M, N
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool live = so_c + e < side_cnt;
+                xo_v[e] = xo_ok && live ? xo_v[e] : (_Float16)0.0f;
+                wo_v[e] = wo_ok && live ? wo_r[e] : (_Float16)0.0f;
+            }
+        if (so_r < BM) *reinterpret_cast<h8*>(&sxo[so_r][so_c]) = xo_v;
+        if (so_r < BN) *reinterpret_cast<h8*>(&swo[so_r][so_c]) = wo_v;
     }
     // The epilogue's kernel arguments go to registers now: scalar loads still in
     // flight when the loop starts would make the compiler's fragment waits in it
@@ -320,43 +397,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 
     wait_all_loads();
     block_barrier();                                      // ring no longer read
-    // LLM.int8() side operands of this wave's rows and columns for the first 16 outlier columns,
-    // loaded in one batch so their latencies overlap (more than 16 columns load per chunk below).
-    // Activations come from the gathered panel Xo [M x ldo]; weights straight from the fp16
-    // weight's rows, at the outlier columns sidx[t].
-    auto side_frag = [&](const _Float16* p, bool ok, int tk) {
-        h8 v{};
-        if (ok) {
-            if (tk + 8 <= side_cnt) v = *reinterpret_cast<const h8*>(p + tk);
-            else
-                for (int e = 0; e < 8; ++e) v[e] = tk + e < side_cnt ? p[tk + e] : (_Float16)0.0f;
-        }
-        return v;
-    };
-    auto wside_frag = [&](const _Float16* row, bool ok, const int* col, int tk) {
-        h8 v{};
-        if (ok)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = tk + e < side_cnt ? row[col[e]] : (_Float16)0.0f;
-        return v;
-    };
+    // LLM.int8() side operands of this wave's rows and columns for the first 16 outlier
+    // columns, from the prologue's LDS copy (more than 16 columns load per chunk below).
     h8 xpre[SIDE ? TM : 1], wpre[SIDE ? TN : 1];
     if constexpr (SIDE) {
-        int col[8];                                      // this lane's outlier columns 8 lk .. 8 lk + 7
 #pragma unroll
-        for (int e = 0; e < 8; ++e) col[e] = 8 * lk + e < side_cnt ? sidx[8 * lk + e] : 0;
+        for (int i = 0; i < TM; ++i) xpre[i] = *reinterpret_cast<const h8*>(&sxo[wm * WTM + i * 32 + lrow][8 * lk]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int arow = m0 + wm * WTM + i * 32 + lrow;
-            xpre[i] = side_frag(Xo + (int64_t)(arow < M ? arow : 0) * ldo, arow < M && side_cnt > 0, 8 * lk);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int bcol = n0 + wn * WTN + j * 32 + lrow;
-            wpre[j] = wside_frag(W16 + (int64_t)(bcol < N ? bcol : 0) * K, bcol < N && side_cnt > 0, col, 8 * lk);
-        }
+        for (int j = 0; j < TN; ++j) wpre[j] = *reinterpret_cast<const h8*>(&swo[wn * WTN + j * 32 + lrow][8 * lk]);
     }
-    if constexpr (SIDE) wait_all_loads();
 
     // This lane's row and column scales for the whole epilogue, read from LDS in
     // one batch (one latency instead of one per accumulator group); the optional
