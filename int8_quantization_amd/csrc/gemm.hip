@@ -270,40 +270,39 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     static_assert(!SIDE || (2 * BM <= NT && 2 * BN <= NT), "one side chunk per thread");
     __shared__ __attribute__((aligned(16))) _Float16 sxo[SIDE ? BM : 1][16], swo[SIDE ? BN : 1][16];
     const int so_r = tid >> 1, so_c = 8 * (tid & 1);
-    // When the panel rows and the outlier list hold at least 16 entries (the usual case), the
-    // loads are issued unconditionally, in one batch, and the values past the count (or of rows
-    // past M, N) are zeroed when they are stored: columns past the count read column 0 of the
-    // weight row and the panel's unused columns.  Otherwise the guarded per-element form.
+    // With panel rows and an outlier list of at least 16 entries (the usual case) the loads are
+    // issued unconditionally, in one batch, and the values past the count (or of rows past M,
+    // N) are zeroed when they are stored; columns past the count read column 0 of the weight
+    // row and the panel's unused columns.  Otherwise guarded per-element loads.
     const bool side_fast = SIDE && ldo >= 16 && K >= 16;
     h8 xo_v{}, wo_v{};
-    v4i c_lo{}, c_hi{};
     const int so_row = m0 + (so_r < BM ? so_r : 0), so_col = n0 + (so_r < BN ? so_r : 0);
     const bool xo_ok = SIDE && so_r < BM && so_row < M, wo_ok = SIDE && so_r < BN && so_col < N;
     const _Float16* xo_p = SIDE ? Xo + (int64_t)(so_row < M ? so_row : 0) * ldo : nullptr;
     const _Float16* wo_p = SIDE ? W16 + (int64_t)(so_col < N ? so_col : 0) * K : nullptr;
     _Float16 wo_r[8];
+    // The first K tile's DMA goes out first.
+    if (has_tail) tail_tile(0, kofs(0));
+    else dma(0, kofs(0));
     if constexpr (SIDE) {
         if (side_fast) {
-            // the outlier list first (a few bytes, resident in L2 after the first tile); the
-            // weight columns, the panel row and the scales then go out together
-            c_lo = *reinterpret_cast<const v4i*>(sidx + so_c);
-            c_hi = *reinterpret_cast<const v4i*>(sidx + so_c + 4);
+            // The outlier list through scalar loads (uniform addresses; they wait on their own
+            // counter, not behind the DMA), then the weight columns and the panel row.
+            int cl[16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wo_r[e] = wo_p[so_c + e < side_cnt ? (e < 4 ? c_lo[e] : c_hi[e - 4]) : 0];
-            xo_v = *reinterpret_cast<const h8*>(xo_p + so_c);
-        } else {
-            if (xo_ok) xo_v = side_frag(xo_p, side_cnt > 0, so_c);
-            if (wo_ok) {
-                int col[8];
+            for (int e = 0; e < 16; ++e) cl[e] = __builtin_amdgcn_readfirstlane(sidx[e]);
+            const int hmask = -(tid & 1);   // all ones for the upper 8 columns
 #pragma unroll
-                for (int e = 0; e < 8; ++e) col[e] = so_c + e < side_cnt ? sidx[so_c + e] : 0;
-                wo_v = wside_frag(wo_p, side_cnt > 0, col, so_c);
+            for (int e = 0; e < 8; ++e) {
+                const int c = cl[e] ^ ((cl[e] ^ cl[8 + e]) & hmask);   // a select, kept out of array indexing
+                wo_r[e] = wo_p[so_c + e < side_cnt ? c : 0];
             }
+            xo_v = *reinterpret_cast<const h8*>(xo_p + so_c);
         }
     }
     // Dequantization scales of the tile's rows and columns: thread t loads row t's and
-    // column t's, all issued before the first K tile's DMA, so that the prologue waits once
-    // for everything; the prologue barrier publishes them.
+    // column t's, all in one batch with the loads above, so that the prologue waits once for
+    // everything; the prologue barrier publishes them.
     static_assert(BM <= NT && BN <= NT, "one row and one column scale per thread");
     float xs_v = 0.0f, ws_v = 0.0f, b_v = -0.0f;   // x + (-0.0) == x for every x: no bias
     if (tid < BM) xs_v = xs[m0 + tid < M ? m0 + tid : M - 1];
@@ -312,8 +311,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         ws_v = ws[(int64_t)n * ws_stride];
         if (bias != nullptr) b_v = bias[n];
     }
-    if (has_tail) tail_tile(0, kofs(0));
-    else dma(0, kofs(0));
     __shared__ float sxs[BM], sws[BN], sbias[BN];
     if (tid < BM) sxs[tid] = xs_v;
     if (tid < BN) {
@@ -321,15 +318,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
         sbias[tid] = b_v;
     }
     if constexpr (SIDE) {
-        if (side_fast)   // zero the values past the count and of rows past M, N
+        if (side_fast) {   // zero the values past the count and of rows past M, N
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const bool live = so_c + e < side_cnt;
                 xo_v[e] = xo_ok && live ? xo_v[e] : (_Float16)0.0f;
                 wo_v[e] = wo_ok && live ? wo_r[e] : (_Float16)0.0f;
             }
-        if (so_r < BM) *reinterpret_cast<h8*>(&sxo[so_r][so_c]) = xo_v;
-        if (so_r < BN) *reinterpret_cast<h8*>(&swo[so_r][so_c]) = wo_v;
+            if (so_r < BM) *reinterpret_cast<h8*>(&sxo[so_r][so_c]) = xo_v;
+            if (so_r < BN) *reinterpret_cast<h8*>(&swo[so_r][so_c]) = wo_v;
+        } else {   // guarded per-element loads, last, so that no other code waits behind them
+            if (xo_ok) xo_v = side_frag(xo_p, side_cnt > 0, so_c);
+            if (wo_ok) {
+                int col[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) col[e] = so_c + e < side_cnt ? sidx[so_c + e] : 0;
+                wo_v = wside_frag(wo_p, side_cnt > 0, col, so_c);
+            }
+            if (so_r < BM) *reinterpret_cast<h8*>(&sxo[so_r][so_c]) = xo_v;
+            if (so_r < BN) *reinterpret_cast<h8*>(&swo[so_r][so_c]) = wo_v;
+        }
     }
     // The epilogue's kernel arguments go to registers now: scalar loads still in
     // flight when the loop starts would make the compiler's fragment waits in it
@@ -409,9 +417,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 
     // This lane's row and column scales for the whole epilogue, read from LDS in
     // one batch (one latency instead of one per accumulator group); the optional
-    // bias is read where it is added.  The LLM.int8() variant has no registers to
-    // spare for them and reads the column scales per accumulator group.
-    constexpr bool HOIST = !SIDE;
+    // bias is read where it is added.
+    constexpr bool HOIST = true;
     float xsr[TM];
     v4f wsr[HOIST ? TN : 1][4];
 #pragma unroll
