@@ -467,6 +467,77 @@ hipError_t launch_colmax(const void* X, int dt, int64_t M, int64_t K, uint32_t* 
     return hipSuccess;
 }
 
+// Column absolute maxima of an fp16 matrix, written (not accumulated): block b owns a
+// strip of 8L columns over all M rows, so there are no atomics and the output needs no
+// zeroing launch beforehand.  Thread t reads 16 bytes (8 columns, chunk t % L of the strip)
+// of rows t / L, t / L + 1024 / L, ... four rows at a time; the maxima then meet across
+// the wave's lanes of the same chunk (shuffles) and across the 16 waves (LDS).
+// Strips sharing a 128-byte line (64 / (8L) of them) go to blocks b, b + 8, ..., which
+// the dispatcher places on the same XCD, so each line is fetched into one L2 only.
+template <int L>
+__global__ __launch_bounds__(1024) void colmax_strip_kernel(const _Float16* __restrict__ X, int64_t M, int64_t K,
+                                                            uint32_t* __restrict__ out_bits) {
+    constexpr int W = 8 * L;                 // columns per strip
+    constexpr int G = 64 / W;                // strips per 128-byte line
+    constexpr int R = 1024 / L;              // rows per pass
+    __shared__ float red[16][W];
+    const int S = (int)((K + W - 1) / W);
+    const int b = blockIdx.x;
+    const int full = (S / (8 * G)) * (8 * G);
+    const int strip = b < full ? G * ((b / (8 * G)) * 8 + b % 8) + (b / 8) % G : b;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = tid % L;
+    const int64_t c0 = (int64_t)strip * W + 8 * g;
+    float mx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx[e] = 0.0f;
+    if (c0 < K) {
+        const _Float16* p = X + c0;
+        int64_t m = tid / L;
+        for (; m + 3 * R < M; m += 4 * R) {
+            h8 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(p + (m + u * R) * K));
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mx[e] = __builtin_fmaxf(mx[e], __builtin_fabsf((float)v[u][e]));
+        }
+        for (; m < M; m += R) {
+            const h8 v = __builtin_nontemporal_load(reinterpret_cast<const h8*>(p + m * K));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx[e] = __builtin_fmaxf(mx[e], __builtin_fabsf((float)v[e]));
+        }
+    }
+    // lanes of one chunk differ in lane bits log2(L) and up
+#pragma unroll
+    for (int off = L; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[e] = __builtin_fmaxf(mx[e], __shfl_xor(mx[e], off, 64));
+    if (lane < L)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = mx[e];
+    __syncthreads();
+    if (tid < W && (int64_t)strip * W + tid < K) {
+        float a = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < 16; ++w) a = __builtin_fmaxf(a, red[w][tid]);
+        out_bits[(int64_t)strip * W + tid] = __float_as_uint(a);
+    }
+}
+
+hipError_t launch_colmax_fresh(const _Float16* X, int64_t M, int64_t K, uint32_t* out_bits, hipStream_t st) {
+    const int64_t cus = dev_info().cus;
+    // the widest strip that still gives every CU a block
+    if (K / 32 >= cus)
+        SQ_LAUNCH(colmax_strip_kernel<4>, dim3((unsigned)((K + 31) / 32)), dim3(1024), 0, st, X, M, K, out_bits);
+    else if (K / 16 >= cus)
+        SQ_LAUNCH(colmax_strip_kernel<2>, dim3((unsigned)(K / 16)), dim3(1024), 0, st, X, M, K, out_bits);
+    else
+        SQ_LAUNCH(colmax_strip_kernel<1>, dim3((unsigned)(K / 8)), dim3(1024), 0, st, X, M, K, out_bits);
+    return hipSuccess;
+}
+
 // ---------------------------------------------------------------------------
 // Smoothing factors: s_j = max(a_j,1e-8)^alpha / max(w_j,1e-8)^(1-alpha) in fp64.
 // ---------------------------------------------------------------------------

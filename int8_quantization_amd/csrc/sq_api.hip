@@ -202,8 +202,7 @@ sq_status int8_outlier_matmul(const void* X, const void* W16, const int8_t* Wq, 
     int8_t* xq = reinterpret_cast<int8_t*>(base + L.xq);
     _Float16* xo = reinterpret_cast<_Float16*>(base + L.xo);
 
-    SQ_TRY(launch_fill_u32(cmax, K, 0u, stream));
-    SQ_TRY(launch_colmax(X, SQ_F16, M, K, cmax, stream));
+    SQ_TRY(launch_colmax_fresh(static_cast<const _Float16*>(X), M, K, cmax, stream));
     if (quant_stream_applies(M, K, false, true)) {
         // the compaction and the activation gather inside the streaming quantizer
         const OutlierSplit os{cmax, threshold, idx, count, n_outliers, outlier_idx, xo};

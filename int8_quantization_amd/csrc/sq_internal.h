@@ -179,6 +179,10 @@ hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const fl
 hipError_t launch_colmax(const void* X, int dt, int64_t M, int64_t K, uint32_t* amax_bits,
                          hipStream_t st);
 
+// Column absolute maxima of an fp16 matrix, written as float bits (any previous
+// contents of out_bits are overwritten; nothing needs zeroing first).
+hipError_t launch_colmax_fresh(const _Float16* X, int64_t M, int64_t K, uint32_t* out_bits, hipStream_t st);
+
 // s_j from act_max and the W column maxima held in s (overwritten in place).
 hipError_t launch_smooth_pow(const float* act_max, float* s_wmax, int64_t K, float alpha,
                              hipStream_t st);

@@ -348,7 +348,14 @@ def gpu_outlier(sq, X, W16, Wq, ws, bias, thr):
                            wsp, cnt.t, idx.t, acc.t)
     torch.cuda.synchronize()
     c = int(cnt.np()[0])
-    return c, idx.np()[:c], acc.np(), Y.np()
+    # the column absolute maxima, as float bits, are the workspace's first 4K bytes (the
+    # library's workspace layout; no output exposes them, so they are checked from there)
+    cmax = wsp[:4 * K].view(torch.int32).cpu().numpy().view(np.uint32)
+    return c, idx.np()[:c], acc.np(), Y.np(), cmax
+
+
+def check_colmax(cmax, X, orc):
+    assert_bits_equal(cmax, orc.col_absmax(X).view(np.uint32), "column maxima")
 
 
 @pytest.mark.parametrize("M,N,K,n_out,thr", [
@@ -364,7 +371,8 @@ def test_outlier_matmul(sq, orc, M, N, K, n_out, thr):
         X = np.where(X == 0, np.float16(0.5), X)
     bias = np.random.default_rng(1).standard_normal(N).astype(np.float32)
     Wq, ws = orc.quantize_weight(W16, None, 0)
-    c, idx, acc, Y = gpu_outlier(sq, X, W16, Wq, ws, bias, thr)
+    c, idx, acc, Y, cmax = gpu_outlier(sq, X, W16, Wq, ws, bias, thr)
+    check_colmax(cmax, X, orc)
     mask, ref_idx, Xq, xs, ref_acc, ref_Y = orc.llm_int8_linear(X, W16, Wq, ws, thr, bias)
     assert c == ref_idx.size
     assert_bits_equal(idx, ref_idx, "outlier idx")
@@ -376,15 +384,16 @@ def test_outlier_matmul(sq, orc, M, N, K, n_out, thr):
 def test_outlier_matmul_large_tiles(sq, orc, M, N, K):
     """LLM.int8() on the large-tile paths, every accumulator and output compared:
     256 x 256 tiles with the fp16 side product in their epilogue (3000 x 5000); the
-    two-launch column split, whose second launch reads the gathered outlier weight
-    rows from the split column on (4096 x 10240: 256 x 256 then 128 x 128 tiles;
-    2085 x 8192: 256 x 192 then 128 x 128)."""
+    two-launch column split, whose second launch reads the fp16 weight rows from the
+    split column on (4096 x 10240: 256 x 256 then 128 x 128 tiles; 2085 x 8192:
+    256 x 192 then 128 x 128)."""
     X, W16, _ = workloads.random_layer(17 + M, M, K, N, np.float16, n_outliers=5, factor=20.0)
     Wq, ws = gpu_quantize_weight(sq, W16, None, 0)
     Wq_r, ws_r = orc.quantize_weight(W16, None, 0)
     assert_bits_equal(Wq, Wq_r, "Wq")
     assert_bits_equal(ws, ws_r, "w_scale")
-    c, idx, acc, Y = gpu_outlier(sq, X, W16, Wq, ws, None, 6.0)
+    c, idx, acc, Y, cmax = gpu_outlier(sq, X, W16, Wq, ws, None, 6.0)
+    check_colmax(cmax, X, orc)
     mask, ref_idx, Xq_r, xs_r, acc_r, Y_r = orc.llm_int8_linear(X, W16, Wq_r, ws_r, 6.0)
     assert c == ref_idx.size and c >= 5
     assert_bits_equal(idx, ref_idx, "outlier idx")
@@ -475,7 +484,8 @@ def test_full_llm_int8(sq, orc):
     Wq_r, ws_r = orc.quantize_weight(W16, None, 0)
     assert_bits_equal(Wq, Wq_r, "Wq")
     assert_bits_equal(ws, ws_r, "w_scale")
-    c, idx, acc, Y = gpu_outlier(sq, X, W16, Wq, ws, None, wl.threshold)
+    c, idx, acc, Y, cmax = gpu_outlier(sq, X, W16, Wq, ws, None, wl.threshold)
+    check_colmax(cmax, X, orc)
     mask, ref_idx, Xq_r, xs_r, acc_r, Y_r = orc.llm_int8_linear(X, W16, Wq_r, ws_r, wl.threshold)
     assert c == ref_idx.size and set(wl.outlier_idx.tolist()) <= set(ref_idx.tolist())
     assert_bits_equal(idx, ref_idx, "outlier idx")
