@@ -58,6 +58,9 @@ def _load():
         "orc_abs_percentile": (F, [P, I, I64, I64, P, D]),
         "orc_static_scale": (F, [P, I, I64, I64, P, D]),
         "orc_quantize_static": (None, [P, I, I64, I64, P, F, P]),
+        "orc_quantize_per_token_asym": (None, [P, I, I64, I64, P, P, P, P]),
+        "orc_weight_rowsum": (None, [P, I64, I64, P]),
+        "orc_dequant_asym": (I64, [P, P, P, P, I, P, P, I64, I64, P, P]),
         "orc_kv_calibrate_per_head": (None, [P, I, I64, I64, I64, F, P]),
         "orc_kv_quantize_per_head": (None, [P, I, I64, I64, I64, P, P]),
         "orc_dequantize": (None, [P, I64, I64, P, I64, I64, P]),
@@ -286,6 +289,56 @@ def w8a8_linear(X, s, Wq, w_scale, gran=0, bias=None, out_dtype=np.float16, rows
     acc = gemm_i8(Xq, Wq)
     y = dequant(acc, xs, w_scale, gran, bias)
     return Xq, xs, acc, _store(y, out_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Asymmetric (zero-point) per-token activations ("量化基础与INT8", 非对称量化):
+# x' ~ scale * (q - zq), the GEMM corrected by zq * rowsum(Wq).
+# ---------------------------------------------------------------------------
+def quantize_per_token_asym(X, s=None):
+    """Returns (Xq int8 [M,K], x_scale [M] float32, x_zero [M] int32)."""
+    X, dt = _fp(X)
+    M, K = X.shape
+    s = None if s is None else _as(s, np.float32)
+    Xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    xz = np.empty(M, np.int32)
+    _load().orc_quantize_per_token_asym(_ptr(X), dt, M, K, _ptr(s), _ptr(Xq), _ptr(xs), _ptr(xz))
+    return Xq, xs, xz
+
+
+def weight_rowsum(Wq):
+    Wq = _as(Wq, np.int8)
+    N, K = Wq.shape
+    rs = np.empty(N, np.int32)
+    _load().orc_weight_rowsum(_ptr(Wq), N, K, _ptr(rs))
+    return rs
+
+
+def dequant_asym(acc, x_scale, x_zero, w_scale, rowsum, gran=0, bias=None):
+    """Returns (y float32 [M,N], corrected accumulators int32 [M,N])."""
+    acc = _as(acc, np.int32)
+    M, N = acc.shape
+    xs, xz = _as(x_scale, np.float32), _as(x_zero, np.int32)
+    ws, rs = _as(w_scale, np.float32), _as(rowsum, np.int32)
+    bias = None if bias is None else _as(bias, np.float32)
+    y = np.empty((M, N), np.float32)
+    acc2 = np.empty((M, N), np.int32)
+    bad = _load().orc_dequant_asym(_ptr(acc), _ptr(xs), _ptr(xz), _ptr(ws), int(gran), _ptr(rs), _ptr(bias), M, N,
+                                   _ptr(y), _ptr(acc2))
+    if bad:
+        raise OverflowError(f"{bad} corrected accumulators exceed int32")
+    return y, acc2
+
+
+def w8a8_asym_linear(X, s, Wq, w_scale, gran=0, bias=None, out_dtype=np.float16):
+    """Zero-point activations: (Xq, xs, xz, rowsum, corrected acc, Y) in the pages' order:
+    quantize, int8 GEMM, correction, dequantize."""
+    Xq, xs, xz = quantize_per_token_asym(X, s)
+    rs = weight_rowsum(Wq)
+    acc = gemm_i8(Xq, Wq)
+    y, acc2 = dequant_asym(acc, xs, xz, w_scale, rs, gran, bias)
+    return Xq, xs, xz, rs, acc2, _store(y, out_dtype)
 
 
 def llm_int8_linear(X16, W16, Wq, w_scale, threshold, bias=None, rows=None):

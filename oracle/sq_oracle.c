@@ -289,6 +289,87 @@ void orc_quantize_per_token(const void* X, int dt, int64_t M, int64_t K, const f
 }
 
 /* ------------------------------------------------------------------ */
+/* Asymmetric (zero-point) per-token activation quantization (basics    */
+/* notes, 非对称量化: scale = (max - min) / 255, a zero point, codes     */
+/* round(x / scale) shifted by it, x ~ scale * (code - zero point)).     */
+/*                                                                      */
+/* Reading (the page's own formulas mix float and code units): the row  */
+/* range is widened to contain 0, lo = min(0, min x'), hi = max(0, max  */
+/* x'), so the zero point is a code; scale = fl32(fl32(hi - lo) / 255);  */
+/* z = clamp(rne(fl32(-lo / scale)), 0, 255); code u = clamp(rne(fl32(  */
+/* x' / scale)) + z, 0, 255).  Stored as int8 q = u - 128 with zero     */
+/* point zq = z - 128, so x' ~ scale * (q - zq).  An all-zero row (scale */
+/* 0) gets u = z = 0.  x' = fl32(x / s_j) with smoothing, as above.     */
+/* ------------------------------------------------------------------ */
+void orc_quantize_per_token_asym(const void* X, int dt, int64_t M, int64_t K, const float* s, int8_t* Xq,
+                                 float* x_scale, int32_t* x_zero)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            float x = load_elem(X, dt, m * K + j);
+            if (s) x = x / s[j];
+            if (x < lo) lo = x;
+            if (x > hi) hi = x;
+        }
+        float sc = (hi - lo) / 255.0f;
+        int z = 0;
+        if (sc != 0.0f) {
+            float zf = rintf(-lo / sc);
+            z = zf < 0.0f ? 0 : (zf > 255.0f ? 255 : (int)zf);
+        }
+        x_scale[m] = sc;
+        x_zero[m] = z - 128;
+        for (int64_t j = 0; j < K; ++j) {
+            int u = 0;
+            if (sc != 0.0f) {
+                float x = load_elem(X, dt, m * K + j);
+                if (s) x = x / s[j];
+                u = (int)rintf(x / sc) + z;
+                u = u < 0 ? 0 : (u > 255 ? 255 : u);
+            }
+            Xq[m * K + j] = (int8_t)(u - 128);
+        }
+    }
+}
+
+/* rowsum[n] = sum_k Wq[n,k]: the weight term of the zero-point correction, once per weight. */
+void orc_weight_rowsum(const int8_t* Wq, int64_t N, int64_t K, int32_t* rowsum)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t t = 0;
+        for (int64_t k = 0; k < K; ++k) t += Wq[n * K + k];
+        rowsum[n] = (int32_t)t;
+    }
+}
+
+/* The corrected accumulator acc'[m,n] = acc[m,n] - zq[m] * rowsum[n] (the sum of
+ * (q - zq) * w over k), in int64 and checked to fit int32 (returns the number that do
+ * not), then dequantized like the symmetric accumulator:
+ * y = ((float)acc' * x_scale[m]) * w_scale[n or 0] (+ bias[n]).  acc_corr may be NULL. */
+int64_t orc_dequant_asym(const int32_t* acc, const float* x_scale, const int32_t* x_zero, const float* w_scale,
+                         int wgran, const int32_t* rowsum, const float* bias, int64_t M, int64_t N, float* y,
+                         int32_t* acc_corr)
+{
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t a = (int64_t)acc[m * N + n] - (int64_t)x_zero[m] * (int64_t)rowsum[n];
+            if (a > INT32_MAX || a < INT32_MIN) ++bad;
+            if (acc_corr) acc_corr[m * N + n] = (int32_t)a;
+            float v = (float)(int32_t)a;
+            v = v * x_scale[m];
+            v = v * w_scale[wgran == 0 ? n : 0];
+            if (bias) v = v + bias[n];
+            y[m * N + n] = v;
+        }
+    return bad;
+}
+
+/* ------------------------------------------------------------------ */
 /* int8 x int8 -> int32 GEMM, "NT": acc[m,n] = sum_k A[m,k] * B[n,k],  */
 /* accumulated in int64 and checked to fit int32 (basics notes          */
 /* "INT8推理流程").  Returns the number of results that did not fit.      */

@@ -56,6 +56,12 @@ MUTATIONS = [
     ("fp8_exponent_bias", "(((E + 7) << 3) | (int)r)", "(((E + 8) << 3) | (int)r)"),
     ("fp8_row_scale_127", "float sc = a / 448.0f;\n        scale[m] = sc;", "float sc = a / 127.0f;\n        scale[m] = sc;"),
     ("fp8_subnormal_units", "int64_t n = E == 0 ? m :", "int64_t n = E == 0 ? 8 + m :"),
+    ("asym_scale_over_256", "float sc = (hi - lo) / 255.0f;", "float sc = (hi - lo) / 256.0f;"),
+    ("asym_range_without_zero", "float lo = 0.0f, hi = 0.0f;", "float lo = 1e30f, hi = -1e30f;"),
+    ("asym_zero_point_sign", "float zf = rintf(-lo / sc);", "float zf = rintf(lo / sc);"),
+    ("asym_shift_before_rounding", "u = (int)rintf(x / sc) + z;", "u = (int)rintf(x / sc + (float)z);"),
+    ("asym_correction_sign", "(int64_t)acc[m * N + n] - (int64_t)x_zero[m]", "(int64_t)acc[m * N + n] + (int64_t)x_zero[m]"),
+    ("rowsum_dropped_row", "for (int64_t k = 0; k < K; ++k) t += Wq[n * K + k];", "for (int64_t k = 1; k < K; ++k) t += Wq[n * K + k];"),
 ]
 
 

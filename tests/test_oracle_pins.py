@@ -892,3 +892,124 @@ def test_oracle_runs_nearest_even_under_another_mode(orc):
     assert np.array_equal(xs_got.view(np.uint32), xs_ref.view(np.uint32))
     assert np.array_equal(Xq_got, Xq_ref)
     assert mode_after == FE_UPWARD
+
+
+# --------------------------------------------------------------------------
+# Asymmetric (zero-point) per-token activations ("量化基础与INT8", 非对称量化)
+# --------------------------------------------------------------------------
+
+def test_asym_closed_form_rows(orc):
+    """Rows whose scale is a power of two, so every quotient is exact:
+    - the ramp 0, 1/8, ..., 255/8: scale 1/8, zero point code 0, codes = the ramp index;
+    - its negative: zero point code 255, codes again the index;
+    - range [-127c, 128c]: scale c, zero point rne(127) = 127 (odd), and the values
+      0.5c, 1.5c round to even before the shift (codes 127, 129; rounding after the
+      shift would give 128 and 128);
+    - range [-127.5c, 127.5c]: zero point rne(127.5) = 128 (ties to even), -1.5c and 1.5c
+      give 126 and 130, 127.5c rounds to 128 and clamps at code 255."""
+    ramp = (np.arange(256, dtype=np.float32) / 8).reshape(1, 256)
+    for row, zq in ((ramp, -128), (-ramp[:, ::-1], 127)):
+        q, xs, xz = orc.quantize_per_token_asym(row)
+        assert xs[0] == np.float32(0.125) and xz[0] == zq
+        assert np.array_equal(q[0].astype(np.int64), np.arange(256) - 128)
+    c = np.float32(0.25)
+    row = (np.array([-127.0, 0.5, 1.5, 128.0], np.float32) * c).reshape(1, 4)
+    q, xs, xz = orc.quantize_per_token_asym(row)
+    assert xs[0] == c and xz[0] == 127 - 128
+    assert q[0].tolist() == [0 - 128, 127 - 128, 129 - 128, 255 - 128]
+    row = (np.array([-127.5, -1.5, 0.0, 1.5, 127.5], np.float32) * c).reshape(1, 5)
+    q, xs, xz = orc.quantize_per_token_asym(row)
+    assert xs[0] == c and xz[0] == 0
+    assert q[0].tolist() == [0 - 128, 126 - 128, 128 - 128, 130 - 128, 255 - 128]
+
+
+def test_asym_zero_and_one_sided_rows(orc):
+    """The range always contains 0: an all-positive row has zero point code 0, an
+    all-negative row 255; an all-zero row has scale 0, zero point 0 and all codes 0."""
+    X = np.array([[0.0, 0.0, 0.0, 0.0], [1.0, 2.0, 3.0, 4.0], [-4.0, -3.0, -2.0, -1.0]], np.float32)
+    q, xs, xz = orc.quantize_per_token_asym(X)
+    assert xs[0] == 0 and xz[0] == -128 and np.all(q[0] == -128)
+    assert xz[1] == -128 and xz[2] == 127
+    assert xs[1] == np.float32(np.float32(4.0) / np.float32(255.0)) == xs[2]
+    assert q[1, 3] == 127 and q[2, 0] == -128       # the extremes reach the ends of the code range
+
+
+def test_asym_codes_are_nearest_levels(orc):
+    """Brute force on small random rows: each code u = q + 128 is the integer nearest to
+    v + z over [0, 255], with v = fl32(x / scale) and ties broken by rounding v to even
+    before the shift; the zero point is the nearest integer to -lo / scale."""
+    rng = np.random.default_rng(31)
+    X = (rng.standard_normal((40, 24)) * rng.uniform(0.01, 30, (40, 1)) + rng.uniform(-5, 5, (40, 1))).astype(np.float32)
+    X[3] = np.abs(X[3])
+    X[5] = -np.abs(X[5])
+    q, xs, xz = orc.quantize_per_token_asym(X)
+    for m in range(X.shape[0]):
+        lo, hi = min(0.0, float(X[m].min())), max(0.0, float(X[m].max()))
+        sc = xs[m]
+        assert abs(float(sc) * 255 - (hi - lo)) <= 2e-6 * (hi - lo)
+        z = int(xz[m]) + 128
+        zz = -lo / float(sc)
+        assert abs(z - zz) <= 0.5 + 1e-6 and 0 <= z <= 255
+        for k in range(X.shape[1]):
+            v = float(np.float32(X[m, k]) / np.float32(sc))
+            cands = [u for u in range(256) if abs(v + z - u) == min(abs(v + z - w) for w in range(256))]
+            if len(cands) == 2:
+                cands = [u for u in cands if (u - z) % 2 == 0]
+            assert int(q[m, k]) + 128 == cands[0], (m, k)
+
+
+def test_asym_round_trip_bound_and_invariance(orc):
+    """|x - scale (q - zq)| <= scale / 2 inside the range (scale at its two ends, where the
+    shifted code can be clamped); scaling a row by a power of two scales its scale and
+    keeps its codes and zero point; a power-of-two smoothing vector equals dividing first."""
+    rng = np.random.default_rng(32)
+    X = (rng.standard_normal((64, 300)) * 3 + rng.uniform(-4, 4, (64, 1))).astype(np.float32)
+    q, xs, xz = orc.quantize_per_token_asym(X)
+    xhat = xs[:, None].astype(np.float64) * (q.astype(np.float64) - xz[:, None])
+    err = np.abs(X - xhat)
+    lo = np.minimum(X.min(1), 0)[:, None]
+    hi = np.maximum(X.max(1), 0)[:, None]
+    inner = (X > lo + xs[:, None]) & (X < hi - xs[:, None])
+    assert np.all(err <= xs[:, None] * (1 + 1e-6))
+    assert np.all(err[inner] <= (xs[:, None] * np.ones_like(X))[inner] * (0.5 + 1e-6))
+    q2, xs2, xz2 = orc.quantize_per_token_asym(X * np.float32(8.0))
+    assert np.array_equal(q2, q) and np.array_equal(xz2, xz) and np.array_equal(xs2, xs * np.float32(8.0))
+    s = np.exp2(rng.integers(-3, 4, 300)).astype(np.float32)
+    q3, xs3, xz3 = orc.quantize_per_token_asym(X, s)
+    q4, xs4, xz4 = orc.quantize_per_token_asym(X / s)
+    assert np.array_equal(q3, q4) and np.array_equal(xs3, xs4) and np.array_equal(xz3, xz4)
+
+
+def test_asym_corrected_accumulator_is_dezeroed_integer_product(orc):
+    """The corrected accumulator equals sum_k (q - zq) * w, computed here the other way
+    round (zero point removed from every code first, then an int64 product), and the
+    row sums are numpy's."""
+    rng = np.random.default_rng(33)
+    X = (rng.standard_normal((37, 200)) + 1.5).astype(np.float32)
+    W = (rng.standard_normal((29, 200)) * 0.05).astype(np.float32)
+    Wq, ws = orc.quantize_weight(W, None, 0)
+    rs = orc.weight_rowsum(Wq)
+    assert np.array_equal(rs, Wq.astype(np.int64).sum(1))
+    q, xs, xz = orc.quantize_per_token_asym(X)
+    acc = orc.gemm_i8(q, Wq)
+    y, acc2 = orc.dequant_asym(acc, xs, xz, ws, rs, 0, None)
+    ref = (q.astype(np.int64) - xz[:, None]) @ Wq.astype(np.int64).T
+    assert np.array_equal(acc2.astype(np.int64), ref)
+    # with power-of-two scales the dequantization is exact
+    y2, _ = orc.dequant_asym(acc, np.full(37, 0.5, np.float32), xz, np.full(29, 0.25, np.float32), rs, 0, None)
+    assert np.array_equal(y2.astype(np.float64), ref * 0.125)
+
+
+def test_asym_linear_error_bound(orc):
+    """The zero-point layer against fp64 X W^T: per element within the sum of the two
+    quantization errors (activation at most one scale step, weight half a step) plus
+    fp32 rounding."""
+    rng = np.random.default_rng(34)
+    X = (rng.standard_normal((48, 256)) + 0.7).astype(np.float32)
+    W = (rng.standard_normal((40, 256)) * 0.05).astype(np.float32)
+    Wq, ws = orc.quantize_weight(W, None, 0)
+    Xq, xs, xz, rs, acc2, Y = orc.w8a8_asym_linear(X, None, Wq, ws, 0, None, np.float32)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    what = Wq.astype(np.float64) * ws[:, None]
+    bound = xs[:, None] * np.abs(what).sum(1)[None, :] + np.abs(X).astype(np.float64) @ (ws[:, None] / 2 * np.ones_like(W)).T
+    assert np.all(np.abs(Y - exact) <= bound * 1.001 + 1e-5 * np.abs(exact) + 1e-6)
