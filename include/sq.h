@@ -283,6 +283,39 @@ sq_status sq_calibrate_static_scale(const void* X_cal, int xdt, int64_t M_cal, i
 sq_status sq_quantize_static(const void* X, int xdt, int64_t M, int64_t K, const float* s,
                              const float* x_scale, int8_t* Xq, float* x_scale_rows, hipStream_t stream);
 
+/* Zero-point (asymmetric) activation variant.
+ * [basics notes, 非对称量化: scale from the range, (max - min) / 255, and a zero point, so
+ *  that a range that is not centred on 0 uses all 256 codes; the dequantized value is
+ *  scale * (code - zero point).  The page's own formulas mix float and code units; the
+ *  reading taken: the row range is widened to contain 0, so the zero point is a code.]
+ * Per-token activation codes:
+ *   X, s, M, K as for sq_quantize_per_token (x' = fl32(x / s_j) with s, else x).
+ *   x_scale  device float [M], out: sc = fl32(fl32(hi - lo) / 255) with lo = min(0, min_j x'_j),
+ *            hi = max(0, max_j x'_j) (0 for an all-zero row).
+ *   x_zero   device int32 [M], out: z - 128 with z = clamp(rne(fl32(-lo / sc)), 0, 255) (z = 0 when sc == 0).
+ *   Xq       device int8 [M x K], out: u - 128 with u = clamp(rne(fl32(x'_j / sc)) + z, 0, 255)
+ *            (u = 0 when sc == 0), so x'_j ~ sc * (Xq - x_zero).
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status sq_quantize_per_token_asym(const void* X, int xdt, int64_t M, int64_t K, const float* s,
+                                     int8_t* Xq, float* x_scale, int32_t* x_zero, hipStream_t stream);
+
+/* Row sums of the quantized weight, rowsum[n] = sum_k Wq[n,k] (offline, once per weight):
+ * the weight term of the zero-point correction.
+ *   Wq      device int8 [N x K];  rowsum  device int32 [N], out.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_HIP. */
+sq_status sq_weight_rowsum(const int8_t* Wq, int64_t N, int64_t K, int32_t* rowsum, hipStream_t stream);
+
+/* int8 GEMM with zero-point activations and the dequantizing epilogue (any M):
+ *   acc'[m,n] = sum_k Xq[m,k] Wq[n,k] - x_zero[m] * w_rowsum[n]  (= sum_k (Xq - x_zero) Wq),
+ *   exact int32 when it fits int32;  y = ((float)acc' * x_scale[m]) * w_scale[n or 0] (+ bias[n]),
+ *   fp32 steps, stored as ydt.  x_zero and w_rowsum come from sq_quantize_per_token_asym and
+ *   sq_weight_rowsum; other arguments as for w8a8_gemm_dequant; acc_out (device int32
+ *   [M x N] or NULL) receives acc'.
+ * Errors: SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALIGN, SQ_ERR_DTYPE, SQ_ERR_HIP. */
+sq_status w8a8_asym_gemm_dequant(const int8_t* Xq, const float* x_scale, const int32_t* x_zero, const int8_t* Wq,
+                                 const float* w_scale, int g, const int32_t* w_rowsum, const float* bias, int64_t M,
+                                 int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out, hipStream_t stream);
+
 /* FP8 W8A8 variant: FP8 E4M3 codes (OCP "e4m3fn": bias 7, 3 mantissa bits, largest
  * finite 448, smallest subnormal 2^-9, no infinities; byte = sign | exponent | mantissa).
  * [SmoothQuant page, section 6.1: W8A8 in FP8 is the scheme to prefer on hardware

@@ -51,6 +51,9 @@ def _load():
         "sq_quantize_per_token_fp8": (I, [P, I, I64, I64, P, P, P, P]),
         "sq_quantize_weight_fp8": (I, [P, I, I64, I64, P, I, P, P, P, SZ, P]),
         "fp8_gemm_dequant": (I, [P, P, P, P, I, P, I64, I64, I64, P, I, P, P]),
+        "sq_quantize_per_token_asym": (I, [P, I, I64, I64, P, P, P, P, P]),
+        "sq_weight_rowsum": (I, [P, I64, I64, P, P]),
+        "w8a8_asym_gemm_dequant": (I, [P, P, P, P, P, I, P, P, I64, I64, I64, P, I, P, P]),
         "sq_kv_calibrate_per_head": (I, [P, I, I64, I64, I64, F, P, P]),
         "sq_kv_quantize_per_head": (I, [P, I, I64, I64, I64, P, P, P]),
         "sq_dequantize": (I, [P, I64, I64, P, I64, I64, P, I, P]),
@@ -68,7 +71,8 @@ EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quan
            "sq_quantize_weight", "w8a8_gemm_dequant", "int8_outlier_matmul", "sq_fold_smoothing_layernorm",
            "sq_layernorm_quantize_per_token", "sq_calibrate_static_scale", "sq_quantize_static",
            "sq_kv_calibrate_per_head", "sq_kv_quantize_per_head", "sq_dequantize", "sq_quantize_per_token_fp8",
-           "sq_quantize_weight_fp8", "fp8_gemm_dequant", "sq_w8a8_linear", "sq_w8a8_linear_noalloc")
+           "sq_quantize_weight_fp8", "fp8_gemm_dequant", "sq_w8a8_linear", "sq_w8a8_linear_noalloc",
+           "sq_quantize_per_token_asym", "sq_weight_rowsum", "w8a8_asym_gemm_dequant")
 
 
 def _p(t):
@@ -356,6 +360,37 @@ def fp8_gemm_dequant(Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out=None):
     _check(fn, _lib.fp8_gemm_dequant(
         _p(Xq), _p(x_scale), _p(Wq), _p(w_scale), int(gran), _p(bias), M, N, K, _p(Y), _dt(Y),
         _p(acc_out), _stream()))
+
+
+def sq_quantize_per_token_asym(X, s, Xq, x_scale, x_zero):
+    """Zero-point per-token codes: Xq int8 [M, K], x_scale fp32 [M], x_zero int32 [M] out."""
+    fn = "sq_quantize_per_token_asym"
+    M, K = _rows_in(fn, X, s)
+    _need(fn, "Xq", Xq, (I8,), shape=(M, K))
+    _need(fn, "x_scale", x_scale, (F32,), numel=M)
+    _need(fn, "x_zero", x_zero, (I32,), numel=M)
+    _check(fn, _lib.sq_quantize_per_token_asym(
+        _p(X), _dt(X), M, K, _p(s), _p(Xq), _p(x_scale), _p(x_zero), _stream()))
+
+
+def sq_weight_rowsum(Wq, rowsum):
+    """rowsum int32 [N] out: the sum of each row of Wq int8 [N, K]."""
+    fn = "sq_weight_rowsum"
+    _need(fn, "Wq", Wq, (I8,), ndim=2)
+    N, K = Wq.shape
+    _need(fn, "rowsum", rowsum, (I32,), numel=N)
+    _check(fn, _lib.sq_weight_rowsum(_p(Wq), N, K, _p(rowsum), _stream()))
+
+
+def w8a8_asym_gemm_dequant(Xq, x_scale, x_zero, Wq, w_scale, gran, w_rowsum, bias, Y, acc_out=None):
+    """The int8 GEMM with zero-point activations; acc_out int32 [M, N] receives the corrected accumulators."""
+    fn = "w8a8_asym_gemm_dequant"
+    M, N, K = _gemm_args(fn, Xq, x_scale, Wq, w_scale, gran, bias, Y, acc_out, I8, I32)
+    _need(fn, "x_zero", x_zero, (I32,), numel=M)
+    _need(fn, "w_rowsum", w_rowsum, (I32,), numel=N)
+    _check(fn, _lib.w8a8_asym_gemm_dequant(
+        _p(Xq), _p(x_scale), _p(x_zero), _p(Wq), _p(w_scale), int(gran), _p(w_rowsum), _p(bias), M, N, K, _p(Y),
+        _dt(Y), _p(acc_out), _stream()))
 
 
 def sq_w8a8_linear(X, s, Wq, w_scale, gran, bias, Y, ws, x_scale=None):

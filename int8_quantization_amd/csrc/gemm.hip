@@ -93,20 +93,20 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8>
+template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8, bool ASYM>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
     void* __restrict__ Yv, int32_t* __restrict__ acc_out, const _Float16* __restrict__ Xo,
     const _Float16* __restrict__ W16, const int32_t* __restrict__ sidx, const int32_t* __restrict__ cnt, int64_t ldo,
-    int64_t ldy, int tiles_m,
-    int tiles_n) {
+    int64_t ldy, int tiles_m, int tiles_n, const int32_t* __restrict__ xz, const int32_t* __restrict__ wrs) {
     constexpr int BK = 128;                  // bytes of K per stage: one cache line per row
     constexpr int S = 2;                     // LDS stages
     constexpr int KS = BK / (FP8 ? 64 : 32); // MFMA k-steps per stage
     using Frag = typename std::conditional<FP8, v8i, v4i>::type;
     using Acc = typename std::conditional<FP8, v16f, v16i>::type;
     static_assert(!(FP8 && SIDE), "the LLM.int8() side product is int8 only");
+    static_assert(!ASYM || (!FP8 && !SIDE), "zero-point activations: plain int8 products only");
     constexpr int NW = WM * WN;              // waves, in a WM x WN grid over the tile
     constexpr int NT = 64 * NW;              // threads
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -305,17 +305,27 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // everything; the prologue barrier publishes them.
     static_assert(BM <= NT && BN <= NT, "one row and one column scale per thread");
     float xs_v = 0.0f, ws_v = 0.0f, b_v = -0.0f;   // x + (-0.0) == x for every x: no bias
-    if (tid < BM) xs_v = xs[m0 + tid < M ? m0 + tid : M - 1];
+    int xz_v = 0, rs_v = 0;                         // zero-point activations: zero point, weight row sum
+    if (tid < BM) {
+        xs_v = xs[m0 + tid < M ? m0 + tid : M - 1];
+        if constexpr (ASYM) xz_v = xz[m0 + tid < M ? m0 + tid : M - 1];
+    }
     if (tid < BN) {
         const int n = n0 + tid < N ? n0 + tid : N - 1;
         ws_v = ws[(int64_t)n * ws_stride];
         if (bias != nullptr) b_v = bias[n];
+        if constexpr (ASYM) rs_v = wrs[n];
     }
     __shared__ float sxs[BM], sws[BN], sbias[BN];
+    __shared__ int szq[ASYM ? BM : 1], srs[ASYM ? BN : 1];
     if (tid < BM) sxs[tid] = xs_v;
     if (tid < BN) {
         sws[tid] = ws_v;
         sbias[tid] = b_v;
+    }
+    if constexpr (ASYM) {
+        if (tid < BM) szq[tid] = xz_v;
+        if (tid < BN) srs[tid] = rs_v;
     }
     if constexpr (SIDE) {
         if (side_fast) {   // zero the values past the count and of rows past M, N
@@ -446,6 +456,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
                         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(iv[b]) : "a"(acc[i][j][4 * a + b]));
+                    if constexpr (ASYM) {   // the corrected accumulator: acc - zq * rowsum (int32, wraps like int64 when it fits)
+                        const int zq = szq[wm * WTM + i * 32 + lrow];
+                        const v4i r4 = *reinterpret_cast<const v4i*>(&srs[wn * WTN + j * 32 + 8 * a + 4 * lk]);
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) iv[b] -= zq * r4[b];
+                    }
                     if (m < M)
                         for (int b = 0; b < 4; ++b)
                             if (n + b < N) acc_out[(int64_t)m * ldy + n + b] = iv[b];
@@ -463,6 +479,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             const int lr = wm * (TMH * 32) + ii * 32 + lrow;      // LDS row
             const int mloc = wm * WTM + i * 32 + lrow;           // tile row
             const float xsv = xsr[i];
+            const int zq = ASYM ? szq[mloc] : 0;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -472,11 +489,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
                     const int nloc = wn * WTN + j * 32 + 8 * a + 4 * lk;
                     const v4f w4 = HOIST ? wsr[HOIST ? j : 0][a] : *reinterpret_cast<const v4f*>(&sws[nloc]);
                     const v4f b4 = *reinterpret_cast<const v4f*>(&sbias[nloc]);
+                    v4i r4{};
+                    if constexpr (ASYM) r4 = *reinterpret_cast<const v4i*>(&srs[nloc]);
                     int iv[4];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         // read the accumulator register directly, one value at a time
                         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(iv[b]) : "a"(acc[i][j][4 * a + b]));
+                        if constexpr (ASYM) iv[b] -= zq * r4[b];
                         float v = FP8 ? __builtin_bit_cast(float, iv[b]) : (float)iv[b];
                         v = v * xsv;
                         v = v * w4[b];
@@ -571,26 +591,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8>
+template <int BM, int BN, int WM, int WN, bool OUT_F16, bool SIDE, bool FP8, bool ASYM = false>
 hipError_t run(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int32_t* acc_out,
-               const SideArgs* side, hipStream_t st) {
+               const SideArgs* side, hipStream_t st, const AsymArgs* asym = nullptr) {
     const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
     const _Float16* Xo = side ? side->Xo : nullptr;
     const _Float16* W16 = side ? side->W16 : nullptr;
     const int32_t* sidx = side ? side->idx : nullptr;
     const int32_t* cnt = side ? side->count : nullptr;
     const int64_t ldo = side ? side->ldo : 0;
-    SQ_LAUNCH((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE, FP8>), dim3((unsigned)(tm * tn)),
+    const int32_t* xz = asym ? asym->xz : nullptr;
+    const int32_t* wrs = asym ? asym->wrs : nullptr;
+    SQ_LAUNCH((gemm_i8_kernel<BM, BN, WM, WN, OUT_F16, SIDE, FP8, ASYM>), dim3((unsigned)(tm * tn)),
                        dim3(64 * WM * WN), 0, st, Xq, xs, Wq, ws, ws_stride, bias, (int)M, (int)N, (int)K, Y, acc_out,
-                       Xo, W16, sidx, cnt, ldo, ldy, tm, tn);
+                       Xo, W16, sidx, cnt, ldo, ldy, tm, tn, xz, wrs);
     return hipSuccess;
 }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                     const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int ydt,
-                    int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st) {
+                    int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st, const AsymArgs* asym) {
+    if (asym) {   // zero-point activations: plain int8 products, fp16 or fp32 output
+        if (fp8 || side) return hipErrorInvalidValue;
+        if (ydt == SQ_F16)
+            return run<BM, BN, WM, WN, true, false, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy,
+                                                                 acc_out, nullptr, st, asym);
+        return run<BM, BN, WM, WN, false, false, false, true>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy,
+                                                              acc_out, nullptr, st, asym);
+    }
     if (fp8) {
         if constexpr (BN == 256) {
             return hipErrorInvalidValue;   // the FP8 fragments do not fit beside 256 x 256 accumulators
@@ -625,7 +655,8 @@ hipError_t dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const f
 // a second launch that picks its own tiles, if that is estimated faster.
 hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, int ydt,
-                       int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st, bool may_split) {
+                       int32_t* acc_out, const SideArgs* side, bool fp8, hipStream_t st, bool may_split,
+                       const AsymArgs* asym = nullptr) {
     const int64_t cus = dev_info().cus;
     struct Cand { int bm, bn, per_cu; double rate; };
     // (FP8 starts at the second candidate: its fragments do not fit beside 256 x 256 accumulators)
@@ -654,8 +685,10 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
         for (int c = fp8 ? 1 : 0; c < 3; ++c) tail_cost = std::min(tail_cost, cost_of(cands[c], N - n_main));
         if (full * b.per_cu * b.bm * b.bn / b.rate + tail_cost < 0.95 * best_cost) {
             const hipError_t e = launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, n_main, K, Y, ldy, ydt, acc_out,
-                                             side, fp8, st, false);
+                                             side, fp8, st, false, asym);
             if (e != hipSuccess) return e;
+            AsymArgs asym2{};
+            if (asym) asym2 = AsymArgs{asym->xz, asym->wrs + n_main};   // row sums of the remaining columns
             SideArgs side2{};
             if (side) {
                 side2 = *side;
@@ -664,16 +697,18 @@ hipError_t launch_cols(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
             return launch_cols(Xq, xs, Wq + n_main * K, ws + n_main * ws_stride, ws_stride,
                                bias ? bias + n_main : nullptr, M, N - n_main, K,
                                static_cast<char*>(Y) + n_main * (ydt == SQ_F16 ? 2 : 4), ldy, ydt,
-                               acc_out ? acc_out + n_main : nullptr, side ? &side2 : nullptr, fp8, st, false);
+                               acc_out ? acc_out + n_main : nullptr, side ? &side2 : nullptr, fp8, st, false,
+                               asym ? &asym2 : nullptr);
         }
     }
     if (best == 0)
         return dispatch<256, 256, SQ_W256_WM, SQ_W256_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt,
-                                                          acc_out, side, fp8, st);
+                                                          acc_out, side, fp8, st, asym);
     if (best == 1)
         return dispatch<256, 192, SQ_W192_WM, SQ_W192_WN>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt,
-                                                          acc_out, side, fp8, st);
-    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt, acc_out, side, fp8, st);
+                                                          acc_out, side, fp8, st, asym);
+    return dispatch<128, 128, 2, 2>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ldy, ydt, acc_out, side, fp8, st,
+                                    asym);
 }
 
 }  // namespace
@@ -682,6 +717,13 @@ hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
                        const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out,
                        const SideArgs* side, hipStream_t st) {
     return launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, N, ydt, acc_out, side, false, st, true);
+}
+
+hipError_t launch_gemm_asym(const int8_t* Xq, const float* xs, const int32_t* xz, const int8_t* Wq, const float* ws,
+                            int ws_stride, const int32_t* wrs, const float* bias, int64_t M, int64_t N, int64_t K,
+                            void* Y, int ydt, int32_t* acc_out, hipStream_t st) {
+    const AsymArgs asym{xz, wrs};
+    return launch_cols(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, N, ydt, acc_out, nullptr, false, st, true, &asym);
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq, const float* ws, int ws_stride,

@@ -93,7 +93,7 @@ template <int RPI, int TG, int RG, int PER, bool HOIST, bool OUT_F16, bool FP8, 
 __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int ws_stride, const float* __restrict__ bias, int M, int N, int K,
-    void* __restrict__ Yv, int32_t* __restrict__ acc_out, FusedIn fin) {
+    void* __restrict__ Yv, int32_t* __restrict__ acc_out, FusedIn fin, AsymArgs asy) {
     static_assert(!FUSED || (HOIST && TG == 1 && RPI == 4 && !FP8), "fused decode: M <= 2, register-resident X");
     constexpr int SPAN = 1024 / RPI;      // bytes of one row per load instruction
     constexpr int TROWS = RG * RPI;       // weight rows per tile
@@ -128,6 +128,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
         v4i w[RG][PER];
         v4i x[PER][TG];
         float wsv, bv;
+        int rsv;
     };
     extern __shared__ __attribute__((aligned(16))) int8_t sxq[];   // FUSED: the block's copy of Xq [M x K]
     auto load_x = [&](int ch, v4i (&x)[PER][TG]) {
@@ -240,6 +241,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const bool eact = (int)threadIdx.x < M * TROWS;
     const int em = eact ? (int)threadIdx.x / TROWS : 0, ej = (int)threadIdx.x % TROWS;
     float xsv = FUSED ? 0.0f : xs[em];   // FUSED: set after the prologue
+    // zero-point activations: acc - zq[m] * rowsum[n] (0 * 0 otherwise)
+    const int xzv = (!FP8 && asy.xz != nullptr) ? asy.xz[em] : 0;
     const float* bsrc = bias != nullptr ? bias : ws;
     auto load_unit = [&](int unit, Buf& b) {
         const int tile = blockIdx.x + (unit / nch) * gridDim.x;
@@ -260,6 +263,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
         const int n = min(tile * TROWS + ej, N - 1);
         b.wsv = ws[(int64_t)n * ws_stride];
         b.bv = bsrc[bias != nullptr ? n : 0];
+        b.rsv = (!FP8 && asy.wrs != nullptr) ? asy.wrs[n] : 0;
     };
 
     using AccV = typename std::conditional<FP8, v4f, v4i>::type;
@@ -319,6 +323,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
             for (int w8 = 0; w8 < kWaves; ++w8)
 #pragma unroll
                 for (int bk = 0; bk < NB; ++bk) sum += pb[w8 * (RG * TG * 256) + (bk * RPI + jj) * 16 + bk * RPI + mm];
+            if constexpr (!FP8) sum -= xzv * b.rsv;
             float y = (float)sum;
             y = y * xsv;
             y = y * b.wsv;
@@ -359,14 +364,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
 template <int RPI, int TG, int RG, int PER, bool HOIST, bool FP8, int FUSED = 0>
 hipError_t launch_cfg(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                       const float* bias, int M, int N, int K, void* Y, int ydt, int32_t* acc_out, int grid,
-                      hipStream_t st, FusedIn fin = FusedIn{nullptr, nullptr, nullptr}) {
+                      hipStream_t st, FusedIn fin = FusedIn{nullptr, nullptr, nullptr}, AsymArgs asy = AsymArgs{}) {
     const size_t dyn = FUSED ? (size_t)FUSED * K : 0;   // the block's Xq copy
     if (ydt == SQ_F16)
         SQ_LAUNCH((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, true, FP8, FUSED>), dim3(grid), dim3(64 * kWaves),
-                           dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin);
+                           dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin, asy);
     else
         SQ_LAUNCH((gemv_i8_kernel<RPI, TG, RG, PER, HOIST, false, FP8, FUSED>), dim3(grid),
-                           dim3(64 * kWaves), dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin);
+                           dim3(64 * kWaves), dyn, st, Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, acc_out, fin,
+                           asy);
     return hipSuccess;
 }
 
@@ -374,7 +380,7 @@ hipError_t launch_cfg(const int8_t* Xq, const float* xs, const int8_t* Wq, const
 template <bool FP8>
 hipError_t gemv_dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int ws_stride,
                          const float* bias, int64_t M, int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out,
-                         hipStream_t st) {
+                         hipStream_t st, AsymArgs asy = AsymArgs{}) {
     const int cus = dev_info().cus;
     const int m = (int)M, n = (int)N, k = (int)K;
     // Steps per wave for a load span of `span` bytes; the register-resident chunk is the next power of two.
@@ -385,7 +391,7 @@ hipError_t gemv_dispatch(const int8_t* Xq, const float* xs, const int8_t* Wq, co
     };
 #define SQ_GEMV(RPI, TG, RG, PER, HOIST, PER_CU) \
     launch_cfg<RPI, TG, RG, PER, HOIST, FP8>(Xq, xs, Wq, ws, ws_stride, bias, m, n, k, Y, ydt, acc_out, \
-                                        grid_of(RG * RPI, PER_CU), st)
+                                        grid_of(RG * RPI, PER_CU), st, FusedIn{nullptr, nullptr, nullptr}, asy)
     if (M <= 4) {
         // 4 rows x 256 bytes per load, one token group.
         const int per = per_of(256);
@@ -421,6 +427,12 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, cons
                        const SideArgs* side, hipStream_t st) {
     (void)side;
     return gemv_dispatch<false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, st);
+}
+
+hipError_t launch_gemv_asym(const int8_t* Xq, const float* xs, const int32_t* xz, const int8_t* Wq, const float* ws,
+                            int ws_stride, const int32_t* wrs, const float* bias, int64_t M, int64_t N, int64_t K,
+                            void* Y, int ydt, int32_t* acc_out, hipStream_t st) {
+    return gemv_dispatch<false>(Xq, xs, Wq, ws, ws_stride, bias, M, N, K, Y, ydt, acc_out, st, AsymArgs{xz, wrs});
 }
 
 namespace {

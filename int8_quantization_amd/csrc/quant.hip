@@ -139,9 +139,12 @@ template <typename T, int VEC, int CH, int MODE, bool OUTL, int FMT>
 __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X, int64_t M, int64_t K,
                                                         const float* __restrict__ s, int8_t* __restrict__ Xq,
                                                         float* __restrict__ scale, const int32_t* __restrict__ pos,
-                                                        _Float16* __restrict__ Xo, int tpg, int G) {
+                                                        _Float16* __restrict__ Xo, int32_t* __restrict__ zero, int tpg,
+                                                        int G) {
     using V = typename VecOf<T, VEC>::V;
+    static_assert(FMT != 2 || (!OUTL && MODE != 2), "zero-point codes are for activation rows");
     __shared__ float red[2][16];
+    __shared__ float red2[FMT == 2 ? 2 : 1][16];   // FMT 2: max(-x'), the bottom of the range
     const int g = threadIdx.x / tpg;          // row group
     const int tid = threadIdx.x - g * tpg;    // thread within the group
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -214,7 +217,8 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
         const bool live = m < M;
         V* rc = buf[0];
         float xv[CH][VEC];
-        float amax = 0.0f;
+        float amax = 0.0f;   // max |x'| (FMT 2: max x', the top of a range that contains 0)
+        float nlo = 0.0f;    // FMT 2: max(-x')
         auto pass1 = [&](auto guarded) {
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
@@ -235,7 +239,12 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
                         skip = (omask[i] >> e) & 1u;
                         if (skip && live) Xo[m * K + opos[i][e]] = (_Float16)rc[i][e];
                     }
-                    if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
+                    if constexpr (FMT == 2) {
+                        amax = __builtin_fmaxf(amax, x);
+                        nlo = __builtin_fmaxf(nlo, -x);
+                    } else {
+                        if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
+                    }
                 }
             }
         };
@@ -244,11 +253,45 @@ __global__ __launch_bounds__(1024) void quant_rows_fast(const T* __restrict__ X,
 
         amax = wave_max(amax);
         if (lane == 0) red[it & 1][wave] = amax;
+        if constexpr (FMT == 2) {
+            nlo = wave_max(nlo);
+            if (lane == 0) red2[it & 1][wave] = nlo;
+        }
         lds_barrier();
         float a = red[it & 1][w0];
         for (int w = 1; w < nw; ++w) a = __builtin_fmaxf(a, red[it & 1][w0 + w]);
+        if constexpr (FMT == 2) {
+            // zero-point codes: scale = fl32(fl32(hi - lo) / 255), z = clamp(rne(fl32(-lo / scale)), 0, 255),
+            // u = clamp(rne(fl32(x' / scale)) + z, 0, 255), stored as u - 128 with the zero point z - 128
+            float b = red2[it & 1][w0];
+            for (int w = 1; w < nw; ++w) b = __builtin_fmaxf(b, red2[it & 1][w0 + w]);
+            const float sc = (a + b) / 255.0f;   // hi - lo with lo = -b
+            int z = 0;
+            if (sc != 0.0f) z = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(b / sc), 0.0f, 255.0f);
+            if (live) {
+                if (tid == 0) {
+                    scale[m] = sc;
+                    zero[m] = z - 128;
+                }
+                const double rx = sc != 0.0f ? rcp64((double)sc) : 0.0;
+                const float zf = (float)z;
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    if (!valid[i]) continue;
+                    const int64_t c = tid + (int64_t)i * tpg;
+                    int q[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        // the quotient is exact in the normal range; below it, it rounds to 0 either way
+                        const float v = __builtin_rintf((float)((double)xv[i][e] * rx)) + zf;
+                        q[e] = sc == 0.0f ? -128 : (int)__builtin_amdgcn_fmed3f(v, 0.0f, 255.0f) - 128;
+                    }
+                    CodeStore<VEC>::store(Xq + m * K + c * VEC, q);
+                }
+            }
+        }
         const float xs = a / (FMT == 0 ? 127.0f : 448.0f);
-        if (live) {
+        if (FMT != 2 && live) {
             if (tid == 0) scale[m] = xs;
             const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
 #pragma unroll
@@ -280,14 +323,15 @@ __global__ __launch_bounds__(1024) void quant_rows_generic(const T* __restrict__
                                                            const float* __restrict__ s, int8_t* __restrict__ Xq,
                                                            float* __restrict__ scale,
                                                            const int32_t* __restrict__ pos,
-                                                           _Float16* __restrict__ Xo) {
+                                                           _Float16* __restrict__ Xo, int32_t* __restrict__ zero) {
     __shared__ float red[2][16];
+    __shared__ float red2[2][16];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63, nwaves = nthr >> 6;
     int it = 0;
     for (int64_t m = blockIdx.x; m < M; m += gridDim.x, ++it) {
         const T* row = X + m * K;
-        float amax = 0.0f;
+        float amax = 0.0f, nlo = 0.0f;
         for (int64_t j = tid; j < K; j += nthr) {
             float x = (float)row[j];
             if constexpr (MODE == 1) x = x / s[j];
@@ -298,13 +342,40 @@ __global__ __launch_bounds__(1024) void quant_rows_generic(const T* __restrict__
                 skip = p >= 0;
                 if (skip) Xo[m * K + p] = (_Float16)row[j];
             }
-            if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
+            if constexpr (FMT == 2) {
+                amax = __builtin_fmaxf(amax, x);
+                nlo = __builtin_fmaxf(nlo, -x);
+            } else {
+                if (!skip) amax = __builtin_fmaxf(amax, __builtin_fabsf(x));
+            }
         }
         amax = wave_max(amax);
         if (lane == 0) red[it & 1][wave] = amax;
+        if constexpr (FMT == 2) {
+            nlo = wave_max(nlo);
+            if (lane == 0) red2[it & 1][wave] = nlo;
+        }
         __syncthreads();
         float a = red[it & 1][0];
         for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[it & 1][w]);
+        if constexpr (FMT == 2) {
+            float b = red2[it & 1][0];
+            for (int w = 1; w < nwaves; ++w) b = __builtin_fmaxf(b, red2[it & 1][w]);
+            const float sc = (a + b) / 255.0f;
+            int z = 0;
+            if (sc != 0.0f) z = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(b / sc), 0.0f, 255.0f);
+            if (tid == 0) {
+                scale[m] = sc;
+                zero[m] = z - 128;
+            }
+            for (int64_t j = tid; j < K; j += nthr) {
+                float x = (float)row[j];
+                if constexpr (MODE == 1) x = x / s[j];
+                const float v = __builtin_rintf(x / sc) + (float)z;
+                Xq[m * K + j] = (int8_t)(sc == 0.0f ? -128 : (int)__builtin_amdgcn_fmed3f(v, 0.0f, 255.0f) - 128);
+            }
+            continue;
+        }
         const float xs = a / (FMT == 0 ? 127.0f : 448.0f);
         if (tid == 0) scale[m] = xs;
         for (int64_t j = tid; j < K; j += nthr) {
@@ -328,7 +399,7 @@ static int blocks_per_cu(Kern k, int threads) {
 
 template <typename T, int VEC, int CH, int MODE, bool OUTL, int FMT>
 static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
-                              const int32_t* pos, _Float16* Xo, hipStream_t st) {
+                              const int32_t* pos, _Float16* Xo, int32_t* zero, hipStream_t st) {
     const int64_t nchunk = K / VEC;
     const int tpg = (int)((((nchunk + CH - 1) / CH) + 63) / 64 * 64);   // threads per row group
     const int G = 1024 / tpg;                                          // row groups per block
@@ -344,7 +415,7 @@ static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, 
     const int64_t rows_blocks = (M + G - 1) / G;
     const int64_t g = (int64_t)dev_info().cus * nb;
     SQ_LAUNCH(k, dim3((unsigned)(g < rows_blocks ? g : rows_blocks)), dim3(threads), 0, st, X, M, K, s, Xq,
-                       scale, pos, Xo, tpg, G);
+                       scale, pos, Xo, zero, tpg, G);
     return hipSuccess;
 }
 
@@ -352,28 +423,38 @@ static hipError_t launch_fast(const T* X, int64_t M, int64_t K, const float* s, 
 // two-pass fallback.
 template <typename T, int MODE, bool OUTL, int FMT>
 static hipError_t quant_rows_t(const T* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
-                               const int32_t* pos, _Float16* Xo, hipStream_t st) {
+                               const int32_t* pos, _Float16* Xo, hipStream_t st, int32_t* zero = nullptr) {
     if constexpr (sizeof(T) == 2) {
         // one 16-byte chunk per thread (one row per block) when there are few rows: the per-block
         // setup is then split over the most threads
         if (K <= 1024 || (K <= 8192 && M <= dev_info().cus))
-            return launch_fast<T, 8, 1, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 16384) return launch_fast<T, 8, 2, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 20480) return launch_fast<T, 4, 5, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
+            return launch_fast<T, 8, 1, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, zero, st);
+        if (K <= 16384) return launch_fast<T, 8, 2, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, zero, st);
+        if (K <= 20480) return launch_fast<T, 4, 5, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, zero, st);
     } else {
-        if (K <= 4096) return launch_fast<T, 4, 1, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 8192) return launch_fast<T, 4, 2, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
-        if (K <= 12288) return launch_fast<T, 4, 3, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, st);
+        if (K <= 4096) return launch_fast<T, 4, 1, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, zero, st);
+        if (K <= 8192) return launch_fast<T, 4, 2, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, zero, st);
+        if (K <= 12288) return launch_fast<T, 4, 3, MODE, OUTL, FMT>(X, M, K, s, Xq, scale, pos, Xo, zero, st);
     }
     auto k = quant_rows_generic<T, MODE, OUTL, FMT>;
     const int64_t g = (int64_t)dev_info().cus * 2;
-    SQ_LAUNCH(k, dim3((unsigned)(g < M ? g : M)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo);
+    SQ_LAUNCH(k, dim3((unsigned)(g < M ? g : M)), dim3(1024), 0, st, X, M, K, s, Xq, scale, pos, Xo, zero);
     return hipSuccess;
 }
 
 hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const float* s, int mode,
-                             int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st, int fmt) {
+                             int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo, hipStream_t st, int fmt,
+                             int32_t* zero) {
     const bool outl = pos != nullptr;
+    if (fmt == 2) {   // zero-point int8 codes of activation rows (mode 0 or 1, no outlier variant)
+        if (dt == SQ_F16) {
+            if (mode == 1)
+                return quant_rows_t<_Float16, 1, false, 2>((const _Float16*)X, M, K, s, Xq, scale, nullptr, nullptr, st, zero);
+            return quant_rows_t<_Float16, 0, false, 2>((const _Float16*)X, M, K, s, Xq, scale, nullptr, nullptr, st, zero);
+        }
+        if (mode == 1) return quant_rows_t<float, 1, false, 2>((const float*)X, M, K, s, Xq, scale, nullptr, nullptr, st, zero);
+        return quant_rows_t<float, 0, false, 2>((const float*)X, M, K, s, Xq, scale, nullptr, nullptr, st, zero);
+    }
     if (dt == SQ_F16 && fmt == 0 && !outl && (mode == 0 || mode == 1) && quant_stream_applies(M, K, mode == 1, false))
         return launch_quant_stream(static_cast<const _Float16*>(X), M, K, mode == 1 ? s : nullptr, Xq, scale, nullptr,
                                    st);
@@ -535,6 +616,31 @@ hipError_t launch_colmax_fresh(const _Float16* X, int64_t M, int64_t K, uint32_t
         SQ_LAUNCH(colmax_strip_kernel<2>, dim3((unsigned)(K / 16)), dim3(1024), 0, st, X, M, K, out_bits);
     else
         SQ_LAUNCH(colmax_strip_kernel<1>, dim3((unsigned)(K / 8)), dim3(1024), 0, st, X, M, K, out_bits);
+    return hipSuccess;
+}
+
+// Row sums of an int8 matrix (the weight term of the zero-point correction, computed once
+// per weight): one wave per row, 16 bytes per lane per step, then a wave sum.
+__global__ __launch_bounds__(256) void rowsum_kernel(const int8_t* __restrict__ Wq, int64_t N, int64_t K,
+                                                     int32_t* __restrict__ rowsum) {
+    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (n >= N) return;   // wave-uniform
+    const v4i* row = reinterpret_cast<const v4i*>(Wq + n * K);
+    int t = 0;
+    for (int64_t c = lane; c < K / 16; c += 64) {
+        const v4i v = row[c];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) t += (int)(int8_t)((uint32_t)v[w] >> (8 * b));
+    }
+    t = wave_sum_int(t);
+    if (lane == 0) rowsum[n] = t;
+}
+
+hipError_t launch_weight_rowsum(const int8_t* Wq, int64_t N, int64_t K, int32_t* rowsum, hipStream_t st) {
+    SQ_LAUNCH(rowsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, Wq, N, K, rowsum);
     return hipSuccess;
 }
 

@@ -263,6 +263,40 @@ sq_status sq_quantize_per_token_fp8(const void* X, int xdt, int64_t M, int64_t K
                                         nullptr, stream, 1));
 }
 
+sq_status sq_quantize_per_token_asym(const void* X, int xdt, int64_t M, int64_t K, const float* s, int8_t* Xq,
+                                     float* x_scale, int32_t* x_zero, hipStream_t stream) {
+    if (!X || !Xq || !x_scale || !x_zero) return SQ_ERR_NULL;
+    if (bad_shape(M, 1, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(xdt)) return SQ_ERR_DTYPE;
+    if (misaligned(X) || misaligned(Xq) || misaligned(x_scale) || misaligned(x_zero) || (s && misaligned(s)))
+        return SQ_ERR_ALIGN;
+    return hip_status(launch_quant_rows(X, xdt, M, K, s, s ? 1 : 0, Xq, x_scale, nullptr, nullptr, stream, 2, x_zero));
+}
+
+sq_status sq_weight_rowsum(const int8_t* Wq, int64_t N, int64_t K, int32_t* rowsum, hipStream_t stream) {
+    if (!Wq || !rowsum) return SQ_ERR_NULL;
+    if (bad_shape(1, N, K)) return SQ_ERR_SHAPE;
+    if (misaligned(Wq) || misaligned(rowsum)) return SQ_ERR_ALIGN;
+    return hip_status(launch_weight_rowsum(Wq, N, K, rowsum, stream));
+}
+
+sq_status w8a8_asym_gemm_dequant(const int8_t* Xq, const float* x_scale, const int32_t* x_zero, const int8_t* Wq,
+                                 const float* w_scale, int g, const int32_t* w_rowsum, const float* bias, int64_t M,
+                                 int64_t N, int64_t K, void* Y, int ydt, int32_t* acc_out, hipStream_t stream) {
+    if (!Xq || !x_scale || !x_zero || !Wq || !w_scale || !w_rowsum || !Y) return SQ_ERR_NULL;
+    if (bad_shape(M, N, K)) return SQ_ERR_SHAPE;
+    if (bad_dtype(ydt) || (g != SQ_PER_CHANNEL && g != SQ_PER_TENSOR)) return SQ_ERR_DTYPE;
+    if (misaligned(Xq) || misaligned(x_scale) || misaligned(x_zero) || misaligned(Wq) || misaligned(w_scale) ||
+        misaligned(w_rowsum) || misaligned(Y) || (bias && misaligned(bias)) || (acc_out && misaligned(acc_out)))
+        return SQ_ERR_ALIGN;
+    const int stride = g == SQ_PER_CHANNEL ? 1 : 0;
+    if (M <= 16)
+        return hip_status(launch_gemv_asym(Xq, x_scale, x_zero, Wq, w_scale, stride, w_rowsum, bias, M, N, K, Y, ydt,
+                                           acc_out, stream));
+    return hip_status(launch_gemm_asym(Xq, x_scale, x_zero, Wq, w_scale, stride, w_rowsum, bias, M, N, K, Y, ydt,
+                                       acc_out, stream));
+}
+
 sq_status sq_quantize_weight_fp8(const void* W, int wdt, int64_t N, int64_t K, const float* s, int g,
                                  uint8_t* Wq, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!W || !Wq || !w_scale) return SQ_ERR_NULL;

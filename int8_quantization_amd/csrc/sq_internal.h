@@ -148,10 +148,12 @@ inline RowPack row_pack(int64_t M, int64_t nchunk, int64_t rows_per_thread, int6
 // Per-row smoothing + absmax quantization (activations per token, weights per channel).
 // mode 0: no smoothing; 1: x / s_j; 2: x * s_j.  pos/Xo (LLM.int8() only): pos[j] >= 0
 // marks an outlier column, whose value is copied to Xo[m*K + pos[j]] and whose code is 0.
-// fmt 0: int8 codes, scale max/127; fmt 1: FP8 E4M3 code bytes, scale max/448 (no pos).
+// fmt 0: int8 codes, scale max/127; fmt 1: FP8 E4M3 code bytes, scale max/448 (no pos);
+// fmt 2: zero-point int8 codes over the row range extended to 0, scale (hi - lo)/255, the
+// zero point (minus 128) to zero[m] (mode 0 or 1, no pos).
 hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const float* s,
                              int mode, int8_t* Xq, float* scale, const int32_t* pos, _Float16* Xo,
-                             hipStream_t st, int fmt = 0);
+                             hipStream_t st, int fmt = 0, int32_t* zero = nullptr);
 
 // The LLM.int8() split done inside the streaming quantizer: from the column maxima (float
 // bits) and the threshold, the ascending outlier list and count (written to idx / count and
@@ -201,6 +203,12 @@ struct SideArgs {
     const int32_t* count;
     int64_t ldo;
 };
+// Zero-point activations: per-row zero points (minus 128) and per-output-row sums of Wq.
+struct AsymArgs {
+    const int32_t* xz;
+    const int32_t* wrs;
+};
+
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
                        int ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
@@ -214,6 +222,16 @@ hipError_t launch_gemm_fp8(const uint8_t* Xq, const float* xs, const uint8_t* Wq
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
                        int ws_stride, const float* bias, int64_t M, int64_t N, int64_t K, void* Y,
                        int ydt, int32_t* acc_out, const SideArgs* side, hipStream_t st);
+// Zero-point activations (x_zero: zero point minus 128 per row, w_rowsum: sum of each Wq
+// row): the same GEMM and decode kernels with acc - x_zero[m] * w_rowsum[n] dequantized.
+hipError_t launch_gemm_asym(const int8_t* Xq, const float* xs, const int32_t* xz, const int8_t* Wq, const float* ws,
+                            int ws_stride, const int32_t* wrs, const float* bias, int64_t M, int64_t N, int64_t K,
+                            void* Y, int ydt, int32_t* acc_out, hipStream_t st);
+hipError_t launch_gemv_asym(const int8_t* Xq, const float* xs, const int32_t* xz, const int8_t* Wq, const float* ws,
+                            int ws_stride, const int32_t* wrs, const float* bias, int64_t M, int64_t N, int64_t K,
+                            void* Y, int ydt, int32_t* acc_out, hipStream_t st);
+// Row sums of an int8 matrix [N x K] (K % 16 == 0), int32.
+hipError_t launch_weight_rowsum(const int8_t* Wq, int64_t N, int64_t K, int32_t* rowsum, hipStream_t st);
 // Fused decode layer (M <= 2, K <= 8192, fp16 X): per-token quantization of X (with
 // x / s_j when s is given) in every block's prologue, then the decode kernel; x_scale
 // (may be null) receives the per-token scales.

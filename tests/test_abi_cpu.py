@@ -45,6 +45,9 @@ def lib():
     lib.sq_kv_calibrate_per_head.argtypes = [V, I, I64, I64, I64, F, V, V]
     lib.sq_kv_quantize_per_head.argtypes = [V, I, I64, I64, I64, V, V, V]
     lib.sq_dequantize.argtypes = [V, I64, I64, V, I64, I64, V, I, V]
+    lib.sq_quantize_per_token_asym.argtypes = [V, I, I64, I64, V, V, V, V, V]
+    lib.sq_weight_rowsum.argtypes = [V, I64, I64, V, V]
+    lib.w8a8_asym_gemm_dequant.argtypes = [V, V, V, V, V, I, V, V, I64, I64, I64, V, I, V, V]
     return lib
 
 
@@ -266,6 +269,32 @@ def test_fp8_validation(lib):
     assert g(P, P, P, P, 0, None, 32, 32, 64, P, 9, None, None) == DTYPE
     assert g(P, P, P, P, 0, MIS, 32, 32, 64, P, 1, None, None) == ALIGN
     assert g(P, P, P, P, 0, None, 32, 32, 64, P, 1, MIS, None) == ALIGN
+
+
+def test_zero_point_validation(lib):
+    q = lib.sq_quantize_per_token_asym
+    assert q(None, 1, 4, 64, None, P, P, P, None) == NULL
+    assert q(P, 1, 4, 64, None, P, P, None, None) == NULL
+    assert q(P, 1, 0, 64, None, P, P, P, None) == SHAPE
+    assert q(P, 1, 4, 40, None, P, P, P, None) == SHAPE
+    assert q(P, 3, 4, 64, None, P, P, P, None) == DTYPE
+    assert q(P, 1, 4, 64, MIS, P, P, P, None) == ALIGN
+    assert q(P, 1, 4, 64, None, P, P, MIS, None) == ALIGN
+    r = lib.sq_weight_rowsum
+    assert r(None, 8, 64, P, None) == NULL
+    assert r(P, 8, 64, None, None) == NULL
+    assert r(P, 0, 64, P, None) == SHAPE
+    assert r(P, 8, 24, P, None) == SHAPE
+    assert r(MIS, 8, 64, P, None) == ALIGN
+    g = lib.w8a8_asym_gemm_dequant
+    assert g(P, P, None, P, P, 0, P, None, 32, 32, 64, P, 1, None, None) == NULL
+    assert g(P, P, P, P, P, 0, None, None, 32, 32, 64, P, 1, None, None) == NULL
+    assert g(P, P, P, P, P, 0, P, None, 32, 0, 64, P, 1, None, None) == SHAPE
+    assert g(P, P, P, P, P, 0, P, None, 32, 32, 72, P, 1, None, None) == SHAPE
+    assert g(P, P, P, P, P, 3, P, None, 32, 32, 64, P, 1, None, None) == DTYPE
+    assert g(P, P, P, P, P, 0, P, None, 32, 32, 64, P, 7, None, None) == DTYPE
+    assert g(P, P, MIS, P, P, 0, P, None, 32, 32, 64, P, 1, None, None) == ALIGN
+    assert g(P, P, P, P, P, 0, MIS, None, 32, 32, 64, P, 1, None, None) == ALIGN
 
 
 def test_linear_validation(lib):

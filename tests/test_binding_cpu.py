@@ -72,6 +72,12 @@ def _valid():
                                bias=t(N, F32), Y=t((M, N), F16), ws=ws, x_scale=t(M, F32)),
         "sq_w8a8_linear_noalloc": dict(X=t((M, K), F32), s=None, Wq=t((N, K), I8), w_scale=t(1, F32), gran=1,
                                        bias=None, Y=t((M, N), F32), x_scale=None),
+        "sq_quantize_per_token_asym": dict(X=t((M, K), F16), s=t(K, F32), Xq=t((M, K), I8), x_scale=t(M, F32),
+                                           x_zero=t(M, I32)),
+        "sq_weight_rowsum": dict(Wq=t((N, K), I8), rowsum=t(N, I32)),
+        "w8a8_asym_gemm_dequant": dict(Xq=t((M, K), I8), x_scale=t(M, F32), x_zero=t(M, I32), Wq=t((N, K), I8),
+                                       w_scale=t(N, F32), gran=0, w_rowsum=t(N, I32), bias=None, Y=t((M, N), F16),
+                                       acc_out=t((M, N), I32)),
     }
 
 
@@ -135,6 +141,15 @@ BAD = [
     ("sq_quantize_weight_fp8", "w_scale", t(N, F32)),
     ("fp8_gemm_dequant", "Xq", t((M, K), I8)),
     ("fp8_gemm_dequant", "acc_out", t((M, N), I32)),
+    ("sq_quantize_per_token_asym", "x_zero", t(M, F32)),
+    ("sq_quantize_per_token_asym", "x_zero", t(M - 1, I32)),
+    ("sq_quantize_per_token_asym", "Xq", t((M, K), U8)),
+    ("sq_weight_rowsum", "rowsum", t(N + 1, I32)),
+    ("sq_weight_rowsum", "Wq", t((N, K), U8)),
+    ("w8a8_asym_gemm_dequant", "x_zero", None),
+    ("w8a8_asym_gemm_dequant", "w_rowsum", t(N - 1, I32)),
+    ("w8a8_asym_gemm_dequant", "w_rowsum", t(N, F32)),
+    ("w8a8_asym_gemm_dequant", "Wq", t((N, K + 16), I8)),
     ("sq_w8a8_linear", "Wq", t((N, K + 16), I8)),
     ("sq_w8a8_linear", "x_scale", t(M + 1, F32)),
     ("sq_w8a8_linear", "Y", t((M + 1, N), F16)),

@@ -132,6 +132,24 @@ def slice_530b(seed: int = 0) -> Workload:
                     X16, {"w": W}, idx)
 
 
+def ffn_down_7b_post_activation(seed: int = 0, M: int = 2048) -> Workload:
+    """The 7B FFN-down projection, whose input is the output of the FFN's activation
+    function and so is not centred on zero (the case zero-point activations are for):
+    X [M x 11008] = h * sigmoid(h) for h ~ N(0, 1) times a per-row factor U(0.5, 3)
+    (the SiLU activation; a long positive tail, negatives only down to about -0.28
+    times the factor); W_down [4096 x 11008] N(0, 0.02).  Draw order: the per-row
+    factors, h, then W; fp16 casts at the end.  No smoothing."""
+    rng = np.random.default_rng(seed)
+    K, N = 11008, 4096
+    fac = rng.uniform(0.5, 3.0, (M, 1)).astype(np.float32)
+    h = rng.standard_normal((M, K), dtype=np.float32) * fac
+    X = h / (np.float32(1.0) + np.exp(-h))
+    del h
+    W = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)).astype(np.float16)
+    return Workload(f"ffn_down_7b_silu_{M}x11008x4096_f16", M, K, None, 0, np.float16, X.astype(np.float16),
+                    {"down": W}, np.zeros(0, np.int64))
+
+
 def random_layer(seed: int, M: int, K: int, N: int, dtype=np.float16, n_outliers: int = 0,
                  factor: float = 50.0, w_sigma: float = 0.02):
     """Small generic case for tests: (X [M,K], W [N,K], outlier idx)."""
