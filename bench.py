@@ -24,8 +24,9 @@ over a second timed pass of the same steps), against the 5.0 POP/s dense int8
 MFMA peak.
 cpu_baseline: the CPU oracle doing the same per-token work on a bounded number
 of token rows, on this host's cores.
-secondary: the 7B prefill projections, decode (GB/s), LLM.int8(), LayerNorm +
-quantization, static scale, FP8 and KV-cache workloads, same method.
+secondary: the 7B prefill projections, decode (GB/s), LLM.int8(), zero-point
+activations, LayerNorm + quantization, static scale, FP8 and KV-cache workloads,
+same method.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -248,6 +249,54 @@ def bench_fp8(torch, sq, d, wl, steps, warmup):
     gemm_tops = ops / len(projs) / (gemm_ms * 1e-3) / 1e12
     return dict(ms_per_step=ms, TOPS=ops / (ms * 1e-3) / 1e12, gemm_us_per_launch=gemm_ms * 1e3,
                 gemm_TOPS=gemm_tops, gemm_mfma_frac=gemm_tops / PEAK_FP8_TOPS)
+
+
+def bench_zero_point(torch, sq, d, wl, steps, warmup, sample_rows=64):
+    """Zero-point activations on the 7B FFN-down projection over SiLU outputs: the step
+    (zero-point per-token quantization + the GEMM with the row-sum correction) beside the
+    symmetric step on the same input, and, on a sample of rows, the error of both against
+    the unquantized fp64 product (as SNR in dB: zero points are for ranges not centred on 0)."""
+    M, K = wl.X.shape
+    W = wl.weights["down"]
+    N = W.shape[0]
+    X = d(wl.X)
+    _, Wq, ws = prepare_weight(torch, sq, d, wl.calib, W, None, 0)
+    rs = torch.empty(N, dtype=torch.int32, device="cuda")
+    sq.sq_weight_rowsum(Wq, rs)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    xz = torch.empty(M, dtype=torch.int32, device="cuda")
+    Ya = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    Ys = torch.empty(M, N, dtype=torch.float16, device="cuda")
+
+    def step_asym(timer):
+        sq.sq_quantize_per_token_asym(X, None, Xq, xs, xz)
+        sq.w8a8_asym_gemm_dequant(Xq, xs, xz, Wq, ws, 0, rs, None, Ya)
+
+    def step_sym(timer):
+        sq.sq_quantize_per_token(X, None, Xq, xs)
+        sq.w8a8_gemm_dequant(Xq, xs, Wq, ws, 0, None, Ys)
+
+    settle(torch, step_asym, 0.3)
+    ms_a, _ = time_steps(torch, step_asym, steps, warmup, kernel_events=False)
+    ms_s, _ = time_steps(torch, step_sym, steps, warmup, kernel_events=False)
+    q_ms, _ = time_steps(torch, lambda t: sq.sq_quantize_per_token_asym(X, None, Xq, xs, xz), steps, 5,
+                         kernel_events=False)
+    step_asym(None)
+    step_sym(None)
+    torch.cuda.synchronize()
+    ref = wl.X[:sample_rows].astype(np.float64) @ W.astype(np.float64).T
+
+    def snr(Y):
+        e = Y[:sample_rows].float().cpu().numpy().astype(np.float64) - ref
+        return float(10 * np.log10((ref ** 2).sum() / (e ** 2).sum()))
+
+    ops = 2.0 * M * N * K
+    qb = 2 * M * K + M * K + 8 * M
+    return dict(workload=wl.name, ms_per_step=ms_a, TOPS=ops / (ms_a * 1e-3) / 1e12,
+                symmetric_ms_per_step=ms_s, symmetric_TOPS=ops / (ms_s * 1e-3) / 1e12,
+                quantize_us=q_ms * 1e3, quantize_hbm_frac=qb / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                snr_db_vs_fp64=snr(Ya), symmetric_snr_db_vs_fp64=snr(Ys), snr_rows=sample_rows)
 
 
 def bench_fp8_decode(torch, sq, d, wl, steps, warmup, copies=3):
@@ -574,7 +623,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default=None,
-                    help="run one workload: slice_530b|prefill_7b|decode_70b|llm_int8|layernorm_quant|static_quant|kv_cache|fp8")
+                    help="run one workload: slice_530b|prefill_7b|decode_70b|llm_int8|zero_point|layernorm_quant|static_quant|kv_cache|fp8")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -674,6 +723,12 @@ def main():
             if not args.no_cpu_baseline:
                 secondary["llm_int8"]["cpu_oracle_one_thread"] = oracle_one_thread(wl4)
             del wl4
+        if args.only in (None, "zero_point"):
+            log("zero_point: generating inputs")
+            wl5 = workloads.ffn_down_7b_post_activation()
+            secondary["zero_point_ffn_down_7b"] = bench_zero_point(torch, sq, d, wl5, sec_steps * 2, sec_warm)
+            del wl5
+            torch.cuda.empty_cache()
         if args.only in (None, "layernorm_quant"):
             log("layernorm_quant: prefill activation")
             secondary["layernorm_quant_7b"] = bench_layernorm_quant(torch, sq, d, workloads.prefill_7b(which=("qkv",)),
