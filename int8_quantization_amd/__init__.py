@@ -76,7 +76,7 @@ EXPORTS = ("sq_status_string", "sq_workspace_size", "sq_smooth_scales", "sq_quan
 
 
 def _p(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _dt(t):
@@ -87,13 +87,20 @@ def _dt(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+# The current stream's raw handle without building a torch.cuda.Stream object (a few
+# microseconds per call, which small kernels would otherwise wait for on the host).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream():
-    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _on_gpu(t):
     """True when t lives on the current GPU (the device the library launches on)."""
-    return t.is_cuda and t.device.index == torch.cuda.current_device()
+    return t.is_cuda and t.get_device() == torch.cuda.current_device()
 
 
 F16, F32, I8, U8, I32 = torch.float16, torch.float32, torch.int8, torch.uint8, torch.int32
