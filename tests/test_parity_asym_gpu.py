@@ -108,7 +108,8 @@ def test_weight_rowsum(sq, orc, N, K):
 # reloaded per chunk); larger M: the tile kernel's 128 x 128, 256 x 192 and 256 x 256 tiles
 # and the two-launch column split (each compared over its whole output)
 ASYM_GEMM_CASES = [
-    (1, 300, 1024), (4, 1000, 4096), (8, 130, 12304), (16, 4100, 8192), (3, 257, 20496),
+    (1, 300, 1024), (4, 1000, 4096), (8, 130, 12304), (16, 4100, 8192), (3, 257, 20496), (12, 77, 16384),
+    (15, 90, 20496),
     (300, 520, 1040), (2047, 6143, 144), (3000, 5000, 272), (4096, 10240, 144),
 ]
 

@@ -219,9 +219,12 @@ GEMM_CASES = [
     (1, 1, 16), (1, 1000, 8192), (4, 1000, 144), (7, 33, 4096), (16, 4100, 8192),
     # decode kernel with the activation slice reloaded per k chunk (K beyond what a wave keeps in
     # registers), ragged N and K
-    (2, 301, 20496), (8, 130, 12304), (16, 257, 12288), (3, 4100, 16400),
+    (2, 301, 20496), (8, 130, 12304), (3, 4100, 16400), (12, 300, 20496),
     # M = 5..8: two token groups of 4 (activations in registers, and reloaded per k chunk)
     (5, 1000, 8192), (6, 301, 20496), (8, 4100, 8192), (7, 9, 272),
+    # M = 9..16: four token groups of 4, activations in registers, 1, 2, 4 and 8 steps of 256
+    # bytes per wave
+    (16, 70, 1040), (11, 500, 3072), (9, 333, 4112), (16, 257, 12288), (14, 129, 16384),
     (17, 32, 16), (33, 70, 144), (200, 300, 1040), (256, 256, 256), (300, 520, 4112),
     # the largest K the library accepts: (-128)*(-128)*K = 2147221504 still fits int32; the tile
     # kernel also gets a partial last K tile (131056 % 128 = 112)
@@ -1037,7 +1040,8 @@ def test_fp8_accumulation_premise(sq, orc):
 @pytest.mark.parametrize("M,N,K,gran,use_bias,out_dt", [
     (1, 100, 512, 0, False, np.float16), (1, 257, 8192, 0, True, np.float32), (3, 1000, 4112, 1, False, np.float16),
     (4, 512, 20480, 0, False, np.float16), (8, 777, 1040, 0, True, np.float16), (13, 300, 16400, 0, False, np.float32),
-    (16, 1024, 8192, 1, True, np.float16), (16, 64, 16, 0, False, np.float16)])
+    (16, 1024, 8192, 1, True, np.float16), (16, 64, 16, 0, False, np.float16), (10, 200, 3008, 0, True, np.float32),
+    (14, 100, 16384, 1, False, np.float16)])
 def test_fp8_decode(sq, orc, M, N, K, gran, use_bias, out_dt):
     """M <= 16 runs on the weight-streaming kernel's FP8 path."""
     r = np.random.default_rng(M * 11 + N + K)
