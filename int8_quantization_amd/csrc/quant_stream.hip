@@ -89,32 +89,6 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
-// Maximum over the wave of non-negative floats, returned to every lane: four DPP steps
-// give each row of 16 lanes its maximum (quad swaps 1 and 2, then the half-row and
-// row mirrors), and the four row maxima are read out (v_readlane) and combined.  Much
-// shorter than the ds_bpermute butterfly of __shfl_xor.
-__device__ __forceinline__ float wave_max_dpp(float v) {
-    auto step = [](float x, int ctrl) -> float {
-        int y;
-        switch (ctrl) {
-            case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
-            case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
-            case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
-            default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false); break; // row_mirror
-        }
-        return __builtin_fmaxf(x, __int_as_float(y));
-    };
-    v = step(v, 0);
-    v = step(v, 1);
-    v = step(v, 2);
-    v = step(v, 3);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
-}
-
 // Code byte of rne(v) for |v| < 2^22, in the low byte of the result.
 __device__ __forceinline__ uint32_t code_bits(float v) { return __float_as_uint(v + 12582912.0f); }
 
@@ -334,7 +308,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
         // the IEEE-division check runs only in waves with some s_j >= 2^100 (a uniform branch)
         if (SMOOTH && guard_wave) pass1(std::true_type{});
         else pass1(std::false_type{});
-        amax = wave_max_dpp(amax);
+        amax = wave_max(amax);
         if (lane == 0) red[j & 1][wave] = amax;
         barrier_lds();                            // also: every wave is done reading the step's slot
         float a = red[j & 1][w0];

@@ -51,10 +51,31 @@ __device__ __forceinline__ int code_of(float v) {
     return (int)r;
 }
 
+// Maximum over the wave of non-negative floats, returned to every lane (all 64 lanes active).
+// Four DPP steps give each row of 16 lanes its maximum (quad swaps 1 and 2, then the
+// half-row and row mirrors), and the four row maxima are read out (v_readlane) and
+// combined: a few cycles per step, against an LDS round trip per step for the
+// ds_bpermute butterfly of __shfl_xor.  The maximum is exact in any order.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    auto step = [](float x, int ctrl) -> float {
+        int y;
+        switch (ctrl) {
+            case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+            case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+            case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+            default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false); break; // row_mirror
+        }
+        return __builtin_fmaxf(x, __int_as_float(y));
+    };
+    v = step(v, 0);
+    v = step(v, 1);
+    v = step(v, 2);
+    v = step(v, 3);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
 }
 
 // 16 bytes per lane from a buffer resource straight into LDS: the wave's 1 KB
