@@ -26,7 +26,8 @@
 // wave w owns a contiguous slice of every row's k range, so its activation
 // fragments are the same for every tile and stay in registers when they fit
 // (HOIST), else they are reloaded per k chunk (from L2).  Blocks are persistent
-// and take tiles blockIdx.x, blockIdx.x + gridDim.x, ..., so the rows in flight
+// and take tiles b, b + gridDim.x, ... (b: the block's slot, blockIdx.x or, at M = 9..16,
+// blockIdx.x permuted so that one XCD's blocks hold consecutive slots), so the rows in flight
 // across the chip form a compact front.  Each wave loads the next tile (or
 // chunk) before running the MFMAs of the current one; the 8 partial tiles are
 // summed through LDS and the dequant epilogue stores Y (and acc).
@@ -108,7 +109,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const int s_end = min(S, s_begin + per);
     const int nch = HOIST ? 1 : (per + PER - 1) / PER;
     const int ntiles = (N + TROWS - 1) / TROWS;
-    const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+    // Block slot.  With four token groups (M = 9..16, one block per CU) and a grid of whole
+    // XCD groups, the blocks of one XCD (blockIdx.x % 8, dealt round-robin) take consecutive
+    // tiles of every round, so the 8-byte output runs of adjacent 4-row tiles meet in that
+    // XCD's L2 and leave it as whole lines (4x fewer HBM write bytes; 70B FFN-up rows at
+    // M = 16: 39.4-39.7 vs 40.6-41.2 us back to back).  The smaller M, with three blocks per
+    // CU, measured slower with it (M = 1: 38.2 vs 35.9 us) and keep blockIdx.x.
+    const int nbk = (int)gridDim.x;
+    const int slot = (TG == 4 && nbk % 8 == 0) ? (int)(blockIdx.x % 8) * (nbk / 8) + (int)(blockIdx.x / 8)
+                                              : (int)blockIdx.x;
+    const int my_tiles = slot < ntiles ? (ntiles - 1 - slot) / nbk + 1 : 0;
     const int nunits = my_tiles * nch;
 
     // Loads go through buffer resources (record counts pass through readfirstlane so that the
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const int xzv = (!FP8 && asy.xz != nullptr) ? asy.xz[em] : 0;
     const float* bsrc = bias != nullptr ? bias : ws;
     auto load_unit = [&](int unit, Buf& b) {
-        const int tile = blockIdx.x + (unit / nch) * gridDim.x;
+        const int tile = slot + (unit / nch) * nbk;
         const int ch = unit % nch;
         if (!HOIST) load_x(ch, b.x);
         const int rows = max(0, min(TROWS, N - tile * TROWS));   // 0 past the last tile
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
         // The other parity's buffer is only rewritten after every wave has passed the next barrier,
         // i.e. after every reader of this tile's buffer has finished with it.
         lds_barrier();
-        const int n = (blockIdx.x + ti * gridDim.x) * TROWS + ej;
+        const int n = (slot + ti * nbk) * TROWS + ej;
         if (eact && n < N) {
             const int rg = ej / RPI, jj = ej % RPI, tg = em / RPI, mm = em % RPI;
             using Elt = typename std::conditional<FP8, float, int>::type;
