@@ -26,7 +26,7 @@
 // wave w owns a contiguous slice of every row's k range, so its activation
 // fragments are the same for every tile and stay in registers when they fit
 // (HOIST), else they are reloaded per k chunk (from L2).  Blocks are persistent
-// and take tiles b, b + gridDim.x, ... (b: the block's slot, blockIdx.x or, at M = 9..16,
+// and take tiles b, b + gridDim.x, ... (b: the block's slot, blockIdx.x or, at M = 5..16,
 // blockIdx.x permuted so that one XCD's blocks hold consecutive slots), so the rows in flight
 // across the chip form a compact front.  Each wave loads the next tile (or
 // chunk) before running the MFMAs of the current one; the 8 partial tiles are
@@ -109,14 +109,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_i8_kernel(
     const int s_end = min(S, s_begin + per);
     const int nch = HOIST ? 1 : (per + PER - 1) / PER;
     const int ntiles = (N + TROWS - 1) / TROWS;
-    // Block slot.  With four token groups (M = 9..16, one block per CU) and a grid of whole
-    // XCD groups, the blocks of one XCD (blockIdx.x % 8, dealt round-robin) take consecutive
-    // tiles of every round, so the 8-byte output runs of adjacent 4-row tiles meet in that
-    // XCD's L2 and leave it as whole lines (4x fewer HBM write bytes; 70B FFN-up rows at
-    // M = 16: 39.4-39.7 vs 40.6-41.2 us back to back).  The smaller M, with three blocks per
-    // CU, measured slower with it (M = 1: 38.2 vs 35.9 us) and keep blockIdx.x.
+    // Block slot.  With two or four token groups (M = 5..16, one block per CU) and a grid of
+    // whole XCD groups, the blocks of one XCD (blockIdx.x % 8, dealt round-robin) take
+    // consecutive tiles of every round, so the 8-byte output runs of adjacent 4-row tiles meet
+    // in that XCD's L2 and leave it as whole lines (4x fewer HBM write bytes; 70B FFN-up rows
+    // back to back: M = 16 39.4-39.7 vs 40.6-41.2 us, M = 8 36.7-36.8 vs 37.1-37.6 us).  M <= 4,
+    // with three blocks per CU, measured slower with it (M = 1: 38.2 vs 35.9 us) and keeps
+    // blockIdx.x.
     const int nbk = (int)gridDim.x;
-    const int slot = (TG == 4 && nbk % 8 == 0) ? (int)(blockIdx.x % 8) * (nbk / 8) + (int)(blockIdx.x / 8)
+    const int slot = (TG >= 2 && nbk % 8 == 0) ? (int)(blockIdx.x % 8) * (nbk / 8) + (int)(blockIdx.x / 8)
                                               : (int)blockIdx.x;
     const int my_tiles = slot < ntiles ? (ntiles - 1 - slot) / nbk + 1 : 0;
     const int nunits = my_tiles * nch;
