@@ -59,13 +59,16 @@ def _rows(seed, M, K, dt):
 
 
 # M, K, dtype, smoothing: the register-resident kernel's configurations (one 16-byte chunk per
-# thread for few rows or short rows, 2 and 5 chunks, the fp32 ones) and the two-pass kernel for
-# longer rows
+# thread for few rows or short rows, 2 and 5 chunks, the fp32 ones, more rows than blocks) and
+# the two-pass kernel for longer rows
 ASYM_CASES = [
     (1, 16, np.float16, False), (7, 48, np.float32, True), (300, 1040, np.float16, True),
     (256, 8192, np.float16, False), (1000, 4096, np.float16, True), (300, 12304, np.float16, True),
     (130, 20480, np.float16, False), (70, 4096, np.float32, False), (90, 12288, np.float32, True),
     (20, 40960, np.float16, True), (9, 20000, np.float32, False),
+    (1024, 16, np.float16, True), (1029, 512, np.float16, False), (2048, 1040, np.float16, False),
+    (1100, 4096, np.float16, True), (1030, 8192, np.float16, True), (1024, 10240, np.float16, False),
+    (1024, 12304, np.float16, True), (1500, 20480, np.float16, False),
 ]
 
 
