@@ -14,19 +14,24 @@
 //   z_j  = fl32( fl32(x_j - fl32(mu)) * fl32(rstd) )
 //   y_j  = fl32( fl32(z_j * gamma'_j) + beta'_j )             (no add without beta)
 //   xs   = fl32( max_j |y_j| / 127 ),  q_j = clamp(rne(fl32(y_j / xs)), -128, 127)
-// (q = 0 and xs = 0 for an all-zero y).  HBM-bound: 2 B read and 1 B written per
-// element, 4 B per row for the scale.
+// (q = 0 and xs = 0 for an all-zero y).  2 B read and 1 B written per element, 4 B
+// per row for the scale; with the exact sums and the fp64 quotient, about 20 vector
+// instructions per element, so the kernels are bound by vector ALU issue rather than
+// by HBM.
 //
-// Layout: rows up to 16384 values are held in registers by groups of threads
-// (one 16-byte chunk per thread and pass, one or two passes); each row needs
-// two block reductions (the integer sums, then the absolute maximum).  Longer
-// rows take one block per row and three passes over the row (sums, maximum,
-// codes), reading it from L2 the second and third time.
+// Layout: with at least four rows per CU and rows up to 8192 values, one wave per row
+// (ln_quant_wave: both reductions inside the wave).  Fewer rows, or rows up to 16384
+// values: a group of up to 1024 threads per row, values held in registers, two block
+// reductions per row (ln_quant_rows).  Longer rows: one block per row and three passes
+// over the row (sums, maximum, codes), reading it from L2 the second and third time
+// (ln_quant_long).
 #include "sq_internal.h"
 
 namespace sq {
 
 namespace {
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // Barrier for LDS traffic only (does not wait for the row prefetch).
 __device__ __forceinline__ void lds_sync() {
@@ -130,44 +135,118 @@ __device__ __forceinline__ uint16_t hbits(const v4i& c, int e) {
     return (uint16_t)((uint32_t)c[e >> 1] >> (16 * (e & 1)));
 }
 
-// One wave per row (rows up to 8192 values): lane l holds the 16-byte chunks
-// l, l + 64, ... (CPL of them), so the two row reductions are wave shuffles and
-// the waves of a CU run independently (no block barrier after the prologue).
-// gamma' and beta' sit in LDS; the normalised values are computed twice (for the
-// row maximum, then for the codes) instead of being kept in registers.  With
-// PF, each wave loads its next row while it works on the current one.
-template <int CPL, bool BETA, bool PF>
+// Lane-to-lane copy of an fp64 value through DPP (CTRL is the dpp_ctrl code); every
+// lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave of fp64 values whose every partial sum is exact (integer multiples
+// of one power of two below 2^53 times it), so the order does not matter: the quad
+// swaps, the half-row and row mirrors give each row of 16 lanes its sum, and the four
+// row sums are read out and added.  All 64 lanes must be active.
+__device__ __forceinline__ double wave_sum_exact(double v) {
+    v += dpp_f64<0xB1>(v);    // quad_perm 1,0,3,2
+    v += dpp_f64<0x4E>(v);    // quad_perm 2,3,0,1
+    v += dpp_f64<0x141>(v);   // row_half_mirror
+    v += dpp_f64<0x140>(v);   // row_mirror
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Four codes, each the low byte of fl32(t + 1.5 2^23) for t = clamp(q, -128, 127): the
+// add rounds t to the nearest integer, ties to even, into the low mantissa bits (the
+// same code as clamping the rounded q); v_perm_b32 gathers the four low bytes.
+__device__ __forceinline__ uint32_t pack_codes(float q0, float q1, float q2, float q3) {
+    auto rb = [](float q) {
+        return __float_as_uint(__builtin_amdgcn_fmed3f(q, -128.0f, 127.0f) + 12582912.0f);
+    };
+    const uint32_t a = __builtin_amdgcn_perm(rb(q1), rb(q0), 0x0c0c0400u);   // bytes q0, q1, 0, 0
+    const uint32_t b = __builtin_amdgcn_perm(rb(q3), rb(q2), 0x0c0c0400u);   // bytes q2, q3, 0, 0
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);                          // q0, q1, q2, q3
+}
+
+// One wave per row (rows up to 8192 values): lane l holds the 16-byte chunks l, l + 64,
+// ... (CPL of them), so the two row reductions stay inside the wave and the waves of a
+// CU run independently (one block barrier, after the prologue).  gamma' and beta' sit
+// in LDS; the prologue issues the first row's loads before it waits for the weights.
+//
+// Row sums, in units of x (each binary16 x is n 2^-24, |n| < 2^40): S1 = sum x, and
+// x^2 (exact in fp64: 22 significant bits) split as q 2^-8 + r with q = floor(x^2 2^8)
+// and r = x^2 - q 2^-8 in [0, 2^-8), a multiple of 2^-48.  Over a row of at most 8192
+// values every partial sum of x, of q and of r is an integer multiple of 2^-24, 1 and
+// 2^-48 below 2^53 times it, so the fp64 sums are exact in any order; then
+// S1 = 2^24 sum x and S2 = sum n^2 = 2^40 sum q + 2^48 sum r as a 128-bit integer.
+//
+// Up to 4096 values per row (KEEP), the values stay in registers as fp32 from the sums
+// to the codes, and the next row's loads are issued as soon as the current row has been
+// converted; longer rows are read again from the chunk registers for the maximum and
+// for the codes.
+template <int CPL, bool BETA>
 __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                      const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, float eps,
                                                      int8_t* __restrict__ Xq, float* __restrict__ scale) {
+    constexpr int kThreads = 256, kWaves = kThreads / 64;
+    constexpr bool KEEP = CPL <= 8;
     extern __shared__ v4f sgb[];             // gamma' [K], then beta' [K]
-    const v4f* sg = sgb;
-    const v4f* sb = sgb + K / 4;
-    for (int64_t j = threadIdx.x; j < K / 4; j += blockDim.x) {
-        sgb[j] = reinterpret_cast<const v4f*>(gamma)[j];
-        if constexpr (BETA) sgb[K / 4 + j] = reinterpret_cast<const v4f*>(beta)[j];
-    }
-    __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int wpb = blockDim.x >> 6;
-    const int64_t nwv = (int64_t)gridDim.x * wpb;
+    const int64_t nwv = (int64_t)gridDim.x * kWaves;
     const int nchunk = (int)(K / 8);
-    int64_t m = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6);   // uniform per wave
-    v4i cur[CPL], nxt[PF ? CPL : 1];
-    auto load = [&](int64_t row, v4i* r) {
-        const v4i* src = reinterpret_cast<const v4i*>(X + row * K);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
-            r[i] = (row < M && c < nchunk) ? src[c] : v4i{0, 0, 0, 0};
-        }
+    const int nv4 = (int)(K / 4);
+    int64_t m = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // rows through buffer resources: a read past the row (or of a row past M, whose
+    // record count is 0) returns zeros, a write there is dropped
+    auto row_rsrc = [&](const void* base, int64_t row, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, row < M ? bytes : 0, 0x00020000);
     };
+    auto load = [&](int64_t row, v4i* r) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(X + (row < M ? row : 0) * K, row, (int)(2 * K));
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            r[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (lane + 64 * i), 0, 0));
+    };
+    // gamma'/beta' (K/4 <= 128 CPL vectors each): every thread loads FPT vectors of each
+    // (index clamped into the array) and writes them to LDS unconditionally (slots past K/4
+    // are slack, never read).  The weight loads are issued before the first row's loads, so
+    // the LDS writes and the barrier wait for the weights only, not for the row.
+    constexpr int FPT = (CPL + 1) / 2;
+    constexpr int NW = kThreads * FPT;       // LDS vectors per array
+    v4f fg[FPT], fb[BETA ? FPT : 1];
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+        const int j = (int)threadIdx.x + kThreads * i;
+        const int jj = j < nv4 ? j : nv4 - 1;
+        fg[i] = reinterpret_cast<const v4f*>(gamma)[jj];
+        if constexpr (BETA) fb[i] = reinterpret_cast<const v4f*>(beta)[jj];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4i cur[CPL];
     load(m, cur);
-    // y for the 8 values of chunk c (clamped into the row for the LDS reads; chunks past
-    // the row end are computed on zeros and never used)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+        const int j = (int)threadIdx.x + kThreads * i;
+        sgb[j] = fg[i];
+        if constexpr (BETA) sgb[NW + j] = fb[i];
+    }
+    lds_sync();
+    const v4f* sg = sgb;
+    const v4f* sb = sgb + NW;
     uint32_t lbase = 0;                       // LDS offset, re-read per row (see below)
-    auto yval = [&](const v4i& h, int c, float mu, float rs, float* y) {
+    // y for the 8 values of chunk c, from their fp32 values (chunks past the row end read
+    // the weights of chunk 0 and are never used)
+    auto yval = [&](const float* x, int c, float mu, float rs, float* y) {
         const int cc = (c < nchunk ? c : 0) + (int)lbase;
         const v4f g0 = sg[2 * cc], g1 = sg[2 * cc + 1];
         v4f b0{}, b1{};
@@ -177,66 +256,99 @@ __global__ __launch_bounds__(256) void ln_quant_wave(const uint16_t* __restrict_
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float v = ((half_bits_to_float(hbits(h, e)) - mu) * rs) * (e < 4 ? g0[e] : g1[e - 4]);
+            float v = ((x[e] - mu) * rs) * (e < 4 ? g0[e] : g1[e - 4]);
             if constexpr (BETA) v = v + (e < 4 ? b0[e] : b1[e - 4]);
             y[e] = v;
         }
     };
-    for (; m < M; m += nwv) {
+    auto xval = [&](const v4i& h, float* x) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = half_bits_to_float(hbits(h, e));
+    };
+    // the first row's pass runs on every wave (a wave without a row reads zeros, and its
+    // code stores are dropped), so that its loads stay ahead of the barrier above
+    do {
         // an opaque zero: keeps the compiler from hoisting every gamma'/beta' read out of
         // the row loop into registers (which would cost the occupancy that hides latency)
         asm volatile("" : "+s"(lbase));
-        if constexpr (PF) load(m + nwv, nxt);
-        Acc ta{0.0, 0.0, 0.0};
+        float xk[KEEP ? CPL : 1][8];
+        double s1 = -0.0, sq = -0.0, sr = -0.0;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
+            float* x = xk[KEEP ? i : 0];
+            xval(cur[i], x);                                        // zeros past the row end
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add_half(ta, half_bits_to_float(hbits(cur[i], e)));   // zeros add nothing
-            __builtin_amdgcn_sched_barrier(0);
+            for (int e = 0; e < 8; ++e) {
+                const double d = (double)x[e];
+                const double d2 = d * d;                            // exact
+                const double q = __builtin_floor(d2 * 256.0);       // exact
+                s1 += d;
+                sq += q;
+                sr += __builtin_fma(-q, 0x1p-8, d2);                // exact
+            }
         }
-        const Sums t = wave_sums(to_sums(ta));
+        if constexpr (KEEP) load(m + nwv, cur);                     // next row, in flight from here
+        s1 = wave_sum_exact(s1);
+        sq = wave_sum_exact(sq);
+        sr = wave_sum_exact(sr);
+        Sums t;
+        t.s1 = (int64_t)(s1 * 0x1p24);
+        {
+            const uint64_t Q = (uint64_t)sq, R = (uint64_t)(sr * 0x1p48);   // exact integers below 2^53
+            t.lo = (Q << 40) + R;
+            t.hi = (Q >> 24) + (t.lo < R ? 1u : 0u);
+        }
         float mu, rs;
         row_stats(t, K, eps, mu, rs);
-        constexpr bool KEEP = CPL <= 8;           // keep y in registers for the code pass
-        float yk[KEEP ? CPL : 1][8];
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            float* y = yk[KEEP ? i : 0];
-            yval(cur[i], c, mu, rs, y);
-            float a = 0.0f;
+            float xt[8];
+            float* x = xk[KEEP ? i : 0];
+            if constexpr (!KEEP) {
+                xval(cur[i], xt);
+                x = xt;
+            }
+            float y[8];
+            yval(x, c, mu, rs, y);
+            float a = __builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(y[e]));
+            for (int e = 2; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(y[e]));
             amax = c < nchunk ? __builtin_fmaxf(amax, a) : amax;
-            __builtin_amdgcn_sched_barrier(0);   // one chunk's values live at a time
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = y[e];            // y replaces x
+            }
         }
         amax = wave_max(amax);
         const float xs = amax / 127.0f;
-        if (lane == 0) scale[m] = xs;
-        const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
+        if (lane == 0 && m < M) scale[m] = xs;
+        const bool zero = xs == 0.0f;
+        const double rx = zero ? 0.0 : rcp64((double)xs);
+        const __amdgpu_buffer_rsrc_t rq = row_rsrc(Xq + m * K, m, (int)K);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + 64 * i;
-            float* y = yk[KEEP ? i : 0];
-            if (!KEEP) yval(cur[i], c, mu, rs, y);
-            int q[8];
+            float yt[8];
+            const float* y = xk[KEEP ? i : 0];
+            if constexpr (!KEEP) {
+                float xt[8];
+                xval(cur[i], xt);
+                yval(xt, c, mu, rs, yt);
+                y = yt;
+            }
+            float q[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = xs == 0.0f ? 0 : code_of((float)((double)y[e] * rx));
-            const uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
-                                ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
-            const uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
-                                ((uint32_t)(q[6] & 0xff) << 16) | ((uint32_t)(q[7] & 0xff) << 24);
-            if (c < nchunk) *reinterpret_cast<uint2*>(Xq + m * K + c * 8) = make_uint2(lo, hi);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int e = 0; e < 8; ++e) q[e] = (float)((double)y[e] * rx);   // = fl32(y / xs)
+            uint32_t lo = pack_codes(q[0], q[1], q[2], q[3]);
+            uint32_t hi = pack_codes(q[4], q[5], q[6], q[7]);
+            if (zero) lo = hi = 0;
+            __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, rq, 8 * c, 0, 0);
         }
-        if constexpr (PF) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) cur[i] = nxt[i];
-        } else {
-            load(m + nwv, cur);
-        }
-    }
+        if constexpr (!KEEP) load(m + nwv, cur);
+        m += nwv;
+    } while (m < M);
 }
 
 // Register-resident rows: CH 16-byte chunks per thread per row.
@@ -424,14 +536,14 @@ hipError_t launch_rows(const uint16_t* X, int64_t M, int64_t K, const float* gam
     return hipSuccess;
 }
 
-template <int CPL, bool BETA, bool PF>
+template <int CPL, bool BETA>
 hipError_t launch_wave(const uint16_t* X, int64_t M, int64_t K, const float* gamma, const float* beta, float eps,
                        int8_t* Xq, float* scale, hipStream_t st) {
     constexpr int kWaves = 4;                                          // rows in flight per block
     const int64_t blocks = (M + kWaves - 1) / kWaves;
     const int64_t cap = (int64_t)dev_info().cus * 8;
-    const size_t lds = (size_t)K * sizeof(float) * (BETA ? 2 : 1);
-    SQ_LAUNCH((ln_quant_wave<CPL, BETA, PF>), dim3((unsigned)(blocks < cap ? blocks : cap)),
+    const size_t lds = (size_t)(64 * kWaves) * ((CPL + 1) / 2) * sizeof(v4f) * (BETA ? 2 : 1);   // >= 4K (or 8K) B
+    SQ_LAUNCH((ln_quant_wave<CPL, BETA>), dim3((unsigned)(blocks < cap ? blocks : cap)),
                        dim3(64 * kWaves), lds, st, X, M, K, gamma, beta, eps, Xq, scale);
     return hipSuccess;
 }
@@ -442,11 +554,11 @@ hipError_t launch_ln(const uint16_t* X, int64_t M, int64_t K, const float* gamma
     // few rows: spread each row over a group of threads (up to 1024) instead of one wave
     if (K <= 8192 && M < 4 * (int64_t)dev_info().cus)
         return launch_rows<1, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
-    if (K <= 512) return launch_wave<1, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
-    if (K <= 1024) return launch_wave<2, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
-    if (K <= 2048) return launch_wave<4, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
-    if (K <= 4096) return launch_wave<8, BETA, true>(X, M, K, gamma, beta, eps, Xq, scale, st);
-    if (K <= 8192) return launch_wave<16, BETA, false>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 512) return launch_wave<1, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 1024) return launch_wave<2, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 2048) return launch_wave<4, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 4096) return launch_wave<8, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
+    if (K <= 8192) return launch_wave<16, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
     if (K <= 16384) return launch_rows<2, BETA>(X, M, K, gamma, beta, eps, Xq, scale, st);
     const int64_t cap = (int64_t)dev_info().cus * 2;
     SQ_LAUNCH((ln_quant_long<BETA>), dim3((unsigned)(M < cap ? M : cap)), dim3(1024), 0, st, X, M, K,

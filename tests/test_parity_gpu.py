@@ -534,6 +534,10 @@ LN_CASES = [
     # M, K   (K <= 8192: one 16-byte chunk per thread; <= 16384: two; longer: three passes per row)
     (1, 16), (3, 64), (7, 1040), (33, 4096), (300, 4112), (64, 8192), (17, 12304), (16, 16384),
     (5, 20480), (2, 131056), (1000, 256),
+    # at least four rows per CU, rows up to 8192 values: one wave per row (1 to 16 chunks per
+    # lane; ragged chunk counts; more rows than waves in the grid, so waves take a second row)
+    (1024, 16), (1100, 528), (1030, 1040), (2048, 2048), (1500, 4096), (1025, 4112), (1024, 8192),
+    (9000, 512),
 ]
 
 
@@ -580,6 +584,32 @@ def test_layernorm_quantize_special_rows(sq, orc):
     # the zero row without beta: scale 0, all codes 0
     Xq, xs = gpu_ln_quant(sq, X[1:2], g, None, 1e-5)
     assert xs[0] == 0.0 and not Xq.any()
+
+
+@pytest.mark.parametrize("K", [4096, 8192])
+def test_layernorm_quantize_special_rows_wave(sq, orc, K):
+    """The special rows (constant, zero, symmetric, binary16 extremes, subnormals, one
+    spike), repeated to enough rows for the one-wave-per-row kernel."""
+    X = np.zeros((9, K), np.float16)
+    X[0] = np.float16(3.25)
+    X[2, ::2], X[2, 1::2] = np.float16(-7.0), np.float16(7.0)
+    X[3] = np.float16(65504.0)
+    X[3, ::3] = np.float16(-65504.0)
+    X[4] = np.float16(6e-8)
+    X[4, 1::2] = np.float16(-1.2e-7)
+    X[5, 17] = np.float16(1.0)
+    r = np.random.default_rng(6)
+    X[6] = (r.standard_normal(K) * 60000 / 4).clip(-65504, 65504).astype(np.float16)
+    X[7] = np.float16(-0.0)
+    X[8] = (r.standard_normal(K) * 1e-4).astype(np.float16)
+    X = np.ascontiguousarray(np.tile(X, (114, 1)))                 # 1026 rows
+    g = r.uniform(0.5, 2.0, K).astype(np.float32)
+    for b in (None, (r.standard_normal(K) * 0.3).astype(np.float32)):
+        for eps in (1e-5, 0.5):
+            Xq, xs = gpu_ln_quant(sq, X, g, b, eps)
+            Xq_r, xs_r = orc.layernorm_quantize(X, g, b, eps)
+            assert_bits_equal(xs, xs_r, f"x_scale eps={eps}")
+            assert_bits_equal(Xq, Xq_r, f"Xq eps={eps}")
 
 
 def test_layernorm_quantize_prefill_7b(sq, orc):
