@@ -9,6 +9,9 @@
 // count) and copies the outlier values of its rows out for the fp16 product, so
 // the bookkeeping needs no launch of its own.
 //
+// Rows of up to 4096 values without outlier columns take quant_wave_kernel (one wave
+// per row, below) instead of the streaming kernel.
+//
 // Persistent blocks (NT threads: two 512-thread blocks per CU, or one of 1024 for
 // rows over 8192 values) walk steps of G consecutive rows (G row groups of NT/G
 // threads).  Input rows reach LDS by DMA (buffer_load ... lds, no registers),
@@ -37,8 +40,10 @@
 //    rounds to the integer 1.5 * 2^23 + rne(v) for |v| < 2^22 (the sum lies in
 //    [2^23, 2^24), where the spacing is 1, and 1.5 * 2^23 is even, so ties go to
 //    even), and the low byte of its bit pattern is the two's-complement code.
-//    No clamp is needed: |x'| <= max gives |v| <= 127 (1 + 2^-23), which rounds
-//    to at most 127.
+//    A normal xs needs no clamp: |x'| <= max gives |v| <= 127 (1 + 2^-23), which
+//    rounds to at most 127.  A subnormal xs (only with smoothing factors of 2^100 and
+//    more, whose quotients x / s_j are subnormal) can be coarse enough for |v| > 127.5,
+//    and such rows clamp v to [-128, 127] first.
 #include <type_traits>
 
 #include "sq_internal.h"
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
         for (int j = R - NP; j < R; ++j) dma_step(j);
     }
     const bool guard_wave = __builtin_amdgcn_ballot_w64(guard) != 0;
+    bool clamp_rows = false;                      // this wave saw a row with a subnormal xs
 
     for (int j = 0; j < steps; ++j) {
         // After this wave's DMA of step j it issued (R-1) L DMA instructions (later steps)
@@ -327,6 +333,10 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
         if (live && t == 0) scale[row] = xs;
         const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;   // xs == 0: every x' is 0, codes 0
 
+        // A normal xs keeps |x' / xs| < 127.5.  With smoothing factors of 2^100 and more,
+        // max |x'| can be so small that xs is a coarse subnormal and the quotient exceeds
+        // the code range: such rows are noted here and get clamped codes after the loop.
+        if (SMOOTH && live && xs < 1.17549435e-38f) clamp_rows = true;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             uint32_t b[4];
@@ -340,6 +350,232 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
         }
         dma_step(j + R);                          // into the slot this step used
     }
+    if (SMOOTH && clamp_rows) {
+        // Rows whose xs is subnormal (see above; a wave-uniform flag, so normal data only
+        // pays this test).  The wave waits for its own stores, then for each of its rows
+        // recomputes the row maximum over all K columns (x / s_j as in pass 1) and, where xs
+        // is subnormal, rewrites its threads' chunks with clamped codes.  Each chunk is only
+        // ever written by its own thread, so no other wave is involved.
+        __builtin_amdgcn_s_waitcnt(0);
+        auto xprime = [&](float x, int col) {
+            float q = (float)((double)x * rcp64((double)s[col]));
+            if (__builtin_fabsf(q) < 1.17549435e-38f && x != 0.0f) q = x / s[col];
+            return q;
+        };
+        for (int j = 0; j < steps; ++j) {
+            const int row = (j * nb + (int)blockIdx.x) * G + g;
+            if (row >= M) continue;                  // uniform: a wave lies in one group
+            const _Float16* xr = X + (int64_t)row * K;
+            float amax = 0.0f;
+            for (int col = lane; col < K; col += 64) amax = __builtin_fmaxf(amax, __builtin_fabsf(xprime((float)xr[col], col)));
+            amax = wave_max(amax);
+            const float xs = amax / 127.0f;
+            if (!(xs < 1.17549435e-38f) || xs == 0.0f) continue;
+            const double rx = rcp64((double)xs);
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int c = t + i * tpg;
+                if (!valid[i]) continue;
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = __builtin_amdgcn_fmed3f((float)((double)xprime((float)xr[4 * c + e], 4 * c + e) * rx),
+                                                            -128.0f, 127.0f);
+                    w |= (code_bits(v) & 0xffu) << (8 * e);
+                }
+                *reinterpret_cast<uint32_t*>(Xq + (int64_t)row * K + 4 * c) = w;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per row, for rows of up to 4096 values with at least four rows per CU (the
+// 7B-class prefill activations), with the same arithmetic as the streaming kernel.
+// Lane l holds the 16-byte chunks l, l + 64, ... of its row (read through a per-row
+// buffer resource: a row past M has 0 records, so its reads return zeros and its
+// stores are dropped), converts them to x' in registers, and the row maximum is a DPP
+// reduction inside the wave, so there is no block barrier in the row loop and no LDS
+// round trip per row.  With smoothing, the block keeps RN64(1/s_j) of every column in
+// LDS (computed once, while the first rows are in flight).  The next row's loads go out
+// as soon as the current row is converted.
+//
+// Without a column s_j >= 2^100 (or NaN), x / s_j never falls below the fp32 normal
+// range (|x| >= 2^-24 for a non-zero binary16), so RN32(RN64(x * RN64(1/s_j))) is the
+// quotient, every non-zero |x'| is at least 2^-124, xs = fl32(max / 127) is within
+// 2^-18 relative of max / 127, and |fl32(x' / xs)| < 127.5: the codes need no clamp.  If
+// some column has s_j >= 2^100, every wave takes a plain two-pass loop per row instead
+// (the IEEE division for quotients below the normal range, and the clamp), which reads
+// the row again for the codes.
+template <int CPL, bool SMOOTH>
+__global__ __launch_bounds__(256) void quant_wave_kernel(const _Float16* __restrict__ X, int M, int K,
+                                                         const float* __restrict__ s, int8_t* __restrict__ Xq,
+                                                         float* __restrict__ scale) {
+    constexpr int kThreads = 256, kWaves = kThreads / 64;
+    constexpr int FPT = (CPL + 1) / 2;           // s vectors (4 floats) per thread: K / 4 <= 128 CPL
+    extern __shared__ double srcp[];             // SMOOTH: RN64(1 / s_j), 4 * kThreads * FPT slots
+    __shared__ int hflag[kWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nchunk = K / 8;
+    const int nv4 = K / 4;
+    const int nwv = (int)gridDim.x * kWaves;
+    int m = (int)blockIdx.x * kWaves + wave;
+    auto row_rsrc = [&](const void* base, int row, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, row < M ? bytes : 0, 0x00020000);
+    };
+    auto load = [&](int row, v4i* r) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(X + (int64_t)(row < M ? row : 0) * K, row, 2 * K);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            r[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (lane + 64 * i), 0, 0));
+    };
+    // prologue: the s loads, then the first row's loads, then the reciprocals into LDS (the
+    // LDS writes wait for the s loads only); the slots past K are slack, never read
+    v4f sv[SMOOTH ? FPT : 1];
+    if constexpr (SMOOTH) {
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) {
+            const int j = (int)threadIdx.x + kThreads * i;
+            sv[i] = reinterpret_cast<const v4f*>(s)[j < nv4 ? j : nv4 - 1];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4i cur[CPL];
+    load(m, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    bool huge = false;
+    if constexpr (SMOOTH) {
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) {
+            const int j = (int)threadIdx.x + kThreads * i;
+            double r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r[e] = rcp64((double)sv[i][e]);
+                huge = huge || (j < nv4 && !(sv[i][e] < 0x1p100f));
+            }
+            reinterpret_cast<v4f*>(srcp)[2 * j] = __builtin_bit_cast(v4f, (double __attribute__((ext_vector_type(2)))){r[0], r[1]});
+            reinterpret_cast<v4f*>(srcp)[2 * j + 1] = __builtin_bit_cast(v4f, (double __attribute__((ext_vector_type(2)))){r[2], r[3]});
+        }
+    }
+    if (lane == 0) hflag[wave] = __builtin_amdgcn_ballot_w64(huge) != 0;
+    barrier_lds();
+    const bool slow = SMOOTH && (hflag[0] | hflag[1] | hflag[2] | hflag[3]) != 0;
+    const v4f* sr = reinterpret_cast<const v4f*>(srcp);
+
+    if (slow) {
+        // some s_j >= 2^100: per element div_rcp64 semantics (the IEEE division below the
+        // normal range) and clamped codes, the row read twice
+        for (; m < M; m += nwv) {
+            const _Float16* xr = X + (int64_t)m * K;
+            auto xprime = [&](_Float16 h, int j) {
+                const float x = (float)h;
+                float q = (float)((double)x * srcp[j]);
+                if (__builtin_fabsf(q) < 1.17549435e-38f && x != 0.0f) q = x / s[j];
+                return q;
+            };
+            float amax = 0.0f;
+            for (int c = lane; c < nchunk; c += 64) {
+                const h8 hv = *reinterpret_cast<const h8*>(xr + 8 * c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(xprime(hv[e], 8 * c + e)));
+            }
+            amax = wave_max(amax);
+            const float xs = amax / 127.0f;
+            if (lane == 0) scale[m] = xs;
+            const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
+            for (int c = lane; c < nchunk; c += 64) {
+                const h8 hv = *reinterpret_cast<const h8*>(xr + 8 * c);
+                uint32_t w[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t b = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int code = xs == 0.0f ? 0 : code_of((float)((double)xprime(hv[4 * h + e], 8 * c + 4 * h + e) * rx));
+                        b |= (uint32_t)(code & 0xff) << (8 * e);
+                    }
+                    w[h] = b;
+                }
+                *reinterpret_cast<uint2*>(Xq + (int64_t)m * K + 8 * c) = make_uint2(w[0], w[1]);
+            }
+        }
+        return;
+    }
+
+    // the first row's pass runs on every wave (a wave without a row reads zeros, and its
+    // stores are dropped), so that its loads stay ahead of the barrier above
+    uint32_t lbase = 0;                            // LDS offset, re-read per row (see below)
+    do {
+        // an opaque zero: keeps the compiler from hoisting the reciprocal reads out of the
+        // row loop into registers (128 of them, which would halve the waves per SIMD)
+        asm volatile("" : "+s"(lbase));
+        float xk[CPL][8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            v4f r4[4];
+            if constexpr (SMOOTH) {
+                const int cc = (c < nchunk ? c : 0) + (int)lbase;   // chunks past the row hold zeros
+#pragma unroll
+                for (int u = 0; u < 4; ++u) r4[u] = sr[4 * cc + u];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)cur[i][e >> 1] >> (16 * (e & 1))));
+                if constexpr (SMOOTH) {
+                    const double r = __builtin_bit_cast(double, (uint64_t)__float_as_uint(r4[e >> 1][2 * (e & 1)]) |
+                                                                    ((uint64_t)__float_as_uint(r4[e >> 1][2 * (e & 1) + 1]) << 32));
+                    x = (float)((double)x * r);
+                }
+                xk[i][e] = x;
+            }
+            float a = __builtin_fmaxf(__builtin_fabsf(xk[i][0]), __builtin_fabsf(xk[i][1]));
+#pragma unroll
+            for (int e = 2; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(xk[i][e]));
+            amax = __builtin_fmaxf(amax, a);
+        }
+        load(m + nwv, cur);                        // next row, in flight from here
+        amax = wave_max(amax);
+        const float xs = amax / 127.0f;
+        if (lane == 0 && m < M) scale[m] = xs;
+        const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;   // xs == 0: every x' is 0, codes 0
+        const __amdgpu_buffer_rsrc_t rq = row_rsrc(Xq + (int64_t)m * K, m, K);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            uint32_t b[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = code_bits((float)((double)xk[i][e] * rx));
+            const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                      __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                      __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+            __builtin_amdgcn_raw_buffer_store_b64((unsigned int __attribute__((ext_vector_type(2)))){lo, hi}, rq,
+                                                  8 * (lane + 64 * i), 0, 0);
+        }
+        m += nwv;
+    } while (m < M);
+}
+
+template <int CPL, bool SMOOTH>
+hipError_t launch_wave(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, hipStream_t st) {
+    constexpr int kWaves = 4;
+    const int64_t blocks = ((int64_t)M + kWaves - 1) / kWaves;
+    const int64_t cap = (int64_t)dev_info().cus * 8;
+    const size_t lds = SMOOTH ? (size_t)256 * ((CPL + 1) / 2) * 4 * sizeof(double) : 0;
+    SQ_LAUNCH((quant_wave_kernel<CPL, SMOOTH>), dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(64 * kWaves), lds,
+              st, X, M, K, s, Xq, scale);
+    return hipSuccess;
+}
+
+template <bool SMOOTH>
+hipError_t launch_wave_k(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, hipStream_t st) {
+    if (K <= 512) return launch_wave<1, SMOOTH>(X, M, K, s, Xq, scale, st);
+    if (K <= 1024) return launch_wave<2, SMOOTH>(X, M, K, s, Xq, scale, st);
+    if (K <= 2048) return launch_wave<4, SMOOTH>(X, M, K, s, Xq, scale, st);
+    return launch_wave<8, SMOOTH>(X, M, K, s, Xq, scale, st);
 }
 
 template <int NT, int CH, bool SMOOTH, bool OUTL>
@@ -389,6 +625,10 @@ hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const fl
     // keep at most 4 chunks per thread (bigger steps spread the per-step reduction and
     // synchronization over more values).  Longer rows: 1024 threads, one row per step,
     // up to 5 chunks per thread.
+    if (!os && K <= 4096) {                      // one wave per row
+        if (s) return launch_wave_k<true>(X, (int)M, (int)K, s, Xq, scale, st);
+        return launch_wave_k<false>(X, (int)M, (int)K, nullptr, Xq, scale, st);
+    }
     const int64_t nch = K / 4;
     const int nt = K <= 8192 ? 512 : 1024;
     int G = nt / 64;

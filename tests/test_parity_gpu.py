@@ -122,6 +122,9 @@ STREAM_CASES = [
     (1024, 16, True), (1031, 48, False), (4099, 144, True), (2048, 4096, True), (1500, 4112, True),
     (1100, 8192, False), (1024, 12304, True), (1030, 16384, True), (1025, 20480, True), (1040, 20464, False),
     (3000, 1040, True), (1100, 10240, True), (1024, 2048, False), (1200, 256, True),
+    # rows of up to 4096 values take one wave per row: 1 to 8 chunks of 8 values per lane,
+    # ragged chunk counts, more rows than waves in the grid (waves take further rows)
+    (1024, 528, False), (1100, 4096, False), (2050, 3072, True), (9000, 1024, True), (8300, 4096, True),
 ]
 
 
@@ -154,6 +157,27 @@ def test_quantize_streaming_ties_and_tiny_quotients(sq, orc):
         ref = orc.quantize_per_token(X, ss)
         assert_bits_equal(got[1], ref[1], "x_scale")
         assert_bits_equal(got[0], ref[0], "Xq")
+
+
+@pytest.mark.parametrize("K", [1024, 4096, 8192])
+def test_quantize_streaming_subnormal_scale(sq, orc, K):
+    """Every s_j = 2^127 and |x| <= 2^-14: every x / s_j is an fp32 subnormal (the IEEE
+    division), the row maximum is about 2^-141, and xs = fl32(max / 127) is a subnormal so
+    coarse that max / xs exceeds 127.5: the codes must be clamped to 127."""
+    M = 1100
+    r = np.random.default_rng(32)
+    X = (r.uniform(-1.0, 1.0, (M, K)) * 2.0 ** -14).astype(np.float16)
+    X[3] = 0.0
+    X[4, :] = np.float16(2.0 ** -14)                                # max / xs = 256 / 2
+    s = np.full(K, np.float32(2.0 ** 127))
+    s[: K // 2] = r.uniform(0.5, 2.0, K // 2).astype(np.float32)
+    for ss in (np.full(K, np.float32(2.0 ** 127)), s):
+        got = gpu_quantize_rows(sq, X, ss)
+        ref = orc.quantize_per_token(X, ss)
+        assert_bits_equal(got[1], ref[1], "x_scale")
+        assert_bits_equal(got[0], ref[0], "Xq")
+    # the case the clamp is for: at least one code at the bound
+    assert np.abs(orc.quantize_per_token(X, np.full(K, np.float32(2.0 ** 127)))[0]).max() == 127
 
 
 # ---------------------------------------------------------------------------
