@@ -80,14 +80,6 @@ template <> struct CodeStore<4> {
     }
 };
 
-// FP8 E4M3 (OCP e4m3fn) codes of four values, one per byte, nearest-even
-// (v_cvt_pk_fp8_f32).  Callers clamp to [-448, 448] first, so no value overflows.
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-__device__ __forceinline__ float fp8_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
-
 // Codes of VEC quotients x'/scale: int8 (FMT 0) or FP8 E4M3 (FMT 1); `zero` marks
 // elements whose code is 0 (scale 0, LLM.int8() outlier columns).
 template <int VEC, int FMT>
@@ -458,6 +450,9 @@ hipError_t launch_quant_rows(const void* X, int dt, int64_t M, int64_t K, const 
     if (dt == SQ_F16 && fmt == 0 && !outl && (mode == 0 || mode == 1) && quant_stream_applies(M, K, mode == 1, false))
         return launch_quant_stream(static_cast<const _Float16*>(X), M, K, mode == 1 ? s : nullptr, Xq, scale, nullptr,
                                    st);
+    if (dt == SQ_F16 && fmt == 1 && !outl && (mode == 0 || mode == 1) && K <= 4096 &&
+        quant_stream_applies(M, K, mode == 1, false))
+        return launch_quant_wave_fp8(static_cast<const _Float16*>(X), M, K, mode == 1 ? s : nullptr, Xq, scale, st);
     if (fmt == 1) {   // FP8 E4M3 codes (no outlier variant)
 #define SQ_QR8(T, MD) return quant_rows_t<T, MD, false, 1>((const T*)X, M, K, s, Xq, scale, nullptr, nullptr, st)
         if (dt == SQ_F16) {

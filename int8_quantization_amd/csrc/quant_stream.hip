@@ -407,7 +407,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 1 : 2) void quant_stream_kernel(co
 // some column has s_j >= 2^100, every wave takes a plain two-pass loop per row instead
 // (the IEEE division for quotients below the normal range, and the clamp), which reads
 // the row again for the codes.
-template <int CPL, bool SMOOTH>
+template <int CPL, bool SMOOTH, int FMT>
 __global__ __launch_bounds__(256) void quant_wave_kernel(const _Float16* __restrict__ X, int M, int K,
                                                          const float* __restrict__ s, int8_t* __restrict__ Xq,
                                                          float* __restrict__ scale) {
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void quant_wave_kernel(const _Float16* __restr
                 for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(xprime(hv[e], 8 * c + e)));
             }
             amax = wave_max(amax);
-            const float xs = amax / 127.0f;
+            const float xs = amax / (FMT == 0 ? 127.0f : 448.0f);
             if (lane == 0) scale[m] = xs;
             const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;
             for (int c = lane; c < nchunk; c += 64) {
@@ -490,13 +490,18 @@ __global__ __launch_bounds__(256) void quant_wave_kernel(const _Float16* __restr
                 uint32_t w[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    uint32_t b = 0;
+                    float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int code = xs == 0.0f ? 0 : code_of((float)((double)xprime(hv[4 * h + e], 8 * c + 4 * h + e) * rx));
-                        b |= (uint32_t)(code & 0xff) << (8 * e);
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = xs == 0.0f ? 0.0f : (float)((double)xprime(hv[4 * h + e], 8 * c + 4 * h + e) * rx);
+                    if constexpr (FMT == 0) {
+                        uint32_t b = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) b |= (uint32_t)(code_of(v[e]) & 0xff) << (8 * e);
+                        w[h] = b;
+                    } else {
+                        w[h] = fp8x4(fp8_clamp(v[0]), fp8_clamp(v[1]), fp8_clamp(v[2]), fp8_clamp(v[3]));
                     }
-                    w[h] = b;
                 }
                 *reinterpret_cast<uint2*>(Xq + (int64_t)m * K + 8 * c) = make_uint2(w[0], w[1]);
             }
@@ -539,19 +544,30 @@ __global__ __launch_bounds__(256) void quant_wave_kernel(const _Float16* __restr
         }
         load(m + nwv, cur);                        // next row, in flight from here
         amax = wave_max(amax);
-        const float xs = amax / 127.0f;
+        const float xs = amax / (FMT == 0 ? 127.0f : 448.0f);
         if (lane == 0 && m < M) scale[m] = xs;
         const double rx = xs != 0.0f ? rcp64((double)xs) : 0.0;   // xs == 0: every x' is 0, codes 0
         const __amdgpu_buffer_rsrc_t rq = row_rsrc(Xq + (int64_t)m * K, m, K);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            uint32_t b[8];
+            uint32_t lo, hi;
+            if constexpr (FMT == 0) {
+                uint32_t b[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = code_bits((float)((double)xk[i][e] * rx));
-            const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
-                                                      __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
-                                                      __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+                for (int e = 0; e < 8; ++e) b[e] = code_bits((float)((double)xk[i][e] * rx));
+                lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                           __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+                hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                           __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+            } else {
+                // E4M3 codes of fl32(x' / xs) clamped to [-448, 448] (a subnormal xs can leave the
+                // quotient above 448; xs == 0 gives rx = 0 and code 0)
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fp8_clamp((float)((double)xk[i][e] * rx));
+                lo = fp8x4(v[0], v[1], v[2], v[3]);
+                hi = fp8x4(v[4], v[5], v[6], v[7]);
+            }
             __builtin_amdgcn_raw_buffer_store_b64((unsigned int __attribute__((ext_vector_type(2)))){lo, hi}, rq,
                                                   8 * (lane + 64 * i), 0, 0);
         }
@@ -559,23 +575,23 @@ __global__ __launch_bounds__(256) void quant_wave_kernel(const _Float16* __restr
     } while (m < M);
 }
 
-template <int CPL, bool SMOOTH>
+template <int CPL, bool SMOOTH, int FMT>
 hipError_t launch_wave(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, hipStream_t st) {
     constexpr int kWaves = 4;
     const int64_t blocks = ((int64_t)M + kWaves - 1) / kWaves;
     const int64_t cap = (int64_t)dev_info().cus * 8;
     const size_t lds = SMOOTH ? (size_t)256 * ((CPL + 1) / 2) * 4 * sizeof(double) : 0;
-    SQ_LAUNCH((quant_wave_kernel<CPL, SMOOTH>), dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(64 * kWaves), lds,
+    SQ_LAUNCH((quant_wave_kernel<CPL, SMOOTH, FMT>), dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(64 * kWaves), lds,
               st, X, M, K, s, Xq, scale);
     return hipSuccess;
 }
 
-template <bool SMOOTH>
+template <bool SMOOTH, int FMT>
 hipError_t launch_wave_k(const _Float16* X, int M, int K, const float* s, int8_t* Xq, float* scale, hipStream_t st) {
-    if (K <= 512) return launch_wave<1, SMOOTH>(X, M, K, s, Xq, scale, st);
-    if (K <= 1024) return launch_wave<2, SMOOTH>(X, M, K, s, Xq, scale, st);
-    if (K <= 2048) return launch_wave<4, SMOOTH>(X, M, K, s, Xq, scale, st);
-    return launch_wave<8, SMOOTH>(X, M, K, s, Xq, scale, st);
+    if (K <= 512) return launch_wave<1, SMOOTH, FMT>(X, M, K, s, Xq, scale, st);
+    if (K <= 1024) return launch_wave<2, SMOOTH, FMT>(X, M, K, s, Xq, scale, st);
+    if (K <= 2048) return launch_wave<4, SMOOTH, FMT>(X, M, K, s, Xq, scale, st);
+    return launch_wave<8, SMOOTH, FMT>(X, M, K, s, Xq, scale, st);
 }
 
 template <int NT, int CH, bool SMOOTH, bool OUTL>
@@ -626,8 +642,8 @@ hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const fl
     // synchronization over more values).  Longer rows: 1024 threads, one row per step,
     // up to 5 chunks per thread.
     if (!os && K <= 4096) {                      // one wave per row
-        if (s) return launch_wave_k<true>(X, (int)M, (int)K, s, Xq, scale, st);
-        return launch_wave_k<false>(X, (int)M, (int)K, nullptr, Xq, scale, st);
+        if (s) return launch_wave_k<true, 0>(X, (int)M, (int)K, s, Xq, scale, st);
+        return launch_wave_k<false, 0>(X, (int)M, (int)K, nullptr, Xq, scale, st);
     }
     const int64_t nch = K / 4;
     const int nt = K <= 8192 ? 512 : 1024;
@@ -638,6 +654,12 @@ hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const fl
     if (s) return launch_mode<true, false>(X, (int)M, (int)K, s, Xq, scale, none, nt, G, ch, st);
     if (os) return launch_mode<false, true>(X, (int)M, (int)K, nullptr, Xq, scale, *os, nt, G, ch, st);
     return launch_mode<false, false>(X, (int)M, (int)K, nullptr, Xq, scale, none, nt, G, ch, st);
+}
+
+hipError_t launch_quant_wave_fp8(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* q, float* scale,
+                                 hipStream_t st) {
+    if (s) return launch_wave_k<true, 1>(X, (int)M, (int)K, s, q, scale, st);
+    return launch_wave_k<false, 1>(X, (int)M, (int)K, nullptr, q, scale, st);
 }
 
 }  // namespace sq

@@ -51,6 +51,14 @@ __device__ __forceinline__ int code_of(float v) {
     return (int)r;
 }
 
+// FP8 E4M3 (OCP e4m3fn) codes of four values, one per byte, nearest-even
+// (v_cvt_pk_fp8_f32).  Callers clamp to [-448, 448] first, so no value overflows.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+__device__ __forceinline__ float fp8_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
 // Maximum over the wave of non-negative floats, returned to every lane (all 64 lanes active).
 // Four DPP steps give each row of 16 lanes its maximum (quad swaps 1 and 2, then the
 // half-row and row mirrors), and the four row maxima are read out (v_readlane) and
@@ -196,6 +204,10 @@ struct OutlierSplit {
 bool quant_stream_applies(int64_t M, int64_t K, bool smooth, bool outliers);
 hipError_t launch_quant_stream(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* Xq, float* scale,
                                const OutlierSplit* os, hipStream_t st);
+// FP8 E4M3 codes of fp16 rows (scale max/448), one wave per row: for at least four rows
+// per CU (quant_stream_applies) and rows of up to 4096 values.
+hipError_t launch_quant_wave_fp8(const _Float16* X, int64_t M, int64_t K, const float* s, int8_t* q, float* scale,
+                                 hipStream_t st);
 
 // Running column absolute maximum: amax_bits[j] = max(amax_bits[j], bits(max_m |X[m,j]|)),
 // where amax_bits holds non-negative floats as their bit patterns (monotone as uint32).

@@ -954,7 +954,11 @@ def check_fp8_acc(orc, acc, exact, Xq, Wq, rows, cols, what):
 @pytest.mark.parametrize("M,K,dt,smooth", [(1, 16, np.float32, False), (7, 48, np.float16, True),
                                            (300, 4096, np.float16, True), (64, 1040, np.float32, True),
                                            (33, 20480, np.float16, False), (5, 131056, np.float16, True),
-                                           (2048, 4096, np.float16, True)])
+                                           (2048, 4096, np.float16, True),
+                                           # fp16 with at least four rows per CU and rows up to 4096
+                                           # values: one wave per row
+                                           (1024, 16, np.float16, True), (1100, 1040, np.float16, False),
+                                           (1500, 4096, np.float16, False), (9000, 512, np.float16, True)])
 def test_fp8_quantize_per_token(sq, orc, M, K, dt, smooth):
     r = np.random.default_rng(3 * M + K)
     X = (r.standard_normal((M, K)) * r.uniform(0.01, 40.0, (M, 1))).astype(dt)
@@ -989,6 +993,40 @@ def test_fp8_quantize_special_rows(sq, orc):
     assert_bits_equal(q, q_ref, "codes")
     assert xs[0] == 0 and not q[0].any()
     assert q[4, 9] == 0xFE and q[1, 5] == 0x7E
+
+
+def test_fp8_quantize_special_rows_wave(sq, orc):
+    """Zero rows, signed zeros, rounding midpoints, codes in the FP8 subnormal range and a
+    single non-zero element, as binary16 rows repeated to 1026 rows (the one-wave-per-row
+    kernel); then every s_j = 2^127 with |x| <= 2^-14, where xs = fl32(max / 448) is a coarse
+    subnormal and the codes must be clamped to +-448 (the kernel's two-pass path)."""
+    K = 1024
+    X = np.zeros((6, K), np.float16)
+    X[1, :] = np.float16(-0.0)
+    X[1, 5] = 3.0
+    mids = np.float32([1.0625, 1.1875, 2.125, 2.375, 3.0 * 2 ** -10, 5.0 * 2 ** -10, 0.5 * 2 ** -9, 1.5 * 2 ** -9])
+    X[2, :8] = (mids / 8).astype(np.float16)
+    X[2, 8:16] = (-mids / 8).astype(np.float16)
+    X[2, 16] = 56.0
+    X[3, 0] = 448.0
+    X[3, 1:7] = np.float16([2 ** -8, 2 ** -9, 2 ** -10, 2 ** -11, -2 ** -9, -2 ** -12])
+    X[4, 9] = -7.5
+    X[5] = np.linspace(-3, 3, K).astype(np.float16)
+    X = np.ascontiguousarray(np.tile(X, (171, 1)))                 # 1026 rows
+    for s in (None, np.full(K, np.float32(2.0))):
+        q, xs = gpu_fp8_quant_rows(sq, X, s)
+        q_ref, xs_ref = orc.fp8_quantize_per_token(X, s)
+        assert_bits_equal(xs, xs_ref, "scales")
+        assert_bits_equal(q, q_ref, "codes")
+    r = np.random.default_rng(33)
+    Xt = (r.uniform(-1.0, 1.0, (1100, K)) * 2.0 ** -14).astype(np.float16)
+    Xt[4, :] = np.float16(600 * 2.0 ** -22)                          # x' = 600 2^-149, xs = 2^-149
+    s = np.full(K, np.float32(2.0 ** 127))
+    q, xs = gpu_fp8_quant_rows(sq, Xt, s)
+    q_ref, xs_ref = orc.fp8_quantize_per_token(Xt, s)
+    assert_bits_equal(xs, xs_ref, "scales, s = 2^127")
+    assert_bits_equal(q, q_ref, "codes, s = 2^127")
+    assert (q_ref[4] == 0x7E).all()                                 # +448: the clamp was needed
 
 
 @pytest.mark.parametrize("gran", [0, 1])
