@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W8A8 linear TOPS incl. quant+dequant (% int8 MFMA peak); decode GB/s (% HBM peak)"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP8_TOPS = 5000.0       # MI355X dense fp8 MFMA, 5.0 PFLOP/s
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "int8_quantization_amd", "csrc", "gemm.hip")
@@ -210,10 +211,33 @@ def bench_w8a8(torch, sq, d, wl, steps, warmup, settle_s=0.5):
     q_ms, _ = time_steps(torch, lambda t: sq.sq_quantize_per_token(X, s0, Xq, xs), steps, 5, kernel_events=False)
     qb = X.element_size() * M * K + M * K + 4 * M
     ops = sum(2.0 * M * p[2].shape[0] * K for p in projs)
+    fp16 = fp16_reference(torch, d, wl, X, steps, warmup, ops, ms) if wl.X.dtype == np.float16 else None
     return dict(ms=ms, gemm_ms=gemm_ms, ops=ops, gemm_ops_per_launch=ops / len(projs),
                 Ns=[p[2].shape[0] for p in projs], pct=pct, settle_steps=settled,
                 quantize=dict(us=q_ms * 1e3, GBps=qb / (q_ms * 1e-3) / 1e9,
-                              hbm_frac=qb / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS))
+                              hbm_frac=qb / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS),
+                fp16_reference=fp16)
+
+
+def fp16_reference(torch, d, wl, X, steps, warmup, ops, w8a8_ms):
+    """The same projections as an unquantized fp16 layer, Y = X W^T through torch.mm
+    (the vendor GEMM library), timed like the W8A8 step: the pages quote W8A8
+    speed-ups over fp16 (1.5-2x), and this is that ratio on this GPU.  Context only: it
+    is not part of the path and no output of it is checked."""
+    Ws = [d(W) for W in wl.weights.values()]
+    Ys = [torch.empty(X.shape[0], W.shape[0], dtype=torch.float16, device="cuda") for W in Ws]
+
+    def step(_):
+        for W, Y in zip(Ws, Ys):
+            torch.mm(X, W.t(), out=Y)
+
+    settle(torch, step, 0.3)
+    ms, _ = time_steps(torch, step, steps, warmup, kernel_events=False)
+    del Ws, Ys
+    torch.cuda.empty_cache()
+    tflops = ops / (ms * 1e-3) / 1e12
+    return dict(ms_per_step=round(ms, 5), TFLOPs=round(tflops, 1), fp16_mfma_frac=round(tflops / PEAK_FP16_TFLOPS, 4),
+                w8a8_speedup=round(ms / w8a8_ms, 3), call="torch.mm(X, W.t(), out=Y), fp16 in and out")
 
 
 def bench_fp8(torch, sq, d, wl, steps, warmup):
@@ -675,6 +699,7 @@ def main():
             "step_ms_percentiles": {k: round(v, 5) for k, v in r["pct"].items()},
             "tops_at_p50": round(r["ops"] / (r["pct"]["p50"] * 1e-3) / 1e12, 2),
             "quantize_530b": r["quantize"],
+            "fp16_reference": r["fp16_reference"],
             "gpu": gpu_info(torch),
             "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                          "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
@@ -704,7 +729,8 @@ def main():
                 workload=wl2.name, ms_per_step=r["ms"], TOPS=tops, mfma_frac_incl_quant=tops / PEAK_INT8_TOPS,
                 step_ms_percentiles=r["pct"], gemm_us_per_launch=r["gemm_ms"] * 1e3, gemm_TOPS=gemm_tops,
                 gemm_mfma_frac=gemm_tops / PEAK_INT8_TOPS, quantize_7b=r["quantize"],
-                gemm_traffic_bytes_per_launch=traffic_for("gemm_prefill_7b", GEMM_SRC))
+                gemm_traffic_bytes_per_launch=traffic_for("gemm_prefill_7b", GEMM_SRC),
+                fp16_reference=r["fp16_reference"])
             if not args.no_cpu_baseline:
                 secondary["prefill_7b"]["cpu_oracle_one_thread"] = oracle_one_thread(wl2)
             del wl2
