@@ -447,8 +447,19 @@ def bench_llm_int8(torch, sq, d, wl, steps, warmup):
     settle(torch, step)
     ms, _ = time_steps(torch, step, steps, warmup)
     ops = 2.0 * M * N * K
+    n_out = int(cnt.item())
+    # the unquantized fp16 layer on the same operands, for the pages' LLM.int8() speed-up over fp16
+    Yf = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    fp16_step = lambda _: torch.mm(Xd, Wd.t(), out=Yf)
+    settle(torch, fp16_step, 0.3)
+    fms, _ = time_steps(torch, fp16_step, steps, warmup, kernel_events=False)
+    tflops = ops / (fms * 1e-3) / 1e12
     return dict(ms_per_step=ms, TOPS=ops / (ms * 1e-3) / 1e12, mfma_frac=ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
-                n_outliers=int(cnt.item()))
+                n_outliers=n_out,
+                fp16_reference=dict(ms_per_step=round(fms, 5), TFLOPs=round(tflops, 1),
+                                    fp16_mfma_frac=round(tflops / PEAK_FP16_TFLOPS, 4),
+                                    llm_int8_speedup=round(fms / ms, 3),
+                                    call="torch.mm(X, W16.t(), out=Y), fp16 in and out"))
 
 
 def bench_layernorm_quant(torch, sq, d, wl, steps, warmup):
