@@ -8,7 +8,11 @@
 // tiles (one cache line per row) held in two LDS stages: while the MFMAs read
 // stage j, buffer_load ... lds (LDS DMA, 1 KB = 8 rows x 128 B per wave
 // instruction) fills stage j+1 straight from global memory, with no register
-// staging.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at slot
+// staging.  In the 256-column tiles a stage is refilled as soon as the barrier
+// that ends the reads of its previous tile has passed (that tile's last k-step
+// is then in registers), one or two DMA instructions after each MFMA of that
+// last k-step, so the loads have four k-steps to land and their issue hides
+// behind the MFMAs.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at slot
 // c ^ ((r >> SWZ) & 7), so the fragment reads (lane -> row lane%32, chunk
 // lane/32) of a wave hit distinct banks.  A K that is not a multiple of 128
 // starts with one partial tile staged through registers with zero fill.
@@ -80,6 +84,15 @@ namespace {
 __device__ __forceinline__ void wait_all_loads() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+// All but the last N vector-memory operations (loads complete in issue order) and
+// every LDS access.
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);   // vmcnt(N) expcnt(7) lgkmcnt(0)
     asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void wait_lds() {
@@ -353,7 +366,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
     // flight when the loop starts would make the compiler's fragment waits in it
     // conservative (it cannot order them against the LDS reads).
     asm volatile("" ::"s"(Yv), "s"(acc_out), "s"(ws_stride));
-    wait_all_loads();
+    // The 256-column tiles keep two K tiles in flight: the second one's DMA goes out here,
+    // and the wait leaves exactly those L loads (the youngest) outstanding.
+    constexpr bool EARLY = BN == 256;
+    if (EARLY && nk > 1) {
+        dma(1, kofs(1));
+        wait_loads_but<L>();
+    } else {
+        wait_all_loads();
+    }
     block_barrier();
     fload(0, 0, 0);
 
@@ -372,6 +393,64 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_i8_kernel(
             fence();
         }
     };
+    // One fragment (q < TM: A fragment q, else B fragment q - TM), one MFMA, one DMA
+    // instruction: the pieces of the hand-interleaved k-step below.
+    auto frag_one = [&](int stage, int ks, int slot, int q) {
+        const int8_t* As = lds + stage * STAGE;
+        const int8_t* Bs = As + BM * BK;
+        if (q < TM) {
+            const int row = wm * WTM + q * 32 + lrow;
+            af[slot][q] = frag(As + row * BK, row, ks);
+        } else {
+            const int row = wn * WTN + (q - TM) * 32 + lrow;
+            bf[slot][q - TM] = frag(Bs + row * BK, row, ks);
+        }
+    };
+    auto mfma_one = [&](int slot, int i, int jj) {
+        if constexpr (FP8)
+            acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[slot][jj], af[slot][i], acc[i][jj], 0, 0, 0,
+                                                                         0, 0, 0);
+        else
+            acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[slot][jj], af[slot][i], acc[i][jj], 0, 0, 0);
+    };
+    auto dma_one = [&](int stage, int k0, int i) {
+        dma_to_lds(wave + NW * i < BM / 8 ? rA : rB, __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE + ldsoff[i]),
+                   voff[i], k0);
+    };
+    if constexpr (EARLY) {
+        // Tile j+1 was issued one barrier earlier (or in the prologue).  Every tile but the
+        // last ends in the barrier; the last runs after the loop.
+        for (int j = 0; j + 1 < nk; ++j) {
+            const int st = j & 1;
+            steps(st);
+            // tile j+1 landed for every wave, and tile j's last fragments are in registers
+            wait_all_loads();
+            block_barrier();
+            // so stage st is free: tile j+2 goes into it (after the last tile, the last tile's
+            // bytes again, into a stage nothing reads any more), spread over the MFMAs of tile
+            // j's last k-step after the first fragment reads of tile j+1.  The scheduling
+            // barriers keep this order.
+            const int k2 = __builtin_amdgcn_readfirstlane(j + 2 < nk ? kofs(j + 2) : kofs(j));
+            constexpr int NM = TM * TN, NQ = TM + TN;
+            static_assert(NM > NQ, "MFMAs left for the DMA instructions");
+            constexpr int PER = (L + NM - NQ - 1) / (NM - NQ);
+            int d = 0;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_one((KS - 1) & 1, m / TN, m % TN);
+                __builtin_amdgcn_sched_barrier(0);
+                if (m < NQ) {
+                    frag_one(st ^ 1, 0, 0, m);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PER; ++e)
+                        if (d < L) dma_one(st, k2, d++);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else
     // Every tile but the last prefetches its successor and ends in the barrier;
     // the last runs after the loop, so the loop body has a single shape.
     for (int j = 0; j + 1 < nk; ++j) {
